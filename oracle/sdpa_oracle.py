@@ -1,0 +1,250 @@
+"""CPU oracle for exact scaled dot-product attention (forward), in float64.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The HIP
+product path never does, and shares no code with it.
+
+What it computes (exactref.ai, ``scaled_dot_product_attention``, sections
+"Arguments" and "Full specification"): for query (..., L, E), key (..., S, E),
+value (..., S, Ev)
+
+    logits = scale * (Q K^T) + bias        (the mask is added after scaling)
+    P      = softmax(logits) over the key axis
+    out    = P V
+    lse    = log(sum_j exp(logits_j))      per query row
+
+The steps follow the "standard attention" the khchao.com NN Lab page describes
+in "The Memory Hierarchy Bottleneck in Standard Attention": the full score
+matrix S, then the full weight matrix A, then A V, all materialised (here in
+host RAM, float64).  Inputs are upcast exactly from whatever dtype they hold;
+nothing is rounded back to a narrow format.  numpy's matmul serves as the one
+library step (the dot products).
+
+Readings where the pages leave a step open (each is also listed in the design doc):
+  * scale=None means 1/sqrt(E) with E the query's last dimension, computed in
+    double; with E = 0 the scores are empty sums equal to 0 and the logits are
+    the bias alone, whatever the scale.
+  * is_causal keeps key j for query i iff j <= i, with i and j counted from the
+    top-left corner (also when L != S).
+  * enable_gqa maps query head h to key/value head h // (Hq / Hkv): query heads
+    are grouped contiguously, as in the xFormers 5-D (B, M, G, Hq, K) layout on
+    the insureai360 xFormers tutorial, section 5.
+  * attn_mask and is_causal may be given together: the kept set is the
+    intersection of both.
+  * Row special values (Full specification): any NaN logit makes the row's
+    output and lse NaN; otherwise any +inf logit makes the output NaN and the
+    lse +inf; otherwise a row with no finite logit has weight 0 on every key,
+    output 0 (0 * v) and lse -inf.
+  * Packed variable-length input with a block-diagonal mask (insureai360
+    tutorial, section 4): keys of another segment are removed; is_causal then
+    applies within a segment with local indices.  Computing each segment on its
+    own is the same thing, since removed keys get weight exactly 0; a test pins
+    the two forms against each other.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "resolve_scale", "bias_from_mask", "causal_bias", "logits", "weights",
+    "sdpa", "block_diagonal_bias", "sdpa_varlen", "entropy",
+]
+
+
+def _f64(x):
+    """Exact float64 copy of an array-like (torch tensors included, any float dtype)."""
+    if hasattr(x, "detach"):  # a torch tensor: upcast exactly on the host
+        x = x.detach().cpu()
+        if x.dtype.is_floating_point:
+            x = x.double()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def resolve_scale(E, scale):
+    """The factor on the scores: ``scale`` if given, else 1/sqrt(E) (Arguments table)."""
+    if scale is not None:
+        return float(scale)
+    if E == 0:
+        return math.inf  # never used: with E = 0 the scores are 0 and the logits are the mask
+    return 1.0 / math.sqrt(E)
+
+
+def bias_from_mask(attn_mask):
+    """A bool mask keeps keys where True (bias 0, else -inf); a float mask is the bias itself."""
+    if attn_mask is None:
+        return None
+    if hasattr(attn_mask, "detach"):
+        attn_mask = attn_mask.detach().cpu()
+        if attn_mask.dtype.is_floating_point:
+            attn_mask = attn_mask.double()
+        attn_mask = attn_mask.numpy()
+    m = np.asarray(attn_mask)
+    if m.dtype == np.bool_:
+        return np.where(m, 0.0, -np.inf)
+    return m.astype(np.float64)
+
+
+def causal_bias(L, S):
+    """(L, S) bias: 0 where key j <= query i, -inf above the diagonal (top-left aligned)."""
+    i = np.arange(L)[:, None]
+    j = np.arange(S)[None, :]
+    return np.where(j <= i, 0.0, -np.inf)
+
+
+def _expand_kv(query, key, value, enable_gqa):
+    """Repeat key/value heads for grouped-query attention (contiguous groups)."""
+    if key.ndim < 3 or query.ndim < 3:
+        return key, value
+    hq, hk = query.shape[-3], key.shape[-3]
+    if enable_gqa and hq != hk:
+        if hk == 0 or hq % hk != 0:
+            raise ValueError(f"query heads ({hq}) must be a multiple of key/value heads ({hk})")
+        rep = hq // hk
+        key = np.repeat(key, rep, axis=-3)
+        value = np.repeat(value, rep, axis=-3)
+    return key, value
+
+
+def logits(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
+    """The (..., L, S) float64 logits scale * q.k + bias, with every mask folded into the bias."""
+    q = _f64(query)
+    k = _f64(key)
+    k, _ = _expand_kv(q, k, k, enable_gqa)
+    E = q.shape[-1]
+    L, S = q.shape[-2], k.shape[-2]
+    bias = np.zeros((L, S))
+    mb = bias_from_mask(attn_mask)
+    if mb is not None:
+        bias = bias + mb
+    if is_causal:
+        bias = bias + causal_bias(L, S)
+    with np.errstate(invalid="ignore", over="ignore"):
+        if E == 0:
+            s = np.zeros(np.broadcast_shapes(q.shape[:-2], k.shape[:-2]) + (L, S))
+            return s + bias
+        s = np.matmul(q, np.swapaxes(k, -1, -2))
+        return resolve_scale(E, scale) * s + bias
+
+
+def _row_classes(ell):
+    """Boolean row classes of the Full specification: NaN rows, +inf rows, empty rows, normal rows."""
+    nan_row = np.isnan(ell).any(axis=-1)
+    inf_row = np.isposinf(ell).any(axis=-1) & ~nan_row
+    has_finite = np.isfinite(ell).any(axis=-1)
+    empty_row = ~nan_row & ~inf_row & ~has_finite
+    normal = ~nan_row & ~inf_row & has_finite
+    return nan_row, inf_row, empty_row, normal
+
+
+def _softmax_parts(ell):
+    """Row max m, unnormalised weights w = exp(l - m), row sum, and row classes."""
+    nan_row, inf_row, empty_row, normal = _row_classes(ell)
+    with np.errstate(invalid="ignore", over="ignore"):
+        m = np.where(normal, np.max(np.where(np.isnan(ell), -np.inf, ell), axis=-1), 0.0)
+        w = np.exp(ell - m[..., None])
+    w = np.where(normal[..., None], w, 0.0)
+    rowsum = w.sum(axis=-1)
+    return m, w, rowsum, (nan_row, inf_row, empty_row, normal)
+
+
+def weights(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
+    """The materialised (..., L, S) attention weights P (NaN rows for NaN/+inf logits, 0 rows when empty)."""
+    ell = logits(query, key, attn_mask, is_causal, scale, enable_gqa)
+    _, w, rowsum, (nan_row, inf_row, _, normal) = _softmax_parts(ell)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(normal[..., None], w / np.where(normal, rowsum, 1.0)[..., None], 0.0)
+    p = np.where((nan_row | inf_row)[..., None], np.nan, p)
+    return p
+
+
+def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+         enable_gqa=False):
+    """Exact attention: returns (out (..., L, Ev), lse (..., L)) in float64.
+
+    exactref.ai ``scaled_dot_product_attention``, Full specification: out is
+    softmax(Q K^T * scale + mask) V and lse is log(sum_j exp(logit_j)).
+    """
+    if dropout_p != 0:
+        raise ValueError("dropout_p must be 0: a random dropout has no exact reference")
+    q, k, v = _f64(query), _f64(key), _f64(value)
+    if k.shape[-1] != q.shape[-1]:
+        raise ValueError("query and key must share the last dimension E")
+    if k.shape[-2] != v.shape[-2]:
+        raise ValueError("key and value must share the sequence length S")
+    if not enable_gqa and q.ndim >= 3 and k.ndim >= 3 and q.shape[-3] != k.shape[-3] \
+            and k.shape[-3] != 1 and q.shape[-3] != 1:
+        raise ValueError("query and key heads differ: pass enable_gqa=True")
+    ell = logits(q, k, attn_mask, is_causal, scale, enable_gqa)
+    _, vv = _expand_kv(q, k, v, enable_gqa)
+    m, w, rowsum, (nan_row, inf_row, empty_row, normal) = _softmax_parts(ell)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(normal[..., None], w / np.where(normal, rowsum, 1.0)[..., None], 0.0)
+        p = np.where((nan_row | inf_row)[..., None], np.nan, p)
+        out = np.matmul(p, vv)
+        lse = np.where(normal, m + np.log(np.where(normal, rowsum, 1.0)), 0.0)
+    lse = np.where(empty_row, -np.inf, lse)
+    lse = np.where(inf_row, np.inf, lse)
+    lse = np.where(nan_row, np.nan, lse)
+    return out, lse
+
+
+def block_diagonal_bias(lengths_q, lengths_k=None, causal=False):
+    """(total_q, total_k) bias of a block-diagonal mask over packed segments.
+
+    insureai360 tutorial, section 4 (``BlockDiagonalMask`` / ``BlockDiagonalCausalMask``):
+    a query sees only keys of its own segment; the causal form also removes keys
+    whose local index exceeds the query's local index.
+    """
+    if lengths_k is None:
+        lengths_k = lengths_q
+    tq, tk = int(sum(lengths_q)), int(sum(lengths_k))
+    bias = np.full((tq, tk), -np.inf)
+    oq = ok = 0
+    for lq, lk in zip(lengths_q, lengths_k):
+        block = causal_bias(lq, lk) if causal else np.zeros((lq, lk))
+        bias[oq:oq + lq, ok:ok + lk] = block
+        oq += lq
+        ok += lk
+    return bias
+
+
+def sdpa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, is_causal=False, scale=None,
+                enable_gqa=False, dropout_p=0.0):
+    """Packed variable-length attention with a block-diagonal mask.
+
+    q (total_q, Hq, E), k (total_k, Hkv, E), v (total_k, Hkv, Ev) packed along
+    the token axis; cu_seqlens are the n+1 cumulative segment offsets.  Returns
+    out (total_q, Hq, Ev) and lse (Hq, total_q), float64.  Each segment is
+    computed on its own, which equals the block-diagonal mask over the packed
+    tensors exactly (see the module docstring).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).ravel()]
+    ck = cq if cu_seqlens_k is None else [int(x) for x in np.asarray(cu_seqlens_k).ravel()]
+    Hq, Ev = q.shape[1], v.shape[2]
+    out = np.zeros((q.shape[0], Hq, Ev))
+    lse = np.full((Hq, q.shape[0]), -np.inf)
+    for s in range(len(cq) - 1):
+        a, b = cq[s], cq[s + 1]
+        c, d = ck[s], ck[s + 1]
+        if b == a:
+            continue
+        qs = np.swapaxes(q[a:b], 0, 1)  # (Hq, lq, E)
+        ks = np.swapaxes(k[c:d], 0, 1)
+        vs = np.swapaxes(v[c:d], 0, 1)
+        o, l_ = sdpa(qs, ks, vs, dropout_p=dropout_p, is_causal=is_causal, scale=scale,
+                     enable_gqa=enable_gqa)
+        out[a:b] = np.swapaxes(o, 0, 1)
+        lse[:, a:b] = l_
+    return out, lse
+
+
+def entropy(p):
+    """Attention entropy -sum_j p_j log p_j per row, in nats (0 log 0 = 0)."""
+    p = np.asarray(p, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    return -t.sum(axis=-1)

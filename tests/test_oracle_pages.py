@@ -1,0 +1,383 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these tests touches the GPU or the HIP library.  Each pin checks the
+oracle against something other than itself: numbers the exactref.ai page
+prints, closed forms, brute force in pure Python on tiny inputs, PyTorch's own
+CPU attention in float64, or statistical facts the pages derive.
+"""
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_oracle as O
+from transformer_attention_04_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# exactref.ai "scaled_dot_product_attention", section "Examples"
+Q3 = np.array([[[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]])
+K3 = np.array([[[1.0, 0.0], [0.0, 1.0], [0.5, 0.5]]])
+V3 = np.array([[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]]])
+
+
+def _variant(name):
+    if name == "default":
+        return O.sdpa(Q3, K3, V3)
+    if name == "causal":
+        return O.sdpa(Q3, K3, V3, is_causal=True)
+    if name == "masked_key1":
+        mask = np.array([[0.0, -np.inf, 0.0]] * 3, dtype=np.float32)
+        return O.sdpa(Q3, K3, V3, attn_mask=mask)
+    if name == "scale1":
+        return O.sdpa(Q3, K3, V3, scale=1.0)
+    raise KeyError(name)
+
+
+def test_worked_example_bit_exact_in_float32():
+    """All printed outputs of the worked example, as float32, bit for bit."""
+    rows = _golden("exactref_worked_example.txt")
+    assert len(rows) == 12
+    for variant, r, a, b in rows:
+        out, _ = _variant(variant)
+        got = out[0, int(r)].astype(np.float32)
+        want = np.array([float(a), float(b)], dtype=np.float32)
+        assert got.tobytes() == want.tobytes(), (variant, r, got, want)
+
+
+def test_worked_example_shapes():
+    """Output (1, 3, 2) and logsumexp (1, 3) (section "Examples")."""
+    out, lse = O.sdpa(Q3, K3, V3)
+    assert out.shape == (1, 3, 2)
+    assert lse.shape == (1, 3)
+
+
+def test_worked_example_lse_closed_forms():
+    """lse rows by hand: log of the sum of exp(logits)."""
+    _, lse = O.sdpa(Q3, K3, V3)
+    s = 1 / math.sqrt(2)
+    assert lse[0, 0] == pytest.approx(math.log(math.exp(s) + 1 + math.exp(0.5 * s)), abs=1e-15)
+    # query 2 scores (1, 1, 1): three equal logits 1/sqrt(2)
+    assert lse[0, 2] == pytest.approx(s + math.log(3), abs=1e-15)
+    _, lc = O.sdpa(Q3, K3, V3, is_causal=True)
+    assert lc[0, 0] == pytest.approx(s, abs=1e-15)  # only key 0: logit q0.k0 * s
+    assert lc[0, 1] == pytest.approx(math.log(1 + math.exp(s)), abs=1e-15)
+    _, l1 = O.sdpa(Q3, K3, V3, scale=1.0)
+    assert l1[0, 0] == pytest.approx(math.log(math.e + 1 + math.exp(0.5)), abs=1e-15)
+
+
+def test_equal_scores_give_mean_of_values():
+    """Query 2 scores every key alike, so its output is exactly the mean of V."""
+    out, _ = O.sdpa(Q3, K3, V3)
+    assert np.array_equal(out[0, 2], [3.0, 4.0])
+    out, _ = O.sdpa(Q3, K3, V3, is_causal=True)
+    assert np.array_equal(out[0, 0], V3[0, 0])  # causal row 0 sees only key 0
+
+
+def test_gqa_example_shape_and_values():
+    """exactref.ai "Masks, causality and scale": 2 query heads share 1 key/value head.
+
+    Printed shape (1, 2, 1, 2).  Query head 1 (q=[0,1]) faces the keys [1,0],
+    [0,1] of the causal worked example's row 1, so its output equals that
+    printed row; by the symmetry of the two keys, head 0 = (4, 6) - head 1.
+    """
+    gq = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])
+    gk = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    gv = np.array([[[[1.0, 2.0], [3.0, 4.0]]]])
+    out, lse = O.sdpa(gq, gk, gv, enable_gqa=True)
+    assert out.shape == (1, 2, 1, 2) and lse.shape == (1, 2, 1)
+    want1 = np.array([2.3395230770111084, 3.3395230770111084], dtype=np.float32)
+    assert out[0, 1, 0].astype(np.float32).tobytes() == want1.tobytes()
+    assert out[0, 0, 0] == pytest.approx(np.array([4.0, 6.0]) - out[0, 1, 0], abs=1e-14)
+    # without enable_gqa a single key head still broadcasts, as batch dims do
+    assert np.array_equal(O.sdpa(gq, gk, gv)[0], out)
+    with pytest.raises(ValueError):  # but 4 query heads over 2 key heads need enable_gqa
+        O.sdpa(np.zeros((1, 4, 1, 2)), np.zeros((1, 2, 2, 2)), np.zeros((1, 2, 2, 2)))
+
+
+def test_gqa_grouping_is_contiguous_against_torch():
+    """Head h uses key head h // (Hq/Hkv): PyTorch's enable_gqa in float64 agrees."""
+    q, k, v = inputs.randn_qkv((2, 8, 5, 16), (2, 2, 7, 16), (2, 2, 7, 16), "fp32", seed=3)
+    out, lse = O.sdpa(q, k, v, enable_gqa=True, is_causal=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.double(), k.double(), v.double(), is_causal=True, enable_gqa=True)
+    assert np.abs(out - ref.numpy()).max() < 1e-12
+
+
+def test_special_values():
+    """exactref.ai "Special values and dropout" and "Full specification"."""
+    qn = np.array([[[np.nan, 0.0]]])
+    out, lse = O.sdpa(qn, K3, V3)
+    assert np.isnan(out).all() and np.isnan(lse).all()
+    # a row with no kept key: output 0, lse -inf
+    mask = np.array([[-np.inf, -np.inf, -np.inf], [0, 0, 0], [0, 0, 0]])
+    out, lse = O.sdpa(Q3, K3, V3, attn_mask=mask)
+    assert np.array_equal(out[0, 0], [0.0, 0.0]) and lse[0, 0] == -np.inf
+    assert np.isfinite(out[0, 1:]).all()
+    bmask = np.array([[False] * 3, [True] * 3, [True] * 3])
+    out_b, lse_b = O.sdpa(Q3, K3, V3, attn_mask=bmask)
+    assert np.array_equal(out_b, out) and np.array_equal(lse_b, lse)
+    # a +inf logit: output NaN, lse +inf
+    pmask = np.array([[np.inf, 0, 0], [0, 0, 0], [0, 0, 0]])
+    out, lse = O.sdpa(Q3, K3, V3, attn_mask=pmask)
+    assert np.isnan(out[0, 0]).all() and lse[0, 0] == np.inf
+    # a non-finite value at a key of weight 0 gives NaN (0 * inf)
+    vinf = V3.copy()
+    vinf[0, 1, 0] = np.inf
+    out, _ = O.sdpa(Q3, K3, vinf, attn_mask=np.array([[0.0, -np.inf, 0.0]] * 3))
+    assert np.isnan(out[0, :, 0]).all() and np.isfinite(out[0, :, 1]).all()
+    # and at a key of positive weight gives that infinity
+    out, _ = O.sdpa(Q3, K3, vinf)
+    assert (out[0, :, 0] == np.inf).all()
+    with pytest.raises(ValueError, match="dropout"):
+        O.sdpa(Q3, K3, V3, dropout_p=0.1)
+
+
+def test_empty_head_dim_gives_mask_only_logits():
+    """Full specification: with E = 0 the scores are 0 and the logits are the mask alone."""
+    q = np.zeros((1, 2, 0))
+    k = np.zeros((1, 3, 0))
+    v = np.array([[[1.0], [2.0], [3.0]]])
+    out, lse = O.sdpa(q, k, v)
+    assert np.allclose(out[0, :, 0], 2.0) and np.allclose(lse, math.log(3))
+    mask = np.array([[0.0, math.log(2), -np.inf], [0.0, 0.0, 0.0]])
+    out, _ = O.sdpa(q, k, v, attn_mask=mask)
+    assert out[0, 0, 0] == pytest.approx((1 * 1 + 2 * 2) / 3)
+
+
+def test_padding_mask_with_lowest_float():
+    """exactref.ai "Padding masks": the float64 oracle gives PyTorch's [1.5], [1.0].
+
+    The page's exact answer for query 0 is ~1.119, but its printed finite range
+    for a correct implementation that rounds the logits is [1.4999989, 1.5000012];
+    in float64 the score is erased by the huge mask value just as in float32.
+    """
+    low = float(np.finfo(np.float32).min)
+    rows = {(r[0], int(r[1])): float(r[2]) for r in _golden("exactref_padding_mask.txt")}
+    query = np.array([[[1.0], [0.5]]])
+    key = np.array([[[1.0], [-1.0]]])
+    value = np.array([[[1.0], [2.0]]])
+    mask = np.array([[[low, low], [0.0, low]]], dtype=np.float32)
+    out, _ = O.sdpa(query, key, value, attn_mask=mask)
+    assert out[0, 0, 0] == rows[("pytorch", 0)]
+    assert out[0, 1, 0] == rows[("pytorch", 1)]
+    assert rows[("finite_range_low", 0)] <= out[0, 0, 0] <= rows[("finite_range_high", 0)]
+
+
+def _brute(q, k, v, bias, scale):
+    """Pure-Python loops over one head: q (L,E), k (S,E), v (S,Ev), bias (L,S)."""
+    L, S, Ev = len(q), len(k), len(v[0]) if len(v) else 0
+    out, lse = [], []
+    for i in range(L):
+        ell = []
+        for j in range(S):
+            d = 0.0
+            for e in range(len(q[i])):
+                d += float(q[i][e]) * float(k[j][e])
+            ell.append(scale * d + float(bias[i][j]))
+        m = max(ell)
+        if m == -math.inf:
+            out.append([0.0] * Ev)
+            lse.append(-math.inf)
+            continue
+        w = [math.exp(x - m) for x in ell]
+        tot = sum(w)
+        out.append([sum(w[j] / tot * float(v[j][c]) for j in range(S)) for c in range(Ev)])
+        lse.append(m + math.log(tot))
+    return np.array(out), np.array(lse)
+
+
+@pytest.mark.parametrize("causal,masked,scale", [(False, False, None), (True, False, None),
+                                                 (False, True, 0.7), (True, True, -1.3)])
+def test_against_brute_force_loops(causal, masked, scale):
+    """Small random heads (L != S, E != Ev) against pure-Python loops."""
+    rng = np.random.default_rng(7)
+    B, H, L, S, E, Ev = 2, 3, 5, 7, 4, 3
+    q, k, v = rng.normal(size=(B, H, L, E)), rng.normal(size=(B, H, S, E)), rng.normal(size=(B, H, S, Ev))
+    mask = None
+    if masked:
+        mask = rng.normal(size=(H, L, S))
+        mask[rng.random(size=mask.shape) < 0.3] = -np.inf
+    out, lse = O.sdpa(q, k, v, attn_mask=mask, is_causal=causal, scale=scale)
+    sc = 1 / math.sqrt(E) if scale is None else scale
+    for b in range(B):
+        for h in range(H):
+            bias = np.zeros((L, S)) if mask is None else mask[h].copy()
+            if causal:
+                bias = bias + np.where(np.arange(S)[None] <= np.arange(L)[:, None], 0.0, -np.inf)
+            ro, rl = _brute(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), bias.tolist(), sc)
+            assert np.allclose(out[b, h], ro, atol=1e-13, rtol=0)
+            assert np.array_equal(np.isneginf(lse[b, h]), np.isneginf(rl))
+            fin = np.isfinite(rl)
+            assert np.allclose(lse[b, h][fin], rl[fin], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_against_torch_math_float64(causal):
+    """PyTorch's CPU attention in float64 as an independent library routine."""
+    q, k, v = inputs.randn_qkv((2, 3, 33, 24), (2, 3, 41, 24), (2, 3, 41, 16), "fp32", seed=11)
+    mask = torch.randn(3, 33, 41, generator=torch.Generator().manual_seed(2), dtype=torch.float64)
+    for m in (None, mask):
+        out, lse = O.sdpa(q, k, v, attn_mask=m, is_causal=causal and m is None)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.double(), k.double(), v.double(), attn_mask=m, is_causal=causal and m is None)
+        assert np.abs(out - ref.numpy()).max() < 1e-12
+        ell = O.logits(q, k, attn_mask=m, is_causal=causal and m is None)
+        assert np.abs(lse - torch.logsumexp(torch.from_numpy(ell), -1).numpy()).max() < 1e-12
+
+
+def test_checking_pytorch_seeded_example():
+    """exactref.ai "Checking PyTorch": random.Random(0) gauss draws, (1,2,8,16), causal."""
+    rng = random.Random(0)
+
+    def randn(*shape):
+        vals = [rng.gauss(0, 1) for _ in range(math.prod(shape))]
+        return torch.tensor(vals).reshape(shape)
+
+    tq, tk, tv = randn(1, 2, 8, 16), randn(1, 2, 8, 16), randn(1, 2, 8, 16)
+    out, _ = O.sdpa(tq, tk, tv, is_causal=True)
+    ref32 = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    # PyTorch's float32 result lies within float32 rounding of the exact value
+    assert np.abs(out - ref32.double().numpy()).max() < 1e-5
+    ref64 = torch.nn.functional.scaled_dot_product_attention(
+        tq.double(), tk.double(), tv.double(), is_causal=True)
+    assert np.abs(out - ref64.numpy()).max() < 1e-13
+
+
+def test_causal_equals_explicit_masks():
+    """is_causal = a -inf upper-triangle float mask = a bool lower-triangle mask."""
+    q, k, v = inputs.randn_qkv((1, 2, 9, 8), (1, 2, 9, 8), (1, 2, 9, 8), "fp32", seed=5)
+    a, la = O.sdpa(q, k, v, is_causal=True)
+    fm = np.triu(np.full((9, 9), -np.inf), 1)
+    b, lb = O.sdpa(q, k, v, attn_mask=fm)
+    c, lc = O.sdpa(q, k, v, attn_mask=np.tril(np.ones((9, 9), dtype=bool)))
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert np.array_equal(la, lb) and np.array_equal(la, lc)
+    # mask and causal together: the kept set is the intersection
+    m = np.zeros((9, 9))
+    m[:, 0] = -np.inf
+    d, _ = O.sdpa(q, k, v, attn_mask=m, is_causal=True)
+    e, _ = O.sdpa(q, k, v, attn_mask=m + fm)
+    assert np.array_equal(d, e)
+
+
+def test_single_key():
+    """S = 1: out = v0 and lse = the one logit."""
+    q, k, v = inputs.randn_qkv((1, 1, 4, 8), (1, 1, 1, 8), (1, 1, 1, 8), "fp32", seed=9)
+    out, lse = O.sdpa(q, k, v, scale=0.5)
+    assert np.allclose(out[0, 0], v.double().numpy()[0, 0, 0][None], atol=1e-15)
+    want = 0.5 * (q.double().numpy()[0, 0] @ k.double().numpy()[0, 0, 0])
+    assert np.allclose(lse[0, 0], want, atol=1e-14)
+
+
+def test_equal_keys_give_uniform_weights():
+    """All keys equal: every kept key has weight 1/n_kept and out is the mean of kept V."""
+    q, _, v = inputs.randn_qkv((1, 1, 6, 8), (1, 1, 6, 8), (1, 1, 6, 8), "fp32", seed=4)
+    k = torch.ones(1, 1, 6, 8)
+    p = O.weights(q, k, is_causal=True)
+    for i in range(6):
+        assert np.allclose(p[0, 0, i, : i + 1], 1.0 / (i + 1), atol=1e-15)
+    out, _ = O.sdpa(q, k, v, is_causal=True)
+    vv = v.double().numpy()[0, 0]
+    for i in range(6):
+        assert np.allclose(out[0, 0, i], vv[: i + 1].mean(0), atol=1e-14)
+
+
+def test_rows_sum_to_one():
+    q, k, _ = inputs.randn_qkv((2, 2, 17, 32), (2, 2, 23, 32), (2, 2, 23, 32), "fp32", seed=6)
+    p = O.weights(q, k, is_causal=True, scale=1.0)
+    assert np.abs(p.sum(-1) - 1).max() < 1e-12
+
+
+def test_key_partition_merges_to_whole():
+    """lse over a key partition merges to the whole: the identity a split-KV pass relies on."""
+    q, k, v = inputs.randn_qkv((1, 2, 3, 16), (1, 2, 50, 16), (1, 2, 50, 16), "fp32", seed=8)
+    o, l = O.sdpa(q, k, v)
+    parts = [(0, 13), (13, 14), (14, 50)]
+    os_, ls = zip(*[O.sdpa(q, k[:, :, a:b], v[:, :, a:b]) for a, b in parts])
+    lm = np.logaddexp.reduce(np.stack(ls), axis=0)
+    om = sum(np.exp(li - lm)[..., None] * oi for oi, li in zip(os_, ls))
+    assert np.abs(lm - l).max() < 1e-13 and np.abs(om - o).max() < 1e-13
+
+
+def test_prescaled_query_with_unit_scale():
+    """exactref.ai Full specification / hourtab fix: pre-scaled q with scale=1 = default."""
+    q, k, v = inputs.randn_qkv((1, 4, 12, 96), (1, 4, 12, 96), (1, 4, 12, 96), "fp32", seed=1)
+    a, la = O.sdpa(q, k, v, is_causal=True)
+    b, lb = O.sdpa(q.double() / math.sqrt(96), k, v, is_causal=True, scale=1.0)
+    assert np.abs(a - b).max() < 1e-13 and np.abs(la - lb).max() < 1e-13
+
+
+def test_block_diagonal_equals_per_segment():
+    """insureai360 tutorial section 4: packed segments under a block-diagonal (causal) mask."""
+    lengths = [3, 7, 1, 5]
+    for causal in (False, True):
+        q, k, v, cu = inputs.varlen_inputs(lengths, 2, 2, 8, "fp32", seed=2)
+        out, lse = O.sdpa_varlen(q[0], k[0], v[0], cu.numpy(), is_causal=causal)
+        bias = O.block_diagonal_bias(lengths, causal=causal)
+        qa, ka, va = (t[0].transpose(0, 1) for t in (q, k, v))  # (H, total, E)
+        ref, rl = O.sdpa(qa, ka, va, attn_mask=bias)
+        assert np.abs(out - np.swapaxes(ref, 0, 1)).max() < 1e-14
+        assert np.abs(lse - rl).max() < 1e-14
+        # segment 0 alone equals plain attention on its own tokens
+        s0 = lengths[0]
+        o0, _ = O.sdpa(qa[:, :s0], ka[:, :s0], va[:, :s0], is_causal=causal)
+        assert np.abs(out[:s0] - np.swapaxes(o0, 0, 1)).max() < 1e-15
+
+
+def test_score_variance_matches_head_dim():
+    """khchao.com NN Lab variance proof and lynx-cortex Break 00: Var(q.k) = d_k for N(0,1) inputs.
+
+    At scale 1 the logit variance is ~d_k (96 here); at 1/sqrt(d_k) it is ~1.
+    """
+    q, k, _ = inputs.randn_qkv((1, 1, 2048, 96), (1, 1, 2048, 96), (1, 1, 1, 96), "fp32", seed=0)
+    v1 = O.logits(q, k, scale=1.0).var()
+    vs = O.logits(q, k).var()
+    assert abs(v1 / 96 - 1) < 0.05
+    assert abs(vs - 1) < 0.05
+
+
+def test_double_scaling_gives_near_uniform_weights():
+    """hourtab.com retainer write-up: effective scale 1/head_dim makes attention near uniform.
+
+    With N(0,1) inputs at E=96 and scale 1/96 the entropy of every row is
+    within 0.02 nats of log S and no weight exceeds 2/S; causal rows are near
+    uniform over their own kept keys.
+    """
+    S = 2048
+    q, k, _ = inputs.randn_qkv((1, 1, S, 96), (1, 1, S, 96), (1, 1, 1, 96), "fp32", seed=0)
+    p = O.weights(q, k, scale=1 / 96)
+    ent = O.entropy(p)
+    assert ent.min() >= math.log(S) - 0.02
+    assert S * p.max() < 2
+    pc = O.weights(q, k, scale=1 / 96, is_causal=True)
+    ent_c = O.entropy(pc)[0, 0]
+    n = np.arange(1, S + 1)
+    assert (ent_c >= np.log(n) - 0.02).all()
+    # the correctly scaled head is far from uniform
+    assert O.entropy(O.weights(q, k)).mean() < math.log(S) - 0.3
+
+
+def test_workload_recipe_is_deterministic():
+    a = inputs.randn_qkv((1, 2, 3, 4), (1, 2, 3, 4), (1, 2, 3, 4), "bf16", seed=0)
+    b = inputs.randn_qkv((1, 2, 3, 4), (1, 2, 3, 4), (1, 2, 3, 4), "bf16", seed=0)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    lengths = inputs.segment_lengths()
+    assert len(lengths) == 32 and min(lengths) >= 8 and max(lengths) <= 2048
+    assert sum(lengths) == 32998 and max(lengths) == 1837
+    bias = inputs.alibi_causal_bias(4, 5, 5)
+    assert bias.dtype == torch.float32 and torch.isinf(bias[0, 0, 1]) and bias[0, 3, 1] < 0
