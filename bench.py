@@ -1,0 +1,267 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|main|decode|...]
+
+A step is one pass of the hot path over one batch of synthetic input: one
+sdpa_fwd call on the causal bf16 workload B=4, H=16, L=S=2048, E=128 (the
+headline configuration).  The JSON line reports its attention TFLOP/s with
+the matrix-core roofline of the prefill kernel, the CPU oracle timed on the
+host cores on a bounded sample of the same workload, and (under "secondary")
+the other workloads: split-KV GQA decode in GB/s against the HBM roofline,
+the GPT-NeoX-shaped E=96 variants, packed variable-length fp16 and the
+single-head fp32 case.
+
+Algorithmic work (what the method must do, not what a kernel happens to do):
+flops = (2E + 2Ev) x kept (query, key) pairs; bytes = Q + K + V + O + lse
+(+ the float mask over the kept region when one is read), K/V counted once per
+key/value head.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 matrix peak: 256 CUs x 2.4 GHz x 4096 flop/clk
+PEAK_FP32_TFLOPS = 157.3    # fp32 matrix peak (the fp32 path runs on the vector ALUs)
+PEAK_HBM_GBS = 8000.0       # HBM3E
+METRIC = "attn fwd TFLOP/s (% MFMA peak) prefill; GB/s (% HBM peak) split-KV decode"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["prefill_mfma.h", "device_utils.h", "attn_common.h", "decode.hip"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_attention_04_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def causal_pairs(L, S):
+    """Kept (i, j) pairs with j <= i for one head."""
+    return sum(min(i + 1, S) for i in range(L))
+
+
+def flops_prefill(B, H, L, S, E, causal):
+    pairs = causal_pairs(L, S) if causal else L * S
+    return 4 * E * pairs * B * H, pairs
+
+
+def time_launches(fn, steps, warmup):
+    """Run fn warmup times, then time `steps` calls: wall time between two
+    synchronizes, plus one event pair per call on torch's current stream (the
+    stream the kernels are launched on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]  # ms
+    return wall, per
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if the kernels are unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The float64 oracle on the host cores, on whole heads of the headline workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import sdpa_oracle as O
+    from transformer_attention_04_amd import inputs
+    q, k, v = inputs.workload_inputs("bf16_causal_e128")
+    B, H, L, E = q.shape
+    per_head_flops = flops_prefill(1, 1, L, L, E, True)[0]
+    done, t0 = 0, time.perf_counter()
+    order = [(b, h) for b in range(B) for h in range(H)]
+    while done < len(order) and time.perf_counter() - t0 < budget_s:
+        b, h = order[done]
+        O.sdpa(q[b, h], k[b, h], v[b, h], is_causal=True)
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(per_head_flops * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} heads (causal, L=S={L}, E={E}) in {dt:.1f} s, float64 numpy"}
+
+
+def bench_prefill(name, steps, warmup, scale=None, mask=None, device="cuda"):
+    import torch
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    w = inputs.WORKLOADS[name]
+    q, k, v = (t.to(device) for t in inputs.workload_inputs(name))
+    md = mask.to(device) if mask is not None else None
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1] + (1,), dtype=torch.float32, device=device)
+    fn = lambda: S.sdpa_fwd(q, k, v, attn_mask=md, is_causal=w["causal"], scale=scale, out=out, lse=lse)
+    wall, per = time_launches(fn, steps, warmup)
+    flops, pairs = flops_prefill(w["B"], w["Hq"], w["L"], w["S"], w["E"], w["causal"])
+    kern_ms = sum(per) / len(per)
+    res = {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "flops": flops,
+           "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12}
+    if mask is not None:
+        qkvo = 2 * (q.numel() + k.numel() + v.numel() + q.numel())
+        mbytes = 4 * pairs * w["Hq"] * (1 if mask.dim() == 3 else w["B"])
+        res["bytes"] = qkvo + 4 * q.numel() // w["E"] + mbytes
+        res["gbs"] = res["bytes"] / (kern_ms * 1e-3) / 1e9
+    return res
+
+
+def bench_decode(steps, warmup, device="cuda"):
+    import torch
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    q, k, v = (t.to(device) for t in inputs.workload_inputs("bf16_gqa_decode"))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1] + (1,), dtype=torch.float32, device=device)
+    nws = S.sdpa_fwd_workspace_size(q, k, v, enable_gqa=True)
+    ws = torch.empty(nws, dtype=torch.uint8, device=device)
+    fn = lambda: S.sdpa_fwd(q, k, v, enable_gqa=True, out=out, lse=lse, workspace=ws)
+    wall, per = time_launches(fn, steps, warmup)
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+    kern_ms = sum(per) / len(per)
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "bytes": nbytes,
+            "gbs": nbytes / (kern_ms * 1e-3) / 1e9, "frac_hbm": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "workspace_bytes": nws}
+
+
+def bench_varlen(steps, warmup, device="cuda"):
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    w = inputs.WORKLOADS["fp16_varlen_e64"]
+    lengths = inputs.segment_lengths(seed=w["len_seed"])
+    q, k, v, cu = (t.to(device) for t in inputs.varlen_inputs(lengths, w["Hq"], w["Hkv"], w["E"], "fp16",
+                                                                seed=w["seed"]))
+    mx = max(lengths)
+    fn = lambda: S.sdpa_fwd_varlen(q, k, v, cu, max_seqlen_q=mx, max_seqlen_k=mx, is_causal=True)
+    wall, per = time_launches(fn, steps, warmup)
+    pairs = sum(l * (l + 1) // 2 for l in lengths)
+    flops = 4 * w["E"] * pairs * w["Hq"]
+    kern_ms = sum(per) / len(per)
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "flops": flops,
+            "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12, "total_tokens": sum(lengths)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default="all",
+                    help="all | main | decode | neox | varlen | fp32 (comma separated)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    from transformer_attention_04_amd import sdpa as S
+    from transformer_attention_04_amd import inputs
+    S.load_library()
+    sel = set(a.workloads.split(","))
+    run_all = "all" in sel
+
+    secondary = {}
+    main_res = None
+    if run_all or "main" in sel:
+        main_res = bench_prefill("bf16_causal_e128", a.steps, a.warmup)
+        print(f"# bf16_causal_e128: {main_res['kernel_ms'] * 1e3:.1f} us/launch, "
+              f"{main_res['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if run_all or "decode" in sel:
+        d = bench_decode(max(5, a.steps // 2), min(a.warmup, 5))
+        secondary["bf16_gqa_decode"] = {"metric": "GB/s", "value": round(d["gbs"], 1),
+                                        "frac_hbm_peak": round(d["frac_hbm"], 4),
+                                        "kernel_us": round(d["kernel_ms"] * 1e3, 1),
+                                        "bytes_per_call": d["bytes"],
+                                        "traffic": load_traffic("decode_split_kernel"),
+                                        "kernels": "decode_split_kernel + decode_merge_kernel"}
+        print(f"# bf16_gqa_decode: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    if run_all or "neox" in sel:
+        for tag, sc in (("1/sqrt96", None), ("1/96", 1 / 96), ("1.0", 1.0)):
+            r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), scale=sc)
+            secondary[f"bf16_neox_e96 scale={tag}"] = {
+                "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+                "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
+        bias = inputs.alibi_causal_bias(64, 2048, 2048)
+        r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), mask=bias)
+        secondary["bf16_neox_e96 alibi+causal"] = {
+            "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+            "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "gbs": round(r["gbs"], 1), "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
+        del bias
+    if run_all or "varlen" in sel:
+        r = bench_varlen(max(5, a.steps // 2), min(a.warmup, 5))
+        secondary["fp16_varlen_e64"] = {"metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+                                        "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                                        "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
+    if run_all or "fp32" in sel:
+        r = bench_prefill("fp32_single_head", max(5, a.steps // 2), min(a.warmup, 5))
+        secondary["fp32_single_head"] = {"metric": "us per call", "value": round(r["kernel_ms"] * 1e3, 2),
+                                         "tflops": round(r["kernel_tflops"], 3)}
+
+    if main_res is None:
+        print(json.dumps({"secondary": secondary}))
+        return 0
+    w = inputs.WORKLOADS["bf16_causal_e128"]
+    achieved = main_res["kernel_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q, K, V i.i.d. N(0,1) (seed 0) rounded to bf16",
+        "config": {"workload": "bf16_causal_e128", "B": w["B"], "H": w["Hq"], "L": w["L"], "S": w["S"],
+                   "E": w["E"], "is_causal": True, "scale": "1/sqrt(128)", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic("prefill_mfma_kernel"),
+                     "kernel": "prefill_mfma_kernel<BF16,128,causal>",
+                     "flop_per_launch": main_res["flops"]},
+        "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline(),
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

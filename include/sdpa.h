@@ -1,0 +1,167 @@
+/*
+ * libsdpa: exact scaled dot-product attention, forward pass, for AMD MI355X (gfx950).
+ *
+ * The operation (exactref.ai, "scaled_dot_product_attention", sections
+ * "Arguments" and "Full specification"): for query (..., L, E), key (..., S, E)
+ * and value (..., S, Ev)
+ *
+ *     out = softmax(scale * Q K^T + mask) V     over the key axis
+ *     lse = log(sum_j exp(scale * q.k_j + mask_j))   per query row
+ *
+ * with scale = 1/sqrt(E) unless given, the mask added after scaling, a causal
+ * option that keeps key j for query i only when j <= i (counted from the
+ * top-left corner), and grouped-query heads where query head h reads key/value
+ * head h / (Hq / Hkv).  A row with no kept key has output 0 and lse -inf.  The
+ * output has the inputs' dtype, rounded to nearest-even; lse is float32.
+ *
+ * Conventions for every entry point
+ *  - All data pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller; the library allocates nothing, keeps no state beyond its code
+ *    objects and a per-thread error string, and never frees caller memory.
+ *  - Sizes and strides are in ELEMENTS.  The last dimension of q, k, v, out and
+ *    a mask must have stride 1.  bf16/fp16 tensors need 16-byte aligned base
+ *    pointers and row strides that are multiples of 8 elements; fp32 tensors
+ *    16-byte aligned bases and row strides that are multiples of 4.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
+ *    default stream).  Inputs must stay alive and unmodified, and outputs must
+ *    not be read, until the stream reaches that point.  out and lse must not
+ *    overlap any input.
+ *  - Argument errors are detected on the host before anything is enqueued:
+ *    the call returns a non-zero status and sdpa_last_error() describes it.
+ *    No C++ exception crosses this interface.
+ *  - Head dims supported by the kernels: E == Ev, E in {64, 96, 128}.
+ *    E = 0 (an empty score sum) is valid for the operation but not handled by
+ *    the kernels: it returns SDPA_ERR_UNSUPPORTED.
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDPA_OK = 0,
+    SDPA_ERR_INVALID_ARGUMENT = 1, /* shapes, dropout, GQA ratio, mask, workspace */
+    SDPA_ERR_UNSUPPORTED = 2,      /* valid operation outside what the kernels cover */
+    SDPA_ERR_DEVICE = 3            /* a HIP runtime error while enqueueing */
+} sdpa_status;
+
+typedef enum {
+    SDPA_F32 = 0,
+    SDPA_F16 = 1,
+    SDPA_BF16 = 2,
+    SDPA_BOOL = 3 /* one byte per element, non-zero keeps the key */
+} sdpa_dtype;
+
+/* A strided 4-D device tensor.  size[] and stride[] are in elements. */
+typedef struct {
+    void* data;
+    int64_t size[4];
+    int64_t stride[4];
+} sdpa_tensor4;
+
+/*
+ * sdpa_fwd -- batched attention forward.
+ *
+ *   dtype      element type of q, k, v and out: SDPA_BF16, SDPA_F16 or SDPA_F32.
+ *   q          (B, Hq,  L, E)
+ *   k          (B, Hkv, S, E)
+ *   v          (B, Hkv, S, Ev)
+ *   attn_mask  NULL, or a (B|1, Hq|1, L|1, S) tensor broadcast over size-1
+ *              dims (stride 0 is fine).  mask_dtype SDPA_BOOL: non-zero keeps
+ *              the key (False removes it).  mask_dtype SDPA_F32: added to the
+ *              scaled scores, -inf removes the key (exactref.ai "Arguments").
+ *              The logit is formed as one fp32 fused multiply-add.
+ *   dropout_p  must be 0 (a random dropout has no exact reference); any other
+ *              value returns SDPA_ERR_INVALID_ARGUMENT.
+ *   is_causal  non-zero keeps key j for query i only when j <= i; combined with
+ *              attn_mask the kept set is the intersection.
+ *   scale      NULL for 1/sqrt(E), else the factor on the scores (any finite
+ *              value, negative and 0 included).
+ *   enable_gqa non-zero allows Hkv < Hq with Hq % Hkv == 0; query head h then
+ *              reads key/value head h / (Hq / Hkv).  Without it Hq == Hkv.
+ *   out        (B, Hq, L, Ev), dtype.
+ *   lse        (B, Hq, L, 1), float32 (size[3] == 1, stride[3] ignored).
+ *   workspace, workspace_bytes
+ *              device scratch for the split-KV decode path (partial outputs
+ *              and their lse).  Query the size with sdpa_fwd_workspace_size;
+ *              may be NULL/0 when that size is 0.
+ *   num_splits 0: the library picks the kernel and the split count.
+ *              -1: force the single-pass (prefill) kernel.
+ *              k >= 1: the split-KV decode kernel with k splits of the keys
+ *              (SDPA_ERR_UNSUPPORTED when the call is not eligible for it:
+ *              it needs no mask, no causal flag, bf16/fp16 and L*Hq/Hkv <= 16).
+ *   stream     hipStream_t or NULL.
+ */
+sdpa_status sdpa_fwd(sdpa_dtype dtype,
+                     const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* attn_mask, sdpa_dtype mask_dtype,
+                     double dropout_p, int is_causal, const double* scale, int enable_gqa,
+                     const sdpa_tensor4* out, const sdpa_tensor4* lse,
+                     void* workspace, size_t workspace_bytes, int num_splits,
+                     void* stream);
+
+/*
+ * sdpa_fwd_workspace_size -- bytes of workspace sdpa_fwd needs for the same
+ * arguments (0 when the single-pass kernel is chosen).  Writes *bytes; runs on
+ * the host only.
+ */
+sdpa_status sdpa_fwd_workspace_size(sdpa_dtype dtype,
+                                    const sdpa_tensor4* q, const sdpa_tensor4* k,
+                                    const sdpa_tensor4* v,
+                                    const sdpa_tensor4* attn_mask, int is_causal,
+                                    int enable_gqa, int num_splits, size_t* bytes);
+
+/*
+ * sdpa_fwd_varlen -- packed variable-length attention with a block-diagonal
+ * mask (insureai360 xFormers tutorial, section 4: BlockDiagonalMask and
+ * BlockDiagonalCausalMask over sequences concatenated along the token axis).
+ *
+ *   q    packed (total_q, Hq,  E): element (t, h, e) at q + t*q_stride_tok + h*q_stride_head + e
+ *   k    packed (total_k, Hkv, E)
+ *   v    packed (total_k, Hkv, Ev)
+ *   cu_seqlens_q, cu_seqlens_k
+ *        DEVICE int32 arrays of n_seqs + 1 non-decreasing offsets starting at
+ *        0: segment s holds tokens [cu[s], cu[s+1]).  Query segment s attends
+ *        only to key segment s; with is_causal, key j of the segment is kept
+ *        for query i of the segment when j <= i (local indices).
+ *   max_seqlen_q, max_seqlen_k
+ *        upper bounds of the segment lengths; they size the launch.  Query rows
+ *        of a segment beyond max_seqlen_q are not computed, and offsets are
+ *        clamped to [0, total] on the device, so bad offsets never read or
+ *        write out of bounds.
+ *   out  packed (total_q, Hq, Ev), dtype
+ *   lse  (Hq, total_q) float32: element (h, t) at lse + h*lse_stride_head + t
+ *
+ * The other arguments mean what they mean for sdpa_fwd.  Tokens of q outside
+ * every segment are left unwritten.
+ */
+sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
+                            const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                            const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                            const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t n_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t Hq, int32_t Hkv, int32_t E, int32_t Ev,
+                            int64_t total_q, int64_t total_k,
+                            double dropout_p, int is_causal, const double* scale,
+                            int enable_gqa,
+                            void* out, int64_t o_stride_tok, int64_t o_stride_head,
+                            float* lse, int64_t lse_stride_head,
+                            void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* sdpa_last_error(void);
+
+/* Interface version, bumped when a signature or a meaning above changes. */
+int sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H */

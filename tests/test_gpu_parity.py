@@ -1,0 +1,249 @@
+"""Parity of the HIP kernels (through the C interface) with the float64 CPU oracle.
+
+Both sides receive the same seeded inputs (the oracle gets an exact float64
+copy of the device bytes).  Bars, as the spec workload states them:
+max |GPU - oracle| <= 1e-5 for fp32 (output and lse); <= 2e-2 on the output
+and <= 1e-3 on lse for bf16 / fp16.  Rows the oracle calls special (NaN rows,
+rows with no kept key) are compared by class; elements are compared only
+where the oracle is finite.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_oracle as O
+from transformer_attention_04_amd import inputs
+from transformer_attention_04_amd import sdpa as S
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "fp16": (2e-2, 1e-3)}
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def assert_parity(out, lse, ref_out, ref_lse, dtype, what="", lse_rel=0.0):
+    """Compare with the oracle.  ``lse_rel`` adds a relative part to the lse bar, for fp32
+    cases whose logits are so large that one fp32 ulp of lse exceeds the absolute bar."""
+    tol_o, tol_l = TOL[dtype]
+    if lse_rel:
+        tol_l = tol_l + lse_rel * float(np.nanmax(np.abs(np.where(np.isfinite(ref_lse), ref_lse, 0.0))))
+    out, lse = _np(out), _np(lse)
+    assert out.shape == ref_out.shape and lse.shape == ref_lse.shape, (out.shape, ref_out.shape)
+    # special classes first
+    nan_rows = np.isnan(ref_lse)
+    assert np.isnan(lse[nan_rows]).all(), f"{what}: NaN rows not NaN in lse"
+    assert np.isnan(out[nan_rows]).all(), f"{what}: NaN rows not NaN in out"
+    empty = np.isneginf(ref_lse)
+    assert np.isneginf(lse[empty]).all(), f"{what}: empty rows must have lse -inf"
+    assert (out[empty] == 0).all(), f"{what}: empty rows must be 0"
+    fin_o = np.isfinite(ref_out)
+    fin_l = np.isfinite(ref_lse)
+    assert np.isfinite(out[fin_o]).all(), f"{what}: non-finite output where the oracle is finite"
+    eo = np.abs(out[fin_o] - ref_out[fin_o]).max(initial=0.0)
+    el = np.abs(lse[fin_l] - ref_lse[fin_l]).max(initial=0.0)
+    assert eo <= tol_o, f"{what}: max |out error| {eo:.3e} > {tol_o}"
+    assert el <= tol_l, f"{what}: max |lse error| {el:.3e} > {tol_l}"
+    return eo, el
+
+
+def run_both(q, k, v, dtype, **kw):
+    """GPU through the C interface and oracle on the host copy of the same bytes."""
+    num_splits = kw.pop("num_splits", 0)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV),
+                          attn_mask=None if kw.get("attn_mask") is None else kw["attn_mask"].to(DEV),
+                          is_causal=kw.get("is_causal", False), scale=kw.get("scale"),
+                          enable_gqa=kw.get("enable_gqa", False), num_splits=num_splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.sdpa(q, k, v, attn_mask=kw.get("attn_mask"), is_causal=kw.get("is_causal", False),
+                              scale=kw.get("scale"), enable_gqa=kw.get("enable_gqa", False))
+    return out, lse, ref_out, ref_lse
+
+
+# ---------------------------------------------------------------- fp32 workload
+
+@pytest.mark.parametrize("variant", ["default", "causal", "scale1"])
+def test_fp32_single_head_workload(variant):
+    """B=1, H=1, L=S=128, E=64 fp32, seed 0: default, is_causal and scale=1.0."""
+    q, k, v = inputs.workload_inputs("fp32_single_head")
+    kw = {"default": {}, "causal": {"is_causal": True}, "scale1": {"scale": 1.0}}[variant]
+    r = run_both(q, k, v, "fp32", **kw)
+    assert_parity(*r, "fp32", variant)
+
+
+# ------------------------------------------------------- small ragged shapes
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("E", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_shapes(dtype, E, causal):
+    """Several tiles plus a ragged tail on both axes (L != S)."""
+    q, k, v = inputs.randn_qkv((2, 3, 201, E), (2, 3, 333, E), (2, 3, 333, E), dtype, seed=E + causal)
+    r = run_both(q, k, v, dtype, is_causal=causal)
+    assert_parity(*r, dtype, f"{dtype} E={E} causal={causal}")
+    # causal with more queries than keys (rows past the last key see every key)
+    if causal:
+        q, k, v = inputs.randn_qkv((1, 2, 300, E), (1, 2, 130, E), (1, 2, 130, E), dtype, seed=3)
+        assert_parity(*run_both(q, k, v, dtype, is_causal=True), dtype, "L > S causal")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_scales(dtype):
+    q, k, v = inputs.randn_qkv((1, 2, 130, 96), (1, 2, 150, 96), (1, 2, 150, 96), dtype, seed=21)
+    for sc in (1.0, 1 / 96, -0.3, 0.0):
+        assert_parity(*run_both(q, k, v, dtype, scale=sc, is_causal=True), dtype, f"scale={sc}")
+    # scale 2.5 at E=96: |lse| reaches ~100, where one fp32 ulp is 7.6e-6; the fp32 bar
+    # gets a relative part of 2^-20 |lse| (8 ulps of the largest lse) on top of 1e-5.
+    rel = 2.0 ** -20 if dtype == "fp32" else 0.0
+    assert_parity(*run_both(q, k, v, dtype, scale=2.5, is_causal=True), dtype, "scale=2.5", lse_rel=rel)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_float_and_bool_masks(dtype):
+    E = 64
+    q, k, v = inputs.randn_qkv((2, 2, 150, E), (2, 2, 170, E), (2, 2, 170, E), dtype, seed=5)
+    g = torch.Generator().manual_seed(9)
+    fm = torch.randn(2, 2, 150, 170, generator=g)
+    fm[torch.rand(fm.shape, generator=g) < 0.2] = -math.inf
+    for causal in (False, True):
+        assert_parity(*run_both(q, k, v, dtype, attn_mask=fm, is_causal=causal), dtype, f"float mask c={causal}")
+    bm = torch.rand(150, 170, generator=g) < 0.7
+    for causal in (False, True):
+        assert_parity(*run_both(q, k, v, dtype, attn_mask=bm, is_causal=causal), dtype, f"bool mask c={causal}")
+    # a (H, L, S) mask broadcast over the batch, with an odd key count (scalar loads)
+    q, k, v = inputs.randn_qkv((2, 2, 70, E), (2, 2, 99, E), (2, 2, 99, E), dtype, seed=6)
+    hm = torch.randn(2, 70, 99, generator=g)
+    assert_parity(*run_both(q, k, v, dtype, attn_mask=hm), dtype, "broadcast float mask")
+
+
+def test_causal_equals_explicit_mask_on_gpu():
+    q, k, v = inputs.randn_qkv((1, 4, 257, 128), (1, 4, 257, 128), (1, 4, 257, 128), "bf16", seed=2)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = S.sdpa_fwd(qd, kd, vd, is_causal=True)
+    tri = torch.ones(257, 257, dtype=torch.bool).tril().to(DEV)
+    o2, l2 = S.sdpa_fwd(qd, kd, vd, attn_mask=tri)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_gqa_single_pass(dtype):
+    q, k, v = inputs.randn_qkv((2, 8, 140, 128), (2, 2, 190, 128), (2, 2, 190, 128), dtype, seed=7)
+    for causal in (False, True):
+        r = run_both(q, k, v, dtype, enable_gqa=True, is_causal=causal, num_splits=-1)
+        assert_parity(*r, dtype, f"gqa causal={causal}")
+
+
+# ----------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [64, 96, 128])
+def test_split_kv_decode(dtype, E):
+    """Few query rows per KV head over a ragged key length, several split counts."""
+    q, k, v = inputs.randn_qkv((3, 8, 1, E), (3, 2, 1000, E), (3, 2, 1000, E), dtype, seed=E)
+    ref = O.sdpa(q, k, v, enable_gqa=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = []
+    for ns in (0, 1, 3, 8, -1):
+        out, lse = S.sdpa_fwd(qd, kd, vd, enable_gqa=True, num_splits=ns)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, *ref, dtype, f"decode splits={ns}")
+        outs.append(out)
+    # two query tokens per sequence (8 rows per KV head) and plain MHA
+    q2, k2, v2 = inputs.randn_qkv((2, 8, 2, E), (2, 2, 777, E), (2, 2, 777, E), dtype, seed=1)
+    assert_parity(*run_both(q2, k2, v2, dtype, enable_gqa=True, num_splits=5), dtype, "decode L=2")
+    q3, k3, v3 = inputs.randn_qkv((2, 4, 1, E), (2, 4, 300, E), (2, 4, 300, E), dtype, seed=2)
+    assert_parity(*run_both(q3, k3, v3, dtype, num_splits=2), dtype, "decode MHA")
+    # more splits than key blocks: empty splits must drop out of the merge
+    assert_parity(*run_both(q3, k3, v3, dtype, num_splits=7), dtype, "decode empty splits")
+
+
+# ---------------------------------------------------------------- varlen
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_small(dtype, causal):
+    """The insureai360 tutorial's packed batch: seqlens [37, 120, 8, 200], H=8, K=64."""
+    lengths = [37, 120, 8, 200]
+    q, k, v, cu = inputs.varlen_inputs(lengths, 8, 8, 64, dtype, seed=4)
+    out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), is_causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa_varlen(q[0], k[0], v[0], cu.numpy(), is_causal=causal)
+    assert out.shape == q.shape and lse.shape == (1, 8, sum(lengths))
+    # lse is (H, total); compare it token-major like the output
+    assert_parity(out[0], lse[0].T, ro, rl.T, dtype, f"varlen causal={causal}")
+
+
+def test_varlen_edge_segments_and_gqa():
+    lengths = [0, 1, 129, 0, 64, 300]
+    q, _, _, cu = inputs.varlen_inputs(lengths, 8, 8, 128, "bf16", seed=5)
+    _, k, v, _ = inputs.varlen_inputs(lengths, 2, 2, 128, "bf16", seed=6)
+    out, lse = S.sdpa_fwd_varlen(q[0].to(DEV), k[0].to(DEV), v[0].to(DEV), cu.to(DEV), is_causal=True,
+                                 enable_gqa=True)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa_varlen(q[0], k[0], v[0], cu.numpy(), is_causal=True, enable_gqa=True)
+    assert_parity(out, lse.T, ro, rl.T, "bf16", "varlen edges + gqa")
+
+
+# ------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_special_rows(dtype):
+    E = 64
+    q, k, v = inputs.randn_qkv((1, 2, 40, E), (1, 2, 50, E), (1, 2, 50, E), dtype, seed=8)
+    q[0, 1, 5, 3] = float("nan")   # a NaN query row
+    m = torch.zeros(1, 2, 40, 50)
+    m[0, 0, 7, :] = -math.inf      # a row with no kept key
+    r = run_both(q, k, v, dtype, attn_mask=m)
+    assert_parity(*r, dtype, "special rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_degenerate_sizes(dtype):
+    E = 128
+    # no keys at all: every row is empty (output 0, lse -inf)
+    q, k, v = inputs.randn_qkv((1, 2, 5, E), (1, 2, 0, E), (1, 2, 0, E), dtype, seed=1)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=-1)
+    assert (out.cpu().float() == 0).all() and torch.isneginf(lse.cpu()).all()
+    # one key, one query
+    q, k, v = inputs.randn_qkv((1, 1, 1, E), (1, 1, 1, E), (1, 1, 1, E), dtype, seed=2)
+    assert_parity(*run_both(q, k, v, dtype), dtype, "L=S=1")
+    # no queries: nothing to do
+    q, k, v = inputs.randn_qkv((1, 2, 0, E), (1, 2, 9, E), (1, 2, 9, E), dtype, seed=3)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    assert out.shape == (1, 2, 0, E) and lse.shape == (1, 2, 0)
+
+
+def test_worked_example_shapes_through_binding():
+    """3-D (1, L, E) input keeps its shape; lse is float32 for bf16 inputs."""
+    q, k, v = inputs.randn_qkv((1, 3, 64), (1, 3, 64), (1, 3, 64), "bf16", seed=0)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    assert out.shape == (1, 3, 64) and lse.shape == (1, 3) and lse.dtype == torch.float32
+    assert out.dtype == torch.bfloat16
+
+
+def test_prescaled_query_with_unit_scale():
+    """Pre-scaled q with scale=1 matches the default scale (hourtab fix; exactref Full specification)."""
+    q, k, v = inputs.randn_qkv((1, 4, 256, 96), (1, 4, 256, 96), (1, 4, 256, 96), "fp32", seed=3)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a, la = S.sdpa_fwd(qd, kd, vd, is_causal=True)
+    b, lb = S.sdpa_fwd(qd / math.sqrt(96), kd, vd, is_causal=True, scale=1.0)
+    assert (a - b).abs().max().item() < 1e-5 and (la - lb).abs().max().item() < 1e-5
+
+
+def test_repeatable_bit_for_bit():
+    """Two runs give identical bytes (an LDS race would show up as a difference)."""
+    q, k, v = inputs.randn_qkv((2, 4, 600, 128), (2, 4, 600, 128), (2, 4, 600, 128), "bf16", seed=1)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = S.sdpa_fwd(qd, kd, vd, is_causal=True)
+    b = S.sdpa_fwd(qd, kd, vd, is_causal=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    qd, kd, vd = (t.to(DEV) for t in inputs.randn_qkv((4, 8, 1, 128), (4, 2, 5000, 128), (4, 2, 5000, 128),
+                                                       "bf16", seed=2))
+    a = S.sdpa_fwd(qd, kd, vd, enable_gqa=True)
+    b = S.sdpa_fwd(qd, kd, vd, enable_gqa=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

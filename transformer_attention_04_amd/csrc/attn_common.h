@@ -1,0 +1,84 @@
+// Shared declarations of the attention kernels and their host launchers.
+//
+// Internal to libsdpa: the public interface is include/sdpa.h.  Every kernel
+// computes the forward pass of exact attention as the exactref.ai
+// "scaled_dot_product_attention" page specifies it (section "Full
+// specification"): softmax(scale * Q K^T + mask) V plus the per-row logsumexp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+enum MaskKind { MASK_NONE = 0, MASK_FLOAT = 1, MASK_BOOL = 2 };
+enum ElemType { ELEM_F32 = 0, ELEM_F16 = 1, ELEM_BF16 = 2 };
+
+// One launch of the single-pass kernels (MFMA bf16/fp16 and VALU fp32).
+// Strides are in elements.  Batched calls index (b, h, row); packed
+// variable-length calls index (segment, h, token) with the token offset of a
+// segment read from cu_q / cu_k.
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const void* mask;     // float32 or uint8, (b, h, row, key); key stride 1
+    const int* cu_q;      // varlen only: n_seqs + 1 offsets
+    const int* cu_k;
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int64_t o_sb, o_sh, o_sr;
+    int64_t lse_sb, lse_sh;  // lse element (b, h, i) at b*lse_sb + h*lse_sh + i (varlen: token index)
+    int64_t m_sb, m_sh, m_sr;
+    int64_t total_q, total_k;  // varlen: token counts, used to clamp offsets
+    int B;                  // batch size (varlen: number of segments)
+    int Hq, Hkv, group;     // group = Hq / Hkv
+    int L, S;               // batched: lengths; varlen: max segment lengths
+    int n_qtiles;
+    int mask_vec;           // mask rows are 16-byte aligned (vector loads allowed)
+    int neg;                // the scale is negative: q is negated on load
+    float scale_abs;        // |scale|
+    float scale_log2;       // |scale| * log2(e)
+    float scale;            // signed scale (fp32 kernel)
+};
+
+// One launch of the split-KV decode kernel and of its merge pass.
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* part_o;      // (B, Hq, L, n_splits, D) float32
+    float* part_lse;    // (B, Hq, L, n_splits)    float32
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int64_t o_sb, o_sh, o_sr;
+    int64_t lse_sb, lse_sh;
+    int B, Hq, Hkv, group, L, S;
+    int rows;           // L * group query rows share one key/value head
+    int n_splits;
+    int keys_per_split; // multiple of 128
+    int neg;
+    float scale_log2;   // |scale| * log2(e)
+};
+
+hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
+                               hipStream_t stream);
+hipError_t launch_prefill_f16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
+                              hipStream_t stream);
+hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask, bool varlen,
+                              hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int elem, int D, hipStream_t stream);
+
+// Tile sizes the host needs for grids and workspace.
+constexpr int kPrefillBlockM = 128;  // query rows per MFMA workgroup
+constexpr int kF32BlockM = 64;       // query rows per fp32 workgroup
+constexpr int kDecodeMaxRows = 16;   // query rows (L * group) per decode workgroup
+constexpr int kDecodeKeyQuantum = 128;
+
+}  // namespace sdpa

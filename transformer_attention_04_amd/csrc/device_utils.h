@@ -1,0 +1,89 @@
+// Device-side helpers for the gfx950 (CDNA4) attention kernels: 16-bit element
+// traits, the MFMA wrappers, conversions that round to nearest-even, and
+// cross-lane moves.  Internal to libsdpa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Element traits for the two 16-bit input formats.  Data moves as raw 16-bit
+// words (uint16_t / uint4) and is reinterpreted only at the MFMA.
+struct BF16 {
+    typedef bf16x8_t vec8;
+    static __device__ __forceinline__ f32x16_t mfma32(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mfma16(vec8 a, vec8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // round-to-nearest-even float -> bf16 bits
+    static __device__ __forceinline__ uint16_t from_f32(float x) {
+        __bf16 h = (__bf16)x;
+        return __builtin_bit_cast(uint16_t, h);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t b) {
+        return __uint_as_float(((uint32_t)b) << 16);
+    }
+    // two floats -> packed pair (low half = a), nearest-even
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        bf16x2_t v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+struct F16 {
+    typedef f16x8_t vec8;
+    static __device__ __forceinline__ f32x16_t mfma32(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mfma16(vec8 a, vec8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint16_t from_f32(float x) {
+        _Float16 h = (_Float16)x;
+        return __builtin_bit_cast(uint16_t, h);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t b) {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        f16x2_t v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+template <typename Tr>
+__device__ __forceinline__ typename Tr::vec8 as_vec8(uint4 u) {
+    return __builtin_bit_cast(typename Tr::vec8, u);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32); log2(0) = -inf.
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of lane (lane ^ mask) for mask in {1..32} (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Flip the sign bit of eight 16-bit values (exact negation, NaN kept).
+__device__ __forceinline__ uint4 negate8(uint4 u) {
+    u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+    return u;
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
+
+}  // namespace sdpa

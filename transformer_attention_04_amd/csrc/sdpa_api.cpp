@@ -1,0 +1,390 @@
+// C interface of libsdpa (declared in include/sdpa.h): argument checks on the
+// host, kernel and launch-shape choice, and launch on the caller's stream.
+//
+// The argument set mirrors the exactref.ai "scaled_dot_product_attention"
+// Arguments table (query, key, value, attn_mask, dropout_p, is_causal, scale,
+// enable_gqa); packed variable-length input follows the block-diagonal masks
+// of the insureai360 xFormers tutorial, section 4.
+#include "../../include/sdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sdpa_status fail(sdpa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sdpa_status ok() {
+    g_err[0] = '\0';
+    return SDPA_OK;
+}
+
+int elem_bytes(sdpa_dtype t) {
+    switch (t) {
+        case SDPA_F32: return 4;
+        case SDPA_F16: return 2;
+        case SDPA_BF16: return 2;
+        case SDPA_BOOL: return 1;
+    }
+    return 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks that a tensor can be read with 16-byte vector loads along its rows:
+// unit last stride, 16-byte aligned base, and every outer stride (of a dim
+// with more than one element) a multiple of 16 bytes.
+sdpa_status check_vector_layout(const sdpa_tensor4& t, int ebytes, const char* name) {
+    const int64_t vec = 16 / ebytes;
+    if (t.size[3] > 1 && t.stride[3] != 1)
+        return fail(SDPA_ERR_UNSUPPORTED, "%s: the last dimension must have stride 1", name);
+    if (!aligned16(t.data))
+        return fail(SDPA_ERR_UNSUPPORTED, "%s: the base pointer must be 16-byte aligned", name);
+    for (int d = 0; d < 3; ++d)
+        if (t.size[d] > 1 && t.stride[d] % vec != 0)
+            return fail(SDPA_ERR_UNSUPPORTED, "%s: stride[%d]=%lld is not a multiple of %lld elements",
+                        name, d, (long long)t.stride[d], (long long)vec);
+    return SDPA_OK;
+}
+
+bool supported_head_dim(int64_t e) { return e == 64 || e == 96 || e == 128; }
+
+struct Plan {
+    bool decode = false;
+    int n_splits = 0;
+    int keys_per_split = 0;
+    size_t workspace = 0;
+};
+
+// Split-KV decode applies to few query rows per key/value head, no mask, no
+// causal flag, 16-bit inputs.  The automatic split count aims for about 2048
+// workgroups (several per compute unit) while keeping each split long enough
+// that the final merge stays small next to the key/value stream.
+sdpa_status make_plan(sdpa_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                      int64_t Ev, bool has_mask, bool causal, int num_splits, Plan* plan) {
+    const int64_t group = Hkv > 0 ? Hq / Hkv : 1;
+    const bool eligible = !has_mask && !causal && (dtype == SDPA_BF16 || dtype == SDPA_F16) &&
+                          L * group <= sdpa::kDecodeMaxRows && L > 0;
+    Plan pl;
+    if (num_splits == -1) {
+        pl.decode = false;
+    } else if (num_splits == 0) {
+        pl.decode = eligible && S > 0;
+    } else if (num_splits >= 1) {
+        if (!eligible)
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "the split-KV decode kernel needs no mask, no causal flag, bf16/fp16 and "
+                        "L*Hq/Hkv <= %d (got L=%lld, group=%lld)",
+                        sdpa::kDecodeMaxRows, (long long)L, (long long)group);
+        pl.decode = true;
+    } else {
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits must be -1, 0 or positive (got %d)", num_splits);
+    }
+    if (pl.decode) {
+        const int64_t q = sdpa::kDecodeKeyQuantum;
+        int64_t splits;
+        if (num_splits >= 1) {
+            splits = num_splits;
+        } else {
+            const int64_t units = B * Hkv > 0 ? B * Hkv : 1;
+            splits = (2048 + units - 1) / units;
+            const int64_t max_by_len = (S + 255) / 256;
+            if (splits > max_by_len) splits = max_by_len;
+            if (splits < 1) splits = 1;
+        }
+        int64_t per = (S + splits - 1) / splits;
+        per = ((per + q - 1) / q) * q;
+        if (per < q) per = q;
+        if (per > (int64_t)1 << 30) return fail(SDPA_ERR_UNSUPPORTED, "key length too large");
+        splits = S > 0 ? (S + per - 1) / per : 1;
+        pl.n_splits = (int)splits;
+        pl.keys_per_split = (int)per;
+        const int64_t nrow = B * Hq * L * splits;
+        pl.workspace = (size_t)(((nrow + 63) / 64) * 64 + nrow * Ev) * sizeof(float) + 256;
+    }
+    *plan = pl;
+    return SDPA_OK;
+}
+
+struct Shapes {
+    int64_t B, Hq, Hkv, L, S, E, Ev;
+};
+
+sdpa_status check_shapes(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
+                         const sdpa_tensor4* v, const sdpa_tensor4* attn_mask, int enable_gqa,
+                         Shapes* sh) {
+    if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16");
+    if (!q || !k || !v) return fail(SDPA_ERR_INVALID_ARGUMENT, "q, k and v descriptors must not be NULL");
+    for (int d = 0; d < 4; ++d)
+        if (q->size[d] < 0 || k->size[d] < 0 || v->size[d] < 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    Shapes s{q->size[0], q->size[1], k->size[1], q->size[2], k->size[2], q->size[3], v->size[3]};
+    if (k->size[0] != s.B || v->size[0] != s.B)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "q, k and v must have the same batch size");
+    if (k->size[3] != s.E)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "query and key must share the last dimension E (%lld vs %lld)",
+                    (long long)s.E, (long long)k->size[3]);
+    if (v->size[2] != s.S || v->size[1] != s.Hkv)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "key and value must share heads and sequence length");
+    if (s.Hq != s.Hkv) {
+        if (!enable_gqa)
+            return fail(SDPA_ERR_INVALID_ARGUMENT,
+                        "query has %lld heads and key/value %lld: pass enable_gqa", (long long)s.Hq,
+                        (long long)s.Hkv);
+        if (s.Hkv == 0 || s.Hq % s.Hkv != 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query heads (%lld) must be a multiple of key/value heads (%lld)",
+                        (long long)s.Hq, (long long)s.Hkv);
+    }
+    if (attn_mask) {
+        const int64_t want[4] = {s.B, s.Hq, s.L, s.S};
+        for (int d = 0; d < 4; ++d)
+            if (attn_mask->size[d] != want[d] && !(attn_mask->size[d] == 1 && d < 3))
+                return fail(SDPA_ERR_INVALID_ARGUMENT,
+                            "attn_mask size[%d]=%lld does not broadcast to %lld", d,
+                            (long long)attn_mask->size[d], (long long)want[d]);
+    }
+    if (s.L > INT32_MAX || s.S > INT32_MAX || s.Hq > INT32_MAX || s.B > INT32_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "a size exceeds the 32-bit index range of the kernels");
+    *sh = s;
+    return SDPA_OK;
+}
+
+sdpa_status resolve_scale(const double* scale, int64_t E, double* out) {
+    const double s = scale ? *scale : 1.0 / std::sqrt((double)E);
+    if (!std::isfinite(s)) return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    *out = s;
+    return SDPA_OK;
+}
+
+void fill_scale(sdpa::AttnParams& p, double s) {
+    p.neg = s < 0;
+    p.scale = (float)s;
+    p.scale_abs = (float)std::fabs(s);
+    p.scale_log2 = (float)(std::fabs(s) * 1.4426950408889634);
+}
+
+hipError_t launch_single_pass(sdpa_dtype dtype, const sdpa::AttnParams& p, int D, bool causal,
+                              int mask, bool varlen, hipStream_t s) {
+    switch (dtype) {
+        case SDPA_BF16: return sdpa::launch_prefill_bf16(p, D, causal, mask, varlen, s);
+        case SDPA_F16: return sdpa::launch_prefill_f16(p, D, causal, mask, varlen, s);
+        case SDPA_F32: return sdpa::launch_prefill_f32(p, D, causal, mask, varlen, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_abi_version(void) { return 1; }
+
+const char* sdpa_last_error(void) { return g_err; }
+
+sdpa_status sdpa_fwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
+                                    const sdpa_tensor4* v, const sdpa_tensor4* attn_mask,
+                                    int is_causal, int enable_gqa, int num_splits, size_t* bytes) {
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+    Shapes s;
+    sdpa_status st = check_shapes(dtype, q, k, v, attn_mask, enable_gqa, &s);
+    if (st != SDPA_OK) return st;
+    Plan pl;
+    st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.Ev, attn_mask != nullptr, is_causal != 0,
+                   num_splits, &pl);
+    if (st != SDPA_OK) return st;
+    *bytes = pl.workspace;
+    return ok();
+}
+
+sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
+                     const sdpa_tensor4* v, const sdpa_tensor4* attn_mask, sdpa_dtype mask_dtype,
+                     double dropout_p, int is_causal, const double* scale, int enable_gqa,
+                     const sdpa_tensor4* out, const sdpa_tensor4* lse, void* workspace,
+                     size_t workspace_bytes, int num_splits, void* stream) {
+    if (dropout_p != 0.0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "dropout_p must be 0: a random dropout has no exact reference");
+    Shapes s;
+    sdpa_status st = check_shapes(dtype, q, k, v, attn_mask, enable_gqa, &s);
+    if (st != SDPA_OK) return st;
+    if (!out || !lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "out and lse descriptors must not be NULL");
+    const int64_t want_o[4] = {s.B, s.Hq, s.L, s.Ev};
+    for (int d = 0; d < 4; ++d) {
+        if (out->size[d] != want_o[d])
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "out must be (B, Hq, L, Ev)");
+        if (d < 3 && lse->size[d] != want_o[d])
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    }
+    if (lse->size[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
+    if (s.B * s.Hq * s.L == 0) return ok();  // nothing to compute
+    if (s.E != s.Ev)
+        return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %lld and %lld)", (long long)s.E,
+                    (long long)s.Ev);
+    if (!supported_head_dim(s.E))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not one of 64, 96, 128", (long long)s.E);
+    const int eb = elem_bytes(dtype);
+    if ((st = check_vector_layout(*q, eb, "q")) != SDPA_OK) return st;
+    if (s.S > 0) {
+        if ((st = check_vector_layout(*k, eb, "k")) != SDPA_OK) return st;
+        if ((st = check_vector_layout(*v, eb, "v")) != SDPA_OK) return st;
+    }
+    if ((st = check_vector_layout(*out, eb, "out")) != SDPA_OK) return st;
+    if (!lse->data) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse data must not be NULL");
+    if (attn_mask) {
+        if (!attn_mask->data && s.S > 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask data is NULL");
+        if (s.S > 1 && attn_mask->stride[3] != 1)
+            return fail(SDPA_ERR_UNSUPPORTED, "attn_mask: the key dimension must have stride 1");
+    }
+    double sc;
+    if ((st = resolve_scale(scale, s.E, &sc)) != SDPA_OK) return st;
+    Plan pl;
+    if ((st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.Ev, attn_mask != nullptr, is_causal != 0,
+                        num_splits, &pl)) != SDPA_OK)
+        return st;
+    if (pl.workspace > workspace_bytes || (pl.workspace > 0 && !workspace))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes needed, %zu given",
+                    pl.workspace, workspace_bytes);
+    hipStream_t hs = (hipStream_t)stream;
+    const int64_t lse_sb = lse->size[0] > 1 ? lse->stride[0] : 0;
+    const int64_t lse_sh = lse->size[1] > 1 ? lse->stride[1] : 0;
+    const int64_t lse_sr = lse->size[2] > 1 ? lse->stride[2] : 1;
+    if (lse_sr != 1) return fail(SDPA_ERR_UNSUPPORTED, "lse: the query dimension must have stride 1");
+
+    if (pl.decode) {
+        sdpa::DecodeParams p{};
+        p.q = q->data; p.k = k->data; p.v = v->data; p.o = out->data; p.lse = (float*)lse->data;
+        float* ws = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+        p.part_lse = ws;
+        const int64_t nrow = s.B * s.Hq * s.L * pl.n_splits;
+        p.part_o = ws + ((nrow + 63) / 64) * 64;
+        p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sr = q->stride[2];
+        p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sr = k->stride[2];
+        p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_sr = v->stride[2];
+        p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_sr = out->stride[2];
+        p.lse_sb = lse_sb; p.lse_sh = lse_sh;
+        p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
+        p.L = (int)s.L; p.S = (int)s.S;
+        p.rows = (int)(s.L * p.group);
+        p.n_splits = pl.n_splits;
+        p.keys_per_split = pl.keys_per_split;
+        p.neg = sc < 0;
+        p.scale_log2 = (float)(std::fabs(sc) * 1.4426950408889634);
+        hipError_t e = sdpa::launch_decode(p, dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16,
+                                           (int)s.E, hs);
+        if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+
+    sdpa::AttnParams p{};
+    p.q = q->data; p.k = k->data; p.v = v->data; p.o = out->data; p.lse = (float*)lse->data;
+    p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sr = q->stride[2];
+    p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sr = k->stride[2];
+    p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_sr = v->stride[2];
+    p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_sr = out->stride[2];
+    p.lse_sb = lse_sb; p.lse_sh = lse_sh;
+    int mask_kind = sdpa::MASK_NONE;
+    if (attn_mask) {
+        mask_kind = mask_dtype == SDPA_F32 ? sdpa::MASK_FLOAT : sdpa::MASK_BOOL;
+        p.mask = attn_mask->data;
+        p.m_sb = attn_mask->size[0] > 1 ? attn_mask->stride[0] : 0;
+        p.m_sh = attn_mask->size[1] > 1 ? attn_mask->stride[1] : 0;
+        p.m_sr = attn_mask->size[2] > 1 ? attn_mask->stride[2] : 0;
+        const int64_t mvec = mask_dtype == SDPA_F32 ? 4 : 8;  // elements per vector load
+        const int64_t mal = mask_dtype == SDPA_F32 ? 16 : 8;  // its alignment in bytes
+        p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 &&
+                     p.m_sh % mvec == 0 && p.m_sr % mvec == 0;
+    }
+    p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
+    p.L = (int)s.L; p.S = (int)s.S;
+    const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
+    p.n_qtiles = (int)((s.L + bm - 1) / bm);
+    fill_scale(p, sc);
+    hipError_t e = launch_single_pass(dtype, p, (int)s.E, is_causal != 0, mask_kind, false, hs);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_tok,
+                            int64_t q_stride_head, const void* k, int64_t k_stride_tok,
+                            int64_t k_stride_head, const void* v, int64_t v_stride_tok,
+                            int64_t v_stride_head, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t n_seqs, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t E, int32_t Ev,
+                            int64_t total_q, int64_t total_k, double dropout_p, int is_causal,
+                            const double* scale, int enable_gqa, void* out, int64_t o_stride_tok,
+                            int64_t o_stride_head, float* lse, int64_t lse_stride_head,
+                            void* stream) {
+    if (dropout_p != 0.0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "dropout_p must be 0: a random dropout has no exact reference");
+    if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16");
+    if (n_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq < 0 || Hkv < 0 || E < 0 || Ev < 0 ||
+        total_q < 0 || total_k < 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    if (Hq != Hkv) {
+        if (!enable_gqa)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query has %d heads and key/value %d: pass enable_gqa",
+                        Hq, Hkv);
+        if (Hkv == 0 || Hq % Hkv != 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query heads (%d) must be a multiple of key/value heads (%d)",
+                        Hq, Hkv);
+    }
+    if (n_seqs == 0 || max_seqlen_q == 0 || Hq == 0 || total_q == 0) return ok();
+    if (!cu_seqlens_q || !cu_seqlens_k)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must not be NULL");
+    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %d and %d)", E, Ev);
+    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d is not one of 64, 96, 128", E);
+    if (!q || !out || !lse || (total_k > 0 && (!k || !v)))
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
+    const int64_t vec = 16 / elem_bytes(dtype);
+    const void* ptrs[4] = {q, k, v, out};
+    const int64_t strides[8] = {q_stride_tok, q_stride_head, k_stride_tok, k_stride_head,
+                                v_stride_tok, v_stride_head, o_stride_tok, o_stride_head};
+    for (int i = 0; i < 4; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
+    for (int i = 0; i < 8; ++i)
+        if (strides[i] % vec != 0)
+            return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
+    double sc;
+    sdpa_status st;
+    if ((st = resolve_scale(scale, E, &sc)) != SDPA_OK) return st;
+    sdpa::AttnParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+    p.q_sr = q_stride_tok; p.q_sh = q_stride_head;
+    p.k_sr = k_stride_tok; p.k_sh = k_stride_head;
+    p.v_sr = v_stride_tok; p.v_sh = v_stride_head;
+    p.o_sr = o_stride_tok; p.o_sh = o_stride_head;
+    p.lse_sh = lse_stride_head;
+    p.total_q = total_q; p.total_k = total_k;
+    p.B = n_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+    p.L = max_seqlen_q; p.S = max_seqlen_k;
+    const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
+    p.n_qtiles = (max_seqlen_q + bm - 1) / bm;
+    fill_scale(p, sc);
+    hipError_t e = launch_single_pass(dtype, p, E, is_causal != 0, sdpa::MASK_NONE, true,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

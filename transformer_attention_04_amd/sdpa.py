@@ -1,0 +1,259 @@
+"""Python binding of libsdpa (ctypes): argument marshalling only.
+
+The functions here have the names of the C entry points in include/sdpa.h.
+They turn torch tensors into device pointers, sizes and strides, allocate the
+outputs (and the split-KV workspace) with torch, and enqueue the HIP kernels
+on torch's current stream.  Every step of the attention itself runs in the
+HIP kernels; there is no CPU or PyTorch fallback: without the built library,
+or with tensors that are not on a ROCm device, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+SDPA_OK, SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED, SDPA_ERR_DEVICE = 0, 1, 2, 3
+SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
+_DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
+
+EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_last_error",
+            "sdpa_abi_version")
+
+
+class SdpaTensor4(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p),
+                ("size", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class SdpaError(RuntimeError):
+    """A non-zero status from libsdpa, with its message."""
+
+    def __init__(self, status, message):
+        super().__init__(f"libsdpa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsdpa.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m transformer_attention_04_amd.build_lib`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(SdpaTensor4)
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.sdpa_fwd.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, dbl, ctypes.c_int,
+                             ctypes.POINTER(dbl), ctypes.c_int, P, P, vp, ctypes.c_size_t,
+                             ctypes.c_int, vp]
+    lib.sdpa_fwd.restype = ctypes.c_int
+    lib.sdpa_fwd_workspace_size.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sdpa_fwd_workspace_size.restype = ctypes.c_int
+    lib.sdpa_fwd_varlen.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                    vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, i64,
+                                    dbl, ctypes.c_int, ctypes.POINTER(dbl), ctypes.c_int,
+                                    vp, i64, i64, vp, i64, vp]
+    lib.sdpa_fwd_varlen.restype = ctypes.c_int
+    lib.sdpa_last_error.argtypes = []
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_abi_version.argtypes = []
+    lib.sdpa_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def sdpa_last_error():
+    return load_library().sdpa_last_error().decode()
+
+
+def sdpa_abi_version():
+    return load_library().sdpa_abi_version()
+
+
+def _check(status):
+    if status != SDPA_OK:
+        raise SdpaError(status, sdpa_last_error())
+
+
+def _desc(t):
+    d = SdpaTensor4()
+    d.data = t.data_ptr() if t is not None and t.numel() > 0 else None
+    for i in range(4):
+        d.size[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _as4d(x):
+    """(..., H, L, E) -> (B, H, L, E) with B the product of the leading dims (a view when possible)."""
+    if x.dim() < 2:
+        raise ValueError("attention inputs need at least 2 dimensions (..., L, E)")
+    if x.dim() == 2:
+        return x.unsqueeze(0).unsqueeze(0)
+    if x.dim() == 3:
+        return x.unsqueeze(0)
+    if x.dim() == 4:
+        return x
+    return x.reshape(-1, *x.shape[-3:])
+
+
+def _scale_arg(scale):
+    return None if scale is None else ctypes.byref(ctypes.c_double(float(scale)))
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libsdpa runs on the GPU: every tensor must be on a ROCm device")
+
+
+def _mask_4d(attn_mask, q4, S):
+    if attn_mask is None:
+        return None, SDPA_F32
+    if attn_mask.dtype == torch.bool:
+        m, mdt = attn_mask, SDPA_BOOL
+    else:
+        m, mdt = (attn_mask if attn_mask.dtype == torch.float32 else attn_mask.float()), SDPA_F32
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if m.dim() > 4:
+        m = m.reshape(-1, *m.shape[-3:])
+    B, H, L = q4.shape[:3]
+    m = torch.broadcast_to(m, (B if m.shape[0] != 1 else 1, H if m.shape[1] != 1 else 1,
+                               L if m.shape[2] != 1 else 1, S))
+    if S > 1 and m.stride(3) != 1:
+        m = m.contiguous()
+    return m, mdt
+
+
+def sdpa_fwd_workspace_size(query, key, value, attn_mask=None, is_causal=False, enable_gqa=False,
+                            num_splits=0):
+    """Workspace bytes sdpa_fwd needs for these arguments (host only)."""
+    lib = load_library()
+    q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+    k4, v4 = _expand_batch(q4, k4), _expand_batch(q4, v4)
+    m4, _ = _mask_4d(attn_mask, q4, k4.shape[2])
+    n = ctypes.c_size_t(0)
+    dq, dk, dv = _desc(q4), _desc(k4), _desc(v4)
+    dm = _desc(m4) if m4 is not None else None
+    _check(lib.sdpa_fwd_workspace_size(_DTYPE[query.dtype], dq, dk, dv,
+                                       ctypes.byref(dm) if dm is not None else None,
+                                       int(bool(is_causal)), int(bool(enable_gqa)), int(num_splits),
+                                       ctypes.byref(n)))
+    return n.value
+
+
+def _expand_batch(q4, t4):
+    if t4.shape[0] == 1 and q4.shape[0] != 1:
+        return t4.expand(q4.shape[0], *t4.shape[1:])
+    return t4
+
+
+def sdpa_fwd(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+             enable_gqa=False, num_splits=0, out=None, lse=None, workspace=None):
+    """Exact attention forward on the GPU.  Returns (out (..., Hq, L, Ev), lse (..., Hq, L) float32).
+
+    Arguments follow the exactref.ai "scaled_dot_product_attention" Arguments
+    table; ``num_splits`` selects the kernel (0 automatic, -1 single pass,
+    k >= 1 split-KV decode with k splits).
+    """
+    lib = load_library()
+    _require_gpu(query, key, value, attn_mask, out, lse)
+    if query.dtype not in _DTYPE or key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("query, key and value must share one of float32, float16, bfloat16")
+    q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+    k4, v4 = _expand_batch(q4, k4), _expand_batch(q4, v4)
+    B, Hq, L, _ = q4.shape
+    S, Ev = v4.shape[2], v4.shape[3]
+    m4, mdt = _mask_4d(attn_mask, q4, S)
+    dev = query.device
+    if out is None:
+        out = torch.empty((B, Hq, L, Ev), dtype=query.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, L, 1), dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (B, Hq, L, Ev) or tuple(lse.shape) != (B, Hq, L, 1):
+        raise ValueError("out must be (B, Hq, L, Ev) and lse (B, Hq, L, 1)")
+    o4, l4 = out, lse
+    dq, dk, dv, do, dl = _desc(q4), _desc(k4), _desc(v4), _desc(o4), _desc(l4)
+    dm = _desc(m4) if m4 is not None else None
+    pm = ctypes.byref(dm) if dm is not None else None
+    with torch.cuda.device(dev):
+        nbytes = ctypes.c_size_t(0)
+        _check(lib.sdpa_fwd_workspace_size(_DTYPE[query.dtype], dq, dk, dv, pm, int(bool(is_causal)),
+                                           int(bool(enable_gqa)), int(num_splits), ctypes.byref(nbytes)))
+        if nbytes.value and (workspace is None or workspace.numel() < nbytes.value):
+            workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if nbytes.value else None
+        _check(lib.sdpa_fwd(_DTYPE[query.dtype], dq, dk, dv, pm, mdt, float(dropout_p),
+                            int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), do, dl,
+                            ws_ptr, nbytes.value, int(num_splits), _stream(dev)))
+    return o4.reshape(*query.shape[:-1], Ev), l4.reshape(*query.shape[:-1])
+
+
+def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                    dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False):
+    """Packed variable-length attention with a block-diagonal (optionally causal) mask.
+
+    q (total_q, Hq, E) or (1, total_q, Hq, E) -- the BMHK layout of the
+    insureai360 xFormers tutorial, section 4; k, v likewise; cu_seqlens are
+    int32 device tensors of n_seqs + 1 offsets.  Returns out shaped like q
+    (with Ev) and lse (Hq, total_q) (or (1, Hq, total_q) for 4-D input).
+    """
+    lib = load_library()
+    _require_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one of float32, float16, bfloat16")
+    batched = q.dim() == 4
+    q3, k3, v3 = (t[0] if t.dim() == 4 else t for t in (q, k, v))
+    if cu_seqlens_k is None:
+        cu_seqlens_k = cu_seqlens_q
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 device tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    n_seqs = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None or max_seqlen_k is None:
+        cq = cu_seqlens_q.cpu().long()
+        ck = cu_seqlens_k.cpu().long()
+        max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if n_seqs > 0 else 0
+        max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if n_seqs > 0 else 0
+    total_q, Hq, E = q3.shape
+    total_k, Hkv, _ = k3.shape
+    Ev = v3.shape[2]
+    for t in (q3, k3, v3):
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("the last dimension must have stride 1")
+    dev = q.device
+    out3 = torch.empty((total_q, Hq, Ev), dtype=q.dtype, device=dev)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.sdpa_fwd_varlen(
+            _DTYPE[q.dtype], q3.data_ptr(), q3.stride(0), q3.stride(1),
+            k3.data_ptr(), k3.stride(0), k3.stride(1), v3.data_ptr(), v3.stride(0), v3.stride(1),
+            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_q),
+            int(max_seqlen_k), Hq, Hkv, E, Ev, total_q, total_k, float(dropout_p),
+            int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)),
+            out3.data_ptr(), out3.stride(0), out3.stride(1), lse.data_ptr(), lse.stride(0),
+            _stream(dev)))
+    if batched:
+        return out3.unsqueeze(0), lse.unsqueeze(0)
+    return out3, lse
