@@ -9,7 +9,9 @@
 //
 // gfx950 design
 //  * A workgroup is 4 wavefronts of 64 lanes and owns 128 query rows; each
-//    wavefront owns 32 rows.  Keys advance 64 per step through a
+//    wavefront owns 32 rows.  Two workgroups share a compute unit (at most 256
+//    registers per lane), so one workgroup's loads and softmax overlap the
+//    other's matrix products.  Keys advance 64 per step through a
 //    double-buffered LDS stage: K as rows, V transposed (V^T) so that both
 //    matrix products read 16-byte runs along their contraction axis.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
@@ -24,15 +26,21 @@
 //    score registers (rounded to bf16/fp16, as fused kernels do) with no LDS
 //    round trip.  O^T also has one query per lane, so the rescale by
 //    exp(m_old - m_new) is an in-lane multiply.
+//  * The running max is raised only when a block's max exceeds it by more than
+//    2^8 in the exponent; otherwise the old shift stays (weights stay <= 256)
+//    and the O rescale is skipped.  Output and lse use the same shift as the
+//    row sum, so the result is the same softmax.
 //  * V^T rows are XOR-swizzled in 16-byte chunks by (row / 8) % 8 so that the
 //    transposing writes and the 16-byte MFMA operand reads avoid LDS bank
 //    conflicts.
+//  * Global memory is read and written through buffer resources sized to the
+//    valid rows: rows past the end read as 0 and their stores are dropped, so
+//    edge tiles need no branches.
 //  * Causal: key blocks wholly above the diagonal are never loaded; wavefronts
 //    whose rows all precede a block skip its products; masking by index runs
 //    only on edge blocks.  Workgroups are dispatched heaviest query block first.
-//  * Special rows: a row with no kept key keeps running max -inf, uses a zero
-//    shift, and ends with output 0 and lse -inf; a NaN score makes exp NaN and
-//    the row NaN.
+//  * Special rows: a row with no kept key keeps an unset shift, and ends with
+//    output 0 and lse -inf; a NaN score makes exp NaN and the row NaN.
 #pragma once
 
 #include "attn_common.h"
@@ -45,8 +53,13 @@ __device__ __forceinline__ int swap_bits23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Exponent margin (log2 units) by which a block max may exceed the current
+// shift before the shift is raised.
+constexpr float kLazyRescale = 8.0f;
+
 template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(AttnParams p) {
     constexpr int BM = kPrefillBlockM;
     constexpr int BN = 64;
     constexpr int KS = D + 8;      // LDS row stride of the K tile, in 16-bit words
@@ -57,9 +70,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
     constexpr int NKK = D / 16;    // k-steps of the score product
     constexpr int NDB = D / 32;    // 32-row blocks of O^T
     constexpr int KCH = BN * D / 8;          // 16-byte chunks of a K tile
-    constexpr int KCH_T = (KCH + 255) / 256; // per thread
+    constexpr int KCH_T = KCH / 256;         // per thread
     constexpr int VIT = (D / 8) * (BN / 4);  // V items: 8 columns x 4 keys
-    static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+    static_assert(D % 32 == 0 && KCH % 256 == 0, "head dim must be a multiple of 32");
     static_assert(VIT <= 256, "one V item per thread");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -105,42 +118,43 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
     if (q0 >= Lb) return;
     const int kend = CAUSAL ? min(Sb, min(q0 + BM, Lb)) : Sb;
     const int ntiles = (kend + BN - 1) / BN;
-    const int wrow0 = q0 + wave * 32;      // first row of this wavefront
-    const int my_row = wrow0 + lq;         // the query this lane owns
-    const bool wave_has_rows = wrow0 < Lb;
+    const int qrows = min(BM, Lb - q0);   // valid rows of this block
+    const int wrow0 = wave * 32;          // first local row of this wavefront
+    const int lrow = wrow0 + lq;          // local row this lane owns
+    const int my_row = q0 + lrow;         // its query index
+    const bool wave_has_rows = wrow0 < qrows;
 
     // Q^T operand, resident for the whole loop (negated when the scale is negative).
-    const uint16_t* qp = (const uint16_t*)p.q + qo;
+    const int q_rs = (int)(p.q_sr * 2);
+    const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
     uint4 qreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-        uint4 u = zero4();
-        if (my_row < Lb) u = *(const uint4*)(qp + (int64_t)my_row * p.q_sr + kk * 16 + hh * 8);
+        const uint4 u = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
         qreg[kk] = p.neg ? negate8(u) : u;
     }
 
-    const uint16_t* kp = (const uint16_t*)p.k + ko;
-    const uint16_t* vp = (const uint16_t*)p.v + vo;
+    const uint16_t* kbase = (const uint16_t*)p.k + ko;
+    const uint16_t* vbase = (const uint16_t*)p.v + vo;
+    const int k_rs = (int)(p.k_sr * 2);
+    const int v_rs = (int)(p.v_sr * 2);
     uint4 kbuf[KCH_T];
     uint4 vbuf[4];
 
     auto load_tile = [&](int key0) {
+        const int rows = min(BN, Sb - key0);
+        const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
+        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + D * 2);
 #pragma unroll
         for (int i = 0; i < KCH_T; ++i) {
             const int c = tid + 256 * i;
-            kbuf[i] = zero4();
-            if (c < KCH) {
-                const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-                if (key0 + r < Sb) kbuf[i] = *(const uint4*)(kp + (int64_t)(key0 + r) * p.k_sr + col);
-            }
+            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+            kbuf[i] = buf_load16(kr, r * k_rs + col * 2);
         }
-        if (tid < VIT) {
+        if (VIT == 256 || tid < VIT) {
             const int dc = tid % (D / 8), kg = tid / (D / 8);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + kg * 4 + r;
-                vbuf[r] = (key < Sb) ? *(const uint4*)(vp + (int64_t)key * p.v_sr + dc * 8) : zero4();
-            }
+            for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, (kg * 4 + r) * v_rs + dc * 16);
         }
     };
 
@@ -150,13 +164,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < KCH_T; ++i) {
             const int c = tid + 256 * i;
-            if (c < KCH) {
-                const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-                const int row = (r & ~31) | swap_bits23(r & 31);
-                *(uint4*)(Ks + row * KS + col) = kbuf[i];
-            }
+            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+            const int row = (r & ~31) | swap_bits23(r & 31);
+            *(uint4*)(Ks + row * KS + col) = kbuf[i];
         }
-        if (tid < VIT) {
+        if (VIT == 256 || tid < VIT) {
             const int dc = tid % (D / 8), kg = tid / (D / 8);
             const uint32_t* w0 = (const uint32_t*)&vbuf[0];
             const uint32_t* w1 = (const uint32_t*)&vbuf[1];
@@ -166,12 +178,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
             uint16_t* base = Vt + chunk * 8 + (kg & 1) * 4;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int sh = (j & 1) * 16;
-                const uint32_t e0 = (w0[j >> 1] >> sh) & 0xffffu;
-                const uint32_t e1 = (w1[j >> 1] >> sh) & 0xffffu;
-                const uint32_t e2 = (w2[j >> 1] >> sh) & 0xffffu;
-                const uint32_t e3 = (w3[j >> 1] >> sh) & 0xffffu;
-                *(uint2*)(base + (dc * 8 + j) * VS) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+                // keys kg*4 .. kg*4+3 of column dc*8 + j, as two packed pairs
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t lo = __builtin_amdgcn_perm(w1[j >> 1], w0[j >> 1], sel);
+                const uint32_t hi = __builtin_amdgcn_perm(w3[j >> 1], w2[j >> 1], sel);
+                *(uint2*)(base + (dc * 8 + j) * VS) = make_uint2(lo, hi);
             }
         }
     };
@@ -179,15 +190,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
     f32x16_t acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
-    float m_run = kNegInf;  // running max: raw scores, or logits when a float mask is added
-    float l_run = 0.f;      // this lane's share of the row sum
-
-    const float* mrow_f = nullptr;
-    const uint8_t* mrow_b = nullptr;
-    if (MASK == MASK_FLOAT)
-        mrow_f = (const float*)p.mask + mo + (int64_t)min(my_row, Lb - 1) * p.m_sr;
-    if (MASK == MASK_BOOL)
-        mrow_b = (const uint8_t*)p.mask + mo + (int64_t)min(my_row, Lb - 1) * p.m_sr;
+    // Running shift in log2 units (-inf until the row sees a kept key) and this
+    // lane's share of the row sum relative to it.
+    float sh_run = kNegInf;
+    float l_run = 0.f;
+    // log2-domain logit = t * cfac, with t the raw score (or the fp32 logit when a
+    // float mask is added).
+    const float cfac = (MASK == MASK_FLOAT) ? kLog2e : p.scale_log2;
 
     if (ntiles > 0) {
         load_tile(0);
@@ -200,71 +209,88 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
         if (t + 1 < ntiles) load_tile(key0 + BN);
         const uint16_t* Ks = smem + (t & 1) * STAGE;
         const uint16_t* Vt = Ks + KTILE;
-        const bool active = wave_has_rows && (!CAUSAL || key0 <= wrow0 + 31);
+        const bool active = wave_has_rows && (!CAUSAL || key0 <= q0 + wrow0 + 31);
         if (active) {
-            f32x16_t s[2];
+            f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16_t{};
+            for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
+                for (int kb = 0; kb < 2; ++kb) {
                     const uint4 a = *(const uint4*)(Ks + (kb * 32 + lq) * KS + kk * 16 + hh * 8);
                     s[kb] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(qreg[kk]), s[kb]);
                 }
             }
             // s[kb][8c + j] is the score of key key0 + 32kb + 16c + 8hh + j for query my_row.
-            const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > wrow0);
             if (MASK == MASK_FLOAT) {
+                // bias rows of this wavefront from key0 on; past the valid rows/keys reads 0
+                const int mrow_bytes = (int)(p.m_sr * 4);
+                const auto mr = make_rsrc((const float*)p.mask + mo + (int64_t)(q0 + wrow0) * p.m_sr + key0,
+                                          ((qrows - 1 - wrow0) * (int)p.m_sr + (Sb - key0)) * 4);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
-                        const int base = key0 + kb * 32 + c * 16 + hh * 8;
+                        const int off = lq * mrow_bytes + (kb * 32 + c * 16 + hh * 8) * 4;
                         float bias[8];
-                        if (p.mask_vec && base + 8 <= Sb) {
-                            const float4 b0 = *(const float4*)(mrow_f + base);
-                            const float4 b1 = *(const float4*)(mrow_f + base + 4);
-                            bias[0] = b0.x; bias[1] = b0.y; bias[2] = b0.z; bias[3] = b0.w;
-                            bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
+                        if (p.mask_vec) {
+                            const uint4 b0 = buf_load16(mr, off);
+                            const uint4 b1 = buf_load16(mr, off + 16);
+                            bias[0] = __uint_as_float(b0.x); bias[1] = __uint_as_float(b0.y);
+                            bias[2] = __uint_as_float(b0.z); bias[3] = __uint_as_float(b0.w);
+                            bias[4] = __uint_as_float(b1.x); bias[5] = __uint_as_float(b1.y);
+                            bias[6] = __uint_as_float(b1.z); bias[7] = __uint_as_float(b1.w);
                         } else {
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) bias[j] = (base + j < Sb) ? mrow_f[base + j] : kNegInf;
+                            for (int j = 0; j < 8; ++j) bias[j] = __uint_as_float(buf_load4(mr, off + 4 * j));
                         }
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
                             s[kb][c * 8 + j] = fmaf(s[kb][c * 8 + j], p.scale_abs, bias[j]);
                     }
             }
-            bool keep[2][16];
+            const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
             const bool any_mask = edge || MASK == MASK_BOOL;
+            uint32_t keepbits = 0xffffffffu;  // bit kb*16 + r: key kept
             if (any_mask) {
+                uint32_t mbits = 0xffffffffu;
+                if (MASK == MASK_BOOL) {
+                    const int mrow_bytes = (int)p.m_sr;
+                    const auto mr = make_rsrc((const uint8_t*)p.mask + mo + (int64_t)(q0 + wrow0) * p.m_sr + key0,
+                                              (qrows - 1 - wrow0) * (int)p.m_sr + (Sb - key0));
+                    mbits = 0;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            const int off = lq * mrow_bytes + kb * 32 + c * 16 + hh * 8;
+                            uint2 u;
+                            if (p.mask_vec) {
+                                u = buf_load8(mr, off);
+                            } else {
+                                u.x = u.y = 0;
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    u.x |= buf_load1(mr, off + j) << (8 * j);
+                                    u.y |= buf_load1(mr, off + 4 + j) << (8 * j);
+                                }
+                            }
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const uint32_t byte = ((j < 4 ? u.x : u.y) >> (8 * (j & 3))) & 0xffu;
+                                mbits |= (byte != 0 ? 1u : 0u) << (kb * 16 + c * 8 + j);
+                            }
+                        }
+                }
+                keepbits = 0;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int base = key0 + kb * 32 + c * 16 + hh * 8;
-                        uint8_t mb[8] = {1, 1, 1, 1, 1, 1, 1, 1};
-                        if (MASK == MASK_BOOL) {
-                            if (p.mask_vec && base + 8 <= Sb) {
-                                const uint2 u = *(const uint2*)(mrow_b + base);
-#pragma unroll
-                                for (int j = 0; j < 4; ++j) {
-                                    mb[j] = (u.x >> (8 * j)) & 0xff;
-                                    mb[4 + j] = (u.y >> (8 * j)) & 0xff;
-                                }
-                            } else {
-#pragma unroll
-                                for (int j = 0; j < 8; ++j) mb[j] = (base + j < Sb) ? mrow_b[base + j] : 0;
-                            }
-                        }
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int key = base + j;
-                            bool k_ok = key < Sb && mb[j] != 0;
-                            if (CAUSAL) k_ok = k_ok && key <= my_row;
-                            keep[kb][c * 8 + j] = k_ok;
-                            if (!k_ok) s[kb][c * 8 + j] = kNegInf;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = key0 + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
+                        bool ok = key < Sb && ((mbits >> (kb * 16 + r)) & 1u);
+                        if (CAUSAL) ok = ok && key <= my_row;
+                        keepbits |= (ok ? 1u : 0u) << (kb * 16 + r);
+                        s[kb][r] = ok ? s[kb][r] : kNegInf;
                     }
             }
             float mx = kNegInf;
@@ -273,49 +299,27 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = fmaxf(mx, xor_lane(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            float alpha, tsum = 0.f;
-            if (MASK == MASK_FLOAT) {
-                const float shift = (m_new == kNegInf) ? 0.f : m_new;
-                alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * kLog2e);
+            const float mxs = mx * cfac;                    // block max, log2 units
+            const bool raise = mxs > sh_run + kLazyRescale;  // never for an all-masked block
+            const float sh_new = raise ? mxs : sh_run;
+            const float alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
+            sh_run = sh_new;
+            const float shift = (sh_new == kNegInf) ? 0.f : sh_new;
+            float tsum = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float e = fast_exp2((s[kb][r] - shift) * kLog2e);
-                        s[kb][r] = e;
-                        tsum += e;
-                    }
-            } else {
-                // The shift is the running max times |scale| log2(e), rounded once; alpha
-                // compares two such rounded shifts, so an unchanged max gives exactly 1.
-                const float c2 = p.scale_log2;
-                const float shift = (m_new == kNegInf) ? 0.f : m_new * c2;
-                alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run * c2 - shift);
-                if (any_mask) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float e = keep[kb][r] ? fast_exp2(fmaf(s[kb][r], c2, -shift)) : 0.f;
-                            s[kb][r] = e;
-                            tsum += e;
-                        }
-                } else {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float e = fast_exp2(fmaf(s[kb][r], c2, -shift));
-                            s[kb][r] = e;
-                            tsum += e;
-                        }
+                for (int r = 0; r < 16; ++r) {
+                    float e = fast_exp2(fmaf(s[kb][r], cfac, -shift));
+                    if (any_mask) e = ((keepbits >> (kb * 16 + r)) & 1u) ? e : 0.f;
+                    s[kb][r] = e;
+                    tsum += e;
                 }
-            }
-            m_run = m_new;
             l_run = fmaf(l_run, alpha, tsum);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            }
 
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -341,29 +345,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnParams p) {
 
     // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
     const float l_tot = l_run + xor_lane(l_run, 32);
-    if (my_row < Lb) {
-        const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
-        uint16_t* op = (uint16_t*)p.o + oo + (int64_t)my_row * p.o_sr;
+    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
+    const int o_rs = (int)(p.o_sr * 2);
+    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + D * 2);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + g * 8 + hh * 4;
-                uint2 st;
-                st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
-                st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-                *(uint2*)(op + d) = st;
-            }
-        if (hh == 0) {
-            float lse;
-            if (l_tot == 0.f)
-                lse = kNegInf;
-            else if (MASK == MASK_FLOAT)
-                lse = fmaf(fast_log2(l_tot), kLn2, m_run);
-            else
-                lse = (m_run * p.scale_log2 + fast_log2(l_tot)) * kLn2;
-            p.lse[lo + my_row] = lse;
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + hh * 4;
+            uint2 st;
+            st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
+            st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+            buf_store8(st, ors, lrow * o_rs + d * 2);
         }
+    if (hh == 0) {
+        const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
+        const auto lrs = make_rsrc(p.lse + lo + q0, qrows * 4);
+        buf_store4(lse, lrs, lrow * 4);
     }
 }
 

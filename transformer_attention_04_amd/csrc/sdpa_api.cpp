@@ -5,7 +5,7 @@
 // Arguments table (query, key, value, attn_mask, dropout_p, is_causal, scale,
 // enable_gqa); packed variable-length input follows the block-diagonal masks
 // of the insureai360 xFormers tutorial, section 4.
-#include "../../include/sdpa.h"
+#include "sdpa.h"
 
 #include <hip/hip_runtime.h>
 
