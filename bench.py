@@ -175,7 +175,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | decode | neox | varlen | fp32 (comma separated)")
+                    help="all | main | decode | neox | varlen | fp32 | copy (comma separated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -231,6 +231,15 @@ def main(argv=None):
         secondary["fp32_single_head"] = {"metric": "us per call", "value": round(r["kernel_ms"] * 1e3, 2),
                                          "tflops": round(r["kernel_tflops"], 3)}
 
+    if "copy" in sel:
+        # calibration for the HBM byte counters: a plain device copy of a known size
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        secondary["copy_calibration"] = {"bytes_read_per_copy": src.numel(), "bytes_written_per_copy": dst.numel(),
+                                         "copies": 4}
     if main_res is None:
         print(json.dumps({"secondary": secondary}))
         return 0

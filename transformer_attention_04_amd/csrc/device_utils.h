@@ -78,6 +78,18 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Value of lane (lane ^ mask) for mask in {1..32} (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// max / sum of x over the lane pair (l, l ^ 32), on the VALU (v_permlane32_swap).
+// The swap hands each lane its partner's value in one of the two results and
+// keeps its own in the other, so max and sum of the pair are symmetric.
+__device__ __forceinline__ float pair32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Flip the sign bit of eight 16-bit values (exact negation, NaN kept).
 __device__ __forceinline__ uint4 negate8(uint4 u) {
     u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;

@@ -30,9 +30,10 @@
 //    2^8 in the exponent; otherwise the old shift stays (weights stay <= 256)
 //    and the O rescale is skipped.  Output and lse use the same shift as the
 //    row sum, so the result is the same softmax.
-//  * V^T rows are XOR-swizzled in 16-byte chunks by (row / 8) % 8 so that the
-//    transposing writes and the 16-byte MFMA operand reads avoid LDS bank
-//    conflicts.
+//  * V^T rows are XOR-swizzled in 16-byte chunks by (row / 16) % 8.  LDS
+//    serves 16 lanes per pass over 64 four-byte banks: 16 consecutive rows of
+//    144 bytes already fall on distinct banks for the 16-byte operand reads,
+//    and the swizzle spreads the transposing 8-byte writes (rows 8 apart).
 //  * Global memory is read and written through buffer resources sized to the
 //    valid rows: rows past the end read as 0 and their stores are dropped, so
 //    edge tiles need no branches.
@@ -45,6 +46,8 @@
 
 #include "attn_common.h"
 #include "device_utils.h"
+
+#include <type_traits>
 
 namespace sdpa {
 
@@ -174,7 +177,7 @@ void prefill_mfma_kernel(AttnParams p) {
             const uint32_t* w1 = (const uint32_t*)&vbuf[1];
             const uint32_t* w2 = (const uint32_t*)&vbuf[2];
             const uint32_t* w3 = (const uint32_t*)&vbuf[3];
-            const int chunk = (kg >> 1) ^ (dc & 7);
+            const int chunk = (kg >> 1) ^ ((dc >> 1) & 7);  // rows dc*8 + j, j < 8
             uint16_t* base = Vt + chunk * 8 + (kg & 1) * 4;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -249,102 +252,108 @@ void prefill_mfma_kernel(AttnParams p) {
                     }
             }
             const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
-            const bool any_mask = edge || MASK == MASK_BOOL;
-            uint32_t keepbits = 0xffffffffu;  // bit kb*16 + r: key kept
-            if (any_mask) {
-                uint32_t mbits = 0xffffffffu;
-                if (MASK == MASK_BOOL) {
-                    const int mrow_bytes = (int)p.m_sr;
-                    const auto mr = make_rsrc((const uint8_t*)p.mask + mo + (int64_t)(q0 + wrow0) * p.m_sr + key0,
-                                              (qrows - 1 - wrow0) * (int)p.m_sr + (Sb - key0));
-                    mbits = 0;
+            // Register r of block kb holds local key kb*32 + (r/8)*16 + r%8 (+ 8hh + key0).
+            // A key is kept when that local index is below `lim` (and the bool mask says so).
+            uint32_t mbits = 0xffffffffu;
+            if (MASK == MASK_BOOL) {
+                const int mrow_bytes = (int)p.m_sr;
+                const auto mr = make_rsrc((const uint8_t*)p.mask + mo + (int64_t)(q0 + wrow0) * p.m_sr + key0,
+                                          (qrows - 1 - wrow0) * (int)p.m_sr + (Sb - key0));
+                mbits = 0;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const int off = lq * mrow_bytes + kb * 32 + c * 16 + hh * 8;
+                        uint2 u;
+                        if (p.mask_vec) {
+                            u = buf_load8(mr, off);
+                        } else {
+                            u.x = u.y = 0;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                u.x |= buf_load1(mr, off + j) << (8 * j);
+                                u.y |= buf_load1(mr, off + 4 + j) << (8 * j);
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const uint32_t byte = ((j < 4 ? u.x : u.y) >> (8 * (j & 3))) & 0xffu;
+                            mbits |= (byte != 0 ? 1u : 0u) << (kb * 16 + c * 8 + j);
+                        }
+                    }
+            }
+            int lim = Sb - (key0 + hh * 8);
+            if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
+
+            auto softmax_pv = [&](auto masked_tag) {
+                constexpr bool MASKED = decltype(masked_tag)::value;
+                if (MASKED) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int c = 0; c < 2; ++c) {
-                            const int off = lq * mrow_bytes + kb * 32 + c * 16 + hh * 8;
-                            uint2 u;
-                            if (p.mask_vec) {
-                                u = buf_load8(mr, off);
-                            } else {
-                                u.x = u.y = 0;
-#pragma unroll
-                                for (int j = 0; j < 4; ++j) {
-                                    u.x |= buf_load1(mr, off + j) << (8 * j);
-                                    u.y |= buf_load1(mr, off + 4 + j) << (8 * j);
-                                }
-                            }
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                const uint32_t byte = ((j < 4 ? u.x : u.y) >> (8 * (j & 3))) & 0xffu;
-                                mbits |= (byte != 0 ? 1u : 0u) << (kb * 16 + c * 8 + j);
-                            }
+                        for (int r = 0; r < 16; ++r) {
+                            const int li = kb * 32 + (r >> 3) * 16 + (r & 7);
+                            const bool ok = li < lim && ((mbits >> (kb * 16 + r)) & 1u);
+                            s[kb][r] = ok ? s[kb][r] : kNegInf;
                         }
                 }
-                keepbits = 0;
+                float mx = kNegInf;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                mx = pair32_max(mx);
+                const float mxs = mx * cfac;                    // block max, log2 units
+                const bool raise = mxs > sh_run + kLazyRescale;  // never for an all-masked block
+                const float sh_new = raise ? mxs : sh_run;
+                const float alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
+                sh_run = sh_new;
+                const float shift = (sh_new == kNegInf) ? 0.f : sh_new;
+                float tsum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
-                        bool ok = key < Sb && ((mbits >> (kb * 16 + r)) & 1u);
-                        if (CAUSAL) ok = ok && key <= my_row;
-                        keepbits |= (ok ? 1u : 0u) << (kb * 16 + r);
-                        s[kb][r] = ok ? s[kb][r] : kNegInf;
+                        float e = fast_exp2(fmaf(s[kb][r], cfac, -shift));
+                        if (MASKED) e = (s[kb][r] == kNegInf) ? 0.f : e;
+                        s[kb][r] = e;
+                        tsum += e;
                     }
-            }
-            float mx = kNegInf;
+                l_run = fmaf(l_run, alpha, tsum);
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, xor_lane(mx, 32));
-            const float mxs = mx * cfac;                    // block max, log2 units
-            const bool raise = mxs > sh_run + kLazyRescale;  // never for an all-masked block
-            const float sh_new = raise ? mxs : sh_run;
-            const float alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
-            sh_run = sh_new;
-            const float shift = (sh_new == kNegInf) ? 0.f : sh_new;
-            float tsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float e = fast_exp2(fmaf(s[kb][r], cfac, -shift));
-                    if (any_mask) e = ((keepbits >> (kb * 16 + r)) & 1u) ? e : 0.f;
-                    s[kb][r] = e;
-                    tsum += e;
+                    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
                 }
-            l_run = fmaf(l_run, alpha, tsum);
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-            }
-
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                    for (int c = 0; c < 2; ++c) {
+                        uint4 pb;
+                        pb.x = Tr::pack2(s[kb][c * 8 + 0], s[kb][c * 8 + 1]);
+                        pb.y = Tr::pack2(s[kb][c * 8 + 2], s[kb][c * 8 + 3]);
+                        pb.z = Tr::pack2(s[kb][c * 8 + 4], s[kb][c * 8 + 5]);
+                        pb.w = Tr::pack2(s[kb][c * 8 + 6], s[kb][c * 8 + 7]);
+                        const int lchunk = kb * 4 + c * 2 + hh;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    uint4 pb;
-                    pb.x = Tr::pack2(s[kb][c * 8 + 0], s[kb][c * 8 + 1]);
-                    pb.y = Tr::pack2(s[kb][c * 8 + 2], s[kb][c * 8 + 3]);
-                    pb.z = Tr::pack2(s[kb][c * 8 + 4], s[kb][c * 8 + 5]);
-                    pb.w = Tr::pack2(s[kb][c * 8 + 6], s[kb][c * 8 + 7]);
-                    const int lchunk = kb * 4 + c * 2 + hh;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int d = db * 32 + lq;
-                        const uint4 a = *(const uint4*)(Vt + d * VS + ((lchunk ^ ((d >> 3) & 7)) * 8));
-                        acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb), acc[db]);
+                        for (int db = 0; db < NDB; ++db) {
+                            const int d = db * 32 + lq;
+                            const uint4 a = *(const uint4*)(Vt + d * VS + ((lchunk ^ ((d >> 4) & 7)) * 8));
+                            acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb), acc[db]);
+                        }
                     }
-                }
+            };
+            if (edge || MASK == MASK_BOOL)
+                softmax_pv(std::integral_constant<bool, true>{});
+            else
+                softmax_pv(std::integral_constant<bool, false>{});
         }
         if (t + 1 < ntiles) store_tile((t + 1) & 1);
         __syncthreads();
     }
 
     // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
-    const float l_tot = l_run + xor_lane(l_run, 32);
+    const float l_tot = pair32_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const int o_rs = (int)(p.o_sr * 2);
     const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + D * 2);
