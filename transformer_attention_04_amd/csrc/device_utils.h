@@ -90,6 +90,12 @@ __device__ __forceinline__ float pair32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait until every vector-memory load issued so far has returned (s_waitcnt
+// vmcnt(0); expcnt and lgkmcnt left at their maxima, gfx9 encoding).  Used once
+// before a loop whose first use of those registers would otherwise carry the
+// wait into every iteration, where it would also wait for prefetches.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Flip the sign bit of eight 16-bit values (exact negation, NaN kept).
 __device__ __forceinline__ uint4 negate8(uint4 u) {
     u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;

@@ -30,10 +30,13 @@
 //    2^8 in the exponent; otherwise the old shift stays (weights stay <= 256)
 //    and the O rescale is skipped.  Output and lse use the same shift as the
 //    row sum, so the result is the same softmax.
-//  * V^T rows are XOR-swizzled in 16-byte chunks by (row / 16) % 8.  LDS
-//    serves 16 lanes per pass over 64 four-byte banks: 16 consecutive rows of
-//    144 bytes already fall on distinct banks for the 16-byte operand reads,
-//    and the swizzle spreads the transposing 8-byte writes (rows 8 apart).
+//  * LDS layouts were chosen by measuring bank conflicts on gfx950 (the
+//    SQ_LDS_BANK_CONFLICT counter over every access pattern of this kernel):
+//    K rows padded to D+8 elements, and V^T rows of 64+8 elements with no
+//    swizzle, read conflict-free; the transposing 8-byte V^T writes are
+//    conflict-free when the 16 consecutive threads of a group take the 16
+//    four-key groups of one 8-column chunk (rows 8 apart, columns 8 bytes
+//    apart).
 //  * Global memory is read and written through buffer resources sized to the
 //    valid rows: rows past the end read as 0 and their stores are dropped, so
 //    edge tiles need no branches.
@@ -136,6 +139,7 @@ void prefill_mfma_kernel(AttnParams p) {
         const uint4 u = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
         qreg[kk] = p.neg ? negate8(u) : u;
     }
+    wait_vmem_all();
 
     const uint16_t* kbase = (const uint16_t*)p.k + ko;
     const uint16_t* vbase = (const uint16_t*)p.v + vo;
@@ -155,7 +159,7 @@ void prefill_mfma_kernel(AttnParams p) {
             kbuf[i] = buf_load16(kr, r * k_rs + col * 2);
         }
         if (VIT == 256 || tid < VIT) {
-            const int dc = tid % (D / 8), kg = tid / (D / 8);
+            const int kg = tid % (BN / 4), dc = tid / (BN / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, (kg * 4 + r) * v_rs + dc * 16);
         }
@@ -172,13 +176,12 @@ void prefill_mfma_kernel(AttnParams p) {
             *(uint4*)(Ks + row * KS + col) = kbuf[i];
         }
         if (VIT == 256 || tid < VIT) {
-            const int dc = tid % (D / 8), kg = tid / (D / 8);
+            const int kg = tid % (BN / 4), dc = tid / (BN / 4);
             const uint32_t* w0 = (const uint32_t*)&vbuf[0];
             const uint32_t* w1 = (const uint32_t*)&vbuf[1];
             const uint32_t* w2 = (const uint32_t*)&vbuf[2];
             const uint32_t* w3 = (const uint32_t*)&vbuf[3];
-            const int chunk = (kg >> 1) ^ ((dc >> 1) & 7);  // rows dc*8 + j, j < 8
-            uint16_t* base = Vt + chunk * 8 + (kg & 1) * 4;
+            uint16_t* base = Vt + kg * 4;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 // keys kg*4 .. kg*4+3 of column dc*8 + j, as two packed pairs
@@ -298,11 +301,17 @@ void prefill_mfma_kernel(AttnParams p) {
                             s[kb][r] = ok ? s[kb][r] : kNegInf;
                         }
                 }
-                float mx = kNegInf;
+                // row max over this lane's 32 scores: four short chains
+                float m4[4];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int i = 0; i < 4; ++i) {
+                    const int kb = i >> 1, r0 = (i & 1) * 8;
+                    float m = fmaxf(s[kb][r0 + 0], s[kb][r0 + 1]);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                    for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
+                    m4[i] = m;
+                }
+                float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
                 mx = pair32_max(mx);
                 const float mxs = mx * cfac;                    // block max, log2 units
                 const bool raise = mxs > sh_run + kLazyRescale;  // never for an all-masked block
@@ -310,7 +319,6 @@ void prefill_mfma_kernel(AttnParams p) {
                 const float alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
                 sh_run = sh_new;
                 const float shift = (sh_new == kNegInf) ? 0.f : sh_new;
-                float tsum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -318,8 +326,14 @@ void prefill_mfma_kernel(AttnParams p) {
                         float e = fast_exp2(fmaf(s[kb][r], cfac, -shift));
                         if (MASKED) e = (s[kb][r] == kNegInf) ? 0.f : e;
                         s[kb][r] = e;
-                        tsum += e;
                     }
+                // this lane's share of the block's row sum, as a fixed tree
+                float p8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    p8[i] = (s[i >> 2][(i & 3) * 4 + 0] + s[i >> 2][(i & 3) * 4 + 1]) +
+                            (s[i >> 2][(i & 3) * 4 + 2] + s[i >> 2][(i & 3) * 4 + 3]);
+                const float tsum = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
                 l_run = fmaf(l_run, alpha, tsum);
                 if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
@@ -338,7 +352,7 @@ void prefill_mfma_kernel(AttnParams p) {
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
                             const int d = db * 32 + lq;
-                            const uint4 a = *(const uint4*)(Vt + d * VS + ((lchunk ^ ((d >> 4) & 7)) * 8));
+                            const uint4 a = *(const uint4*)(Vt + d * VS + lchunk * 8);
                             acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb), acc[db]);
                         }
                     }
