@@ -118,9 +118,7 @@ def bench_prefill(name, steps, warmup, scale=None, mask=None, device="cuda"):
     w = inputs.WORKLOADS[name]
     q, k, v = (t.to(device) for t in inputs.workload_inputs(name))
     md = mask.to(device) if mask is not None else None
-    out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:-1] + (1,), dtype=torch.float32, device=device)
-    fn = lambda: S.sdpa_fwd(q, k, v, attn_mask=md, is_causal=w["causal"], scale=scale, out=out, lse=lse)
+    fn = S.PreparedSdpaFwd(q, k, v, attn_mask=md, is_causal=w["causal"], scale=scale)
     wall, per = time_launches(fn, steps, warmup)
     flops, pairs = flops_prefill(w["B"], w["Hq"], w["L"], w["S"], w["E"], w["causal"])
     kern_ms = sum(per) / len(per)
@@ -139,13 +137,10 @@ def bench_decode(steps, warmup, device="cuda"):
     from transformer_attention_04_amd import inputs
     from transformer_attention_04_amd import sdpa as S
     q, k, v = (t.to(device) for t in inputs.workload_inputs("bf16_gqa_decode"))
-    out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:-1] + (1,), dtype=torch.float32, device=device)
-    nws = S.sdpa_fwd_workspace_size(q, k, v, enable_gqa=True)
-    ws = torch.empty(nws, dtype=torch.uint8, device=device)
-    fn = lambda: S.sdpa_fwd(q, k, v, enable_gqa=True, out=out, lse=lse, workspace=ws)
+    fn = S.PreparedSdpaFwd(q, k, v, enable_gqa=True)
+    nws = 0 if fn.workspace is None else fn.workspace.numel()
     wall, per = time_launches(fn, steps, warmup)
-    nbytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + fn.out.numel()) + 4 * fn.lse.numel()
     kern_ms = sum(per) / len(per)
     return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "bytes": nbytes,
             "gbs": nbytes / (kern_ms * 1e-3) / 1e9, "frac_hbm": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

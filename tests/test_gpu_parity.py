@@ -247,3 +247,21 @@ def test_repeatable_bit_for_bit():
     a = S.sdpa_fwd(qd, kd, vd, enable_gqa=True)
     b = S.sdpa_fwd(qd, kd, vd, enable_gqa=True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prepared_call_matches_plain_call():
+    """PreparedSdpaFwd (arguments marshalled once) gives the bytes of sdpa_fwd, call after call."""
+    q, k, v = inputs.randn_qkv((2, 8, 300, 96), (2, 2, 300, 96), (2, 2, 300, 96), "bf16", seed=12)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref = S.sdpa_fwd(qd, kd, vd, is_causal=True, enable_gqa=True)
+    prep = S.PreparedSdpaFwd(qd, kd, vd, is_causal=True, enable_gqa=True)
+    for _ in range(3):
+        o, l = prep()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0].reshape(o.shape)) and torch.equal(l.reshape(ref[1].shape), ref[1])
+    qd, kd, vd = (t.to(DEV) for t in inputs.randn_qkv((3, 8, 1, 128), (3, 2, 900, 128), (3, 2, 900, 128),
+                                                       "bf16", seed=13))
+    ref = S.sdpa_fwd(qd, kd, vd, enable_gqa=True)
+    o, l = S.PreparedSdpaFwd(qd, kd, vd, enable_gqa=True)()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0].reshape(o.shape)) and torch.equal(l.reshape(ref[1].shape), ref[1])

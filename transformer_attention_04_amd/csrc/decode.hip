@@ -83,21 +83,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    for (int key0 = ks + wave * 32; key0 < ke; key0 += 128) {
-        uint4 ka[2][NKK];
+    // This split's keys through buffer resources: keys past the split read as 0.
+    const int nk = max(ke - ks, 0);
+    const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
+    const auto kr = make_rsrc(kp + (int64_t)ks * p.k_sr, (nk - 1) * k_rs + D * 2);
+    const auto vr = make_rsrc(vp + (int64_t)ks * p.v_sr, (nk - 1) * v_rs + D * 2);
+    auto load = [&](int key0, uint4 (&ka)[2][NKK], uint4 (&va)[8]) {
+        const int lk = key0 - ks;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int key = key0 + kb * 16 + n;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
-                ka[kb][kk] = key < ke ? *(const uint4*)(kp + (int64_t)key * p.k_sr + kk * 32 + grp * 8) : zero4();
-        }
-        uint4 va[8];
+                ka[kb][kk] = buf_load16(kr, (lk + kb * 16 + n) * k_rs + (kk * 32 + grp * 8) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int key = key0 + grp + 4 * i;
-            va[i] = (key < ke && n < NDC) ? *(const uint4*)(vp + (int64_t)key * p.v_sr + n * 8) : zero4();
-        }
+        for (int i = 0; i < 8; ++i)
+            va[i] = buf_load16(vr, n < NDC ? (lk + grp + 4 * i) * v_rs + n * 16 : 0x7ffffff0);
+    };
+    // One 32-key sub-tile: scores, online softmax, P V.
+    auto compute = [&](int key0, const uint4 (&ka)[2][NKK], const uint4 (&va)[8]) {
         f32x4_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -167,6 +170,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
         }
         wave_lds_sync();
+    };
+    // Each wavefront takes every fourth 32-key sub-tile; the next one's K and V
+    // are in flight while the current one is computed.
+    uint4 kaA[2][NKK], vaA[8], kaB[2][NKK], vaB[8];
+    int key0 = ks + wave * 32;
+    if (key0 < ke) load(key0, kaA, vaA);
+    for (; key0 < ke; key0 += 256) {
+        if (key0 + 128 < ke) load(key0 + 128, kaB, vaB);
+        compute(key0, kaA, vaA);
+        if (key0 + 128 >= ke) break;
+        if (key0 + 256 < ke) load(key0 + 256, kaA, vaA);
+        compute(key0 + 128, kaB, vaB);
     }
 
     // Combine the 4 lane groups (same column chunk, different keys) ...

@@ -257,3 +257,46 @@ def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
     if batched:
         return out3.unsqueeze(0), lse.unsqueeze(0)
     return out3, lse
+
+
+class PreparedSdpaFwd:
+    """sdpa_fwd with its arguments marshalled once, for repeated calls on the same buffers.
+
+    Calling the object enqueues the same C call again (one ctypes call per
+    launch) on the stream that was current when it was prepared; the tensors
+    must stay alive and keep their storage.  Returns (out, lse).
+    """
+
+    def __init__(self, query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+                 enable_gqa=False, num_splits=0, out=None, lse=None):
+        lib = load_library()
+        _require_gpu(query, key, value, attn_mask, out, lse)
+        q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+        k4, v4 = _expand_batch(q4, k4), _expand_batch(q4, v4)
+        B, Hq, L, _ = q4.shape
+        S, Ev = v4.shape[2], v4.shape[3]
+        m4, mdt = _mask_4d(attn_mask, q4, S)
+        dev = query.device
+        self.out = out if out is not None else torch.empty((B, Hq, L, Ev), dtype=query.dtype, device=dev)
+        self.lse = lse if lse is not None else torch.empty((B, Hq, L, 1), dtype=torch.float32, device=dev)
+        self._keep = (q4, k4, v4, m4)
+        self._d = [_desc(q4), _desc(k4), _desc(v4), _desc(self.out), _desc(self.lse)]
+        self._dm = _desc(m4) if m4 is not None else None
+        pm = ctypes.byref(self._dm) if self._dm is not None else None
+        n = ctypes.c_size_t(0)
+        _check(lib.sdpa_fwd_workspace_size(_DTYPE[query.dtype], self._d[0], self._d[1], self._d[2], pm,
+                                           int(bool(is_causal)), int(bool(enable_gqa)), int(num_splits),
+                                           ctypes.byref(n)))
+        self.workspace = torch.empty(n.value, dtype=torch.uint8, device=dev) if n.value else None
+        self._scale = ctypes.c_double(float(scale)) if scale is not None else None
+        self._args = (_DTYPE[query.dtype], ctypes.byref(self._d[0]), ctypes.byref(self._d[1]),
+                      ctypes.byref(self._d[2]), pm, mdt, float(dropout_p), int(bool(is_causal)),
+                      ctypes.byref(self._scale) if self._scale is not None else None, int(bool(enable_gqa)),
+                      ctypes.byref(self._d[3]), ctypes.byref(self._d[4]),
+                      self.workspace.data_ptr() if self.workspace is not None else None, n.value,
+                      int(num_splits), _stream(dev))
+        self._fn = lib.sdpa_fwd
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out, self.lse
