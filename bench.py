@@ -57,23 +57,23 @@ def flops_prefill(B, H, L, S, E, causal):
 
 
 def time_launches(fn, steps, warmup):
-    """Run fn warmup times, then time `steps` calls: wall time between two
-    synchronizes, plus one event pair per call on torch's current stream (the
-    stream the kernels are launched on)."""
+    """Run fn warmup times, then time `steps` back-to-back calls: wall time
+    between two synchronizes, and GPU time from one pair of events recorded on
+    torch's current stream (the stream the kernels are launched on) around the
+    whole timed region.  Returns (wall seconds, [GPU ms per call])."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    a.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]  # ms
-    return wall, per
+    return wall, [a.elapsed_time(b) / steps]
 
 
 def load_traffic(kernel):
