@@ -35,7 +35,7 @@ PEAK_FP32_TFLOPS = 157.3    # fp32 matrix peak (the fp32 path runs on the vector
 PEAK_HBM_GBS = 8000.0       # HBM3E
 METRIC = "attn fwd TFLOP/s (% MFMA peak) prefill; GB/s (% HBM peak) split-KV decode"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["prefill_mfma.h", "device_utils.h", "attn_common.h", "decode.hip"]
+KERNEL_SOURCES = ["prefill_pp.h", "prefill_mfma.h", "device_utils.h", "attn_common.h", "decode.hip"]
 
 
 def kernel_source_hash():
@@ -257,8 +257,8 @@ def main(argv=None):
                    "E": w["E"], "is_causal": True, "scale": "1/sqrt(128)", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic("prefill_mfma_kernel"),
-                     "kernel": "prefill_mfma_kernel<BF16,128,causal>",
+                     "traffic": load_traffic("prefill_pp_kernel"),
+                     "kernel": "prefill_pp_kernel<BF16,128,causal>",
                      "flop_per_launch": main_res["flops"]},
         "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline(),
         "secondary": secondary,

@@ -1,4 +1,7 @@
-// Single-pass attention forward for bf16 / fp16 inputs on gfx950 matrix cores.
+// Single-pass attention forward for bf16 / fp16 inputs on gfx950 matrix cores:
+// the kernel for float and boolean masks and for packed variable-length
+// batches, and the dispatch of all bf16 / fp16 forward calls (unmasked batched
+// calls go to the ping-pong kernel of prefill_pp.h).
 //
 // Method: the blocked form of exact attention described on the khchao.com NN
 // Lab page ("FlashAttention Tiling & Online Softmax Algorithm"): queries in
@@ -49,19 +52,11 @@
 
 #include "attn_common.h"
 #include "device_utils.h"
+#include "prefill_pp.h"
 
 #include <type_traits>
 
 namespace sdpa {
-
-// Swap bits 2 and 3 of a key index within its 32-key block.
-__device__ __forceinline__ int swap_bits23(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-// Exponent margin (log2 units) by which a block max may exceed the current
-// shift before the shift is raised.
-constexpr float kLazyRescale = 8.0f;
 
 template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -401,14 +396,16 @@ template <typename Tr, int D>
 hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool varlen,
                             hipStream_t s) {
     if (varlen) {
+        // packed segments keep the 128-row kernel: 256-row tiles waste more
+        // rows on short segments
         if (mask != MASK_NONE) return hipErrorInvalidValue;
         return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, true>(p, s)
                       : launch_prefill_one<Tr, D, false, MASK_NONE, true>(p, s);
     }
     switch (mask) {
         case MASK_NONE:
-            return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, false>(p, s)
-                          : launch_prefill_one<Tr, D, false, MASK_NONE, false>(p, s);
+            return causal ? launch_prefill_pp<Tr, D, true, false>(p, s)
+                          : launch_prefill_pp<Tr, D, false, false>(p, s);
         case MASK_FLOAT:
             return causal ? launch_prefill_one<Tr, D, true, MASK_FLOAT, false>(p, s)
                           : launch_prefill_one<Tr, D, false, MASK_FLOAT, false>(p, s);
