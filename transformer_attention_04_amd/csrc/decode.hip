@@ -68,9 +68,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         const uint16_t* qp = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh +
                              (int64_t)i * p.q_sr;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const uint4 u = nvalid ? *(const uint4*)(qp + kk * 32 + grp * 8) : zero4();
-            qreg[kk] = p.neg ? negate8(u) : u;
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = nvalid ? *(const uint4*)(qp + kk * 32 + grp * 8) : zero4();
+        // negated after all loads are issued (a select per load would wait for each in turn)
+        if (p.neg) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
         }
     }
     const uint16_t* kp = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;

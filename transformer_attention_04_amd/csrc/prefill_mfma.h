@@ -1,7 +1,7 @@
 // Single-pass attention forward for bf16 / fp16 inputs on gfx950 matrix cores:
 // the kernel for float and boolean masks and for packed variable-length
 // batches, and the dispatch of all bf16 / fp16 forward calls (unmasked batched
-// calls go to the ping-pong kernel of prefill_pp.h).
+// calls go to the eight-wave kernel of prefill_pp.h).
 //
 // Method: the blocked form of exact attention described on the khchao.com NN
 // Lab page ("FlashAttention Tiling & Online Softmax Algorithm"): queries in
@@ -130,11 +130,13 @@ void prefill_mfma_kernel(AttnParams p) {
     const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
     uint4 qreg[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 u = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
-        qreg[kk] = p.neg ? negate8(u) : u;
-    }
+    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
     wait_vmem_all();
+    // negated after all loads have landed (a select per load would wait for each in turn)
+    if (p.neg) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
+    }
 
     const uint16_t* kbase = (const uint16_t*)p.k + ko;
     const uint16_t* vbase = (const uint16_t*)p.v + vo;
@@ -404,8 +406,13 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
     }
     switch (mask) {
         case MASK_NONE:
-            return causal ? launch_prefill_pp<Tr, D, true, false>(p, s)
-                          : launch_prefill_pp<Tr, D, false, false>(p, s);
+            // the eight-wave kernel masks scores with -inf and needs a positive
+            // scale for exp2(-inf * scale) = 0; a zero scale stays here
+            if (p.scale_log2 > 0.f)
+                return causal ? launch_prefill_pp<Tr, D, true, false>(p, s)
+                              : launch_prefill_pp<Tr, D, false, false>(p, s);
+            return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, false>(p, s)
+                          : launch_prefill_one<Tr, D, false, MASK_NONE, false>(p, s);
         case MASK_FLOAT:
             return causal ? launch_prefill_one<Tr, D, true, MASK_FLOAT, false>(p, s)
                           : launch_prefill_one<Tr, D, false, MASK_FLOAT, false>(p, s);

@@ -1,37 +1,38 @@
-// Single-pass attention forward for bf16 / fp16 inputs on gfx950, scheduled as
-// two wavefront groups in lock step ("ping-pong").
+// Single-pass attention forward for bf16 / fp16 inputs on gfx950: eight
+// wavefronts per workgroup, each owning 32 query rows, all running the same
+// software-pipelined program over 64-key blocks.
 //
 // Method: the blocked, online-softmax form of exact attention described on the
 // khchao.com NN Lab page ("FlashAttention Tiling & Online Softmax Algorithm");
 // the result is softmax(scale * Q K^T + mask) V with its logsumexp, as the
 // exactref.ai "scaled_dot_product_attention" Full specification defines it.
 //
-// Why this schedule.  On gfx950 a single wavefront issues a plain vector
-// instruction only every ~4-6 cycles and an exponential every ~9, so the
-// softmax of a 64-key block (about 150 vector instructions for 32 query rows)
-// occupies one wavefront about as long as its 32 matrix instructions keep the
-// matrix core busy (32 cycles each at E = 128); the vector work that does not
-// depend on the block's row max is therefore done between matrix instructions.  A workgroup is therefore 8 wavefronts (256 query
-// rows, 32 per wavefront); waves w and w + 4 share a SIMD.  Waves 0-3 (group A)
-// and 4-7 (group B) run the same two-slot program, group B one slot behind,
-// with a workgroup barrier between slots:
+// Schedule.  On gfx950 one wavefront issues a plain vector instruction every
+// ~5.7 cycles and an exponential every ~9.3, while a 32x32x16 matrix
+// instruction keeps the matrix core busy for 32 cycles; about five vector
+// instructions per matrix instruction come for free when two wavefronts share
+// a SIMD.  So the softmax of a block is spread between matrix instructions of
+// the same wavefront.  Iteration t of a wavefront:
 //
-//   slot X(t)  S^T = K Q^T of block t, then O^T += V^T P^T of block t - 1
-//              (32 MFMAs, operands read from LDS two products ahead of use);
-//              between the score products the weights of block t - 1 are
-//              packed to P^T and summed into the row sum
-//   slot Y(t)  row max and lazy shift of block t, its unnormalised weights
-//              (32 exponentials), the O rescale when the shift moved;
-//              direct-to-LDS loads of block t + 3
+//   section 1  S^T(t + 1) = K(t + 1) Q^T (16 products at E = 128) with the
+//              softmax of block t between them: row max (lazy shift, raised
+//              only when the block max exceeds it by 2^8), then per product
+//              four scaled exponentials, then packing of P^T(t) to 16 bits
+//   (rare)     O rescale when some lane raised its shift
+//   section 2  O^T += V^T(t) P^T(t) (16 products) with the row sum of block t
+//              between them
+//   end        direct-to-LDS loads of block t + 3, one workgroup barrier
 //
-// so while one wavefront of a SIMD issues matrix instructions the other does
-// its vector and memory work.  Every barrier is preceded by a wait for the
-// wave's own LDS reads, so a buffer may be overwritten one slot after its last
-// reader's barrier.
+// Matrix operands are read from LDS six products ahead of their use, in one
+// stream (K of block t + 1, then V of block t).  Scores are transposed (one
+// query per lane), so P^T is the B operand of the second product without any
+// data movement, and Q^T stays in registers for the whole loop.  The vector
+// work is pinned in place with empty volatile statements: without them the
+// compiler sinks it past the rescale branch into section 2 in one block.
 //
 // Key and value blocks travel HBM -> LDS by direct-to-LDS buffer loads (no
-// staging registers, no LDS write instructions) into a ring of 4 stages:
-// group A loads K, group B loads V, three blocks ahead.  Each lane of a load
+// staging registers, no LDS write instructions) into a ring of 4 stages, three
+// blocks ahead: waves 0-3 load K, waves 4-7 load V.  Each lane of a load
 // chooses which global 16-byte chunk lands in its LDS slot, so the layouts are
 // free permutations of chunks, picked to make every operand read free of bank
 // conflicts (64 banks; 16-byte reads serviced 16 lanes at a time, 8-byte reads
@@ -45,29 +46,32 @@
 //      is read with ds_read_b64_tr_b16: within 16 lanes, lane i receives
 //      column i of a 4 x 16 block assembled from four lanes' 8-byte reads, so
 //      each lane gets 4 consecutive keys of one head-dimension column.
-// Scores are transposed (one query per lane), the running max is lazy, and
-// buffer resources turn reads past the last key into zeros.
-//
-// Timing of block t's stage (A runs slot k in phase k + 1, B in phase k + 2,
-// slots numbered X(0) = 0, Y(0) = 1, X(1) = 2, ...): loaded in Y(t - 3) (phases
-// 2t - 4 for K by A, 2t - 3 for V by B); each wave waits for its loads at the
-// end of its Y(t - 1) (phases 2t and 2t + 1); K is read in X(t) (phases 2t + 1,
-// 2t + 2) and V in X(t + 1) (phases 2t + 3, 2t + 4); block t + 4 is loaded into
-// the same stage in Y(t + 1) (phases 2t + 4 and 2t + 5): the V reads of block t
-// by group B share phase 2t + 4 with the K loads by group A, which is why K
-// and V sit in separate halves of a stage and the ring has four stages.
-// The per-wave register state between slots: the scores s of block t
-// (X(t) -> Y(t)), its weights e and rescale factor (Y(t) -> X(t + 1)), O^T.
+// The barrier ending iteration t follows each wave's wait for its loads of
+// block t + 2, so block t + 3 may overwrite the stage of block t - 1, whose
+// last reader (the P.V products of iteration t - 1) is behind that barrier.
+// Buffer resources turn reads past the last key into zeros; keys past the
+// last key or past the causal diagonal get the score -inf (edge blocks only).
 #pragma once
 
 #include "attn_common.h"
 #include "device_utils.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace sdpa {
 
-constexpr int kPPBlockM = 256;  // query rows per ping-pong workgroup
+constexpr int kPPBlockM = 256;  // query rows per workgroup
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 // Swap bits 2 and 3 of a key index within its 32-key block.
 __device__ __forceinline__ int swap_bits23(int r) {
@@ -117,6 +121,23 @@ __device__ __forceinline__ void pp_dma16(u32x4_t rsrc, int voff, uint32_t m0) {
         : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// max of three floats in one instruction, without the quieting copies the
+// compiler adds in front of fmaxf on values it cannot prove canonical (a NaN
+// score makes its row NaN through the exponentials either way).  Only used on
+// scores produced by matrix instructions of the previous iteration.
+__device__ __forceinline__ float pp_max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Pins a value's computation to this point of the instruction stream.  Without
+// it, code motion after scheduling sinks work into the block that first uses
+// it (past the branch of the rare O rescale, or past a barrier), which would
+// undo the interleaving of vector work with matrix instructions.
+__device__ __forceinline__ void pp_pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pp_pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // Raw buffer resource as four scalars (for the asm operand).
 __device__ __forceinline__ u32x4_t pp_rsrc(const void* base, int bytes) {
@@ -198,17 +219,8 @@ void prefill_pp_kernel(AttnParams p) {
                           : CAUSAL ? min(ntiles - 1, (q0 + wrow0 + 31) / BN)
                                    : ntiles - 1;
 
-    // Q^T operand, resident for the whole loop (negated when the scale is negative).
-    uint4 qreg[NKK];
-    {
-        const int q_rs = (int)(p.q_sr * 2);
-        const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const uint4 u = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
-            qreg[kk] = p.neg ? negate8(u) : u;
-        }
-    }
+
+    uint4 qreg[NKK];  // Q^T operand, resident for the whole loop (loaded in the prologue)
 
     // Direct-to-LDS loads of a block: group A moves K, group B moves V, NDMA
     // loads of 64 chunks per wave.  g_off[i] is the global byte offset (within
@@ -240,14 +252,11 @@ void prefill_pp_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) pp_dma16(rs, g_off[i], dst + i * 1024);
     };
-    // End of slot Y(t): the loads of block t + 1 must have landed; those of
-    // blocks t + 2 and t + 3 (issued in Y(t - 1) and Y(t) when they exist;
-    // blocks 0-2 come from the prologue) may still be in flight.
-    auto barrier_y = [&](int t) {
-        const int newer = (t + 2 >= 3 && t + 2 < ntiles ? 1 : 0) + (t + 3 < ntiles ? 1 : 0);
-        if (newer == 2)
-            pp_barrier<2 * NDMA>();
-        else if (newer == 1)
+    // End of iteration t: the loads of block t + 2 (issued in iteration t - 1,
+    // or in the prologue) must have landed; those of block t + 3, issued in
+    // iteration t when it exists, may still be in flight.
+    auto barrier_iter = [&](int t) {
+        if (t + 3 < ntiles)
             pp_barrier<NDMA>();
         else
             pp_barrier<0>();
@@ -268,9 +277,7 @@ void prefill_pp_kernel(AttnParams p) {
     float sh_run = kNegInf;  // running shift, log2 units (-inf until a kept key)
     float l_run = 0.f;       // this lane's share of the row sum relative to it
     const float cfac = p.scale_log2;
-    f32x16_t s[2];           // scores of block t, from X(t) to Y(t)
-    f32x16_t e[2];           // unnormalised weights of block t, from Y(t) to X(t + 1)
-    float alpha_e = 1.f;     // the rescale factor that came with e
+    f32x16_t sA[2], sB[2];   // scores of block t and t + 1, roles swapping each iteration
 
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
@@ -296,164 +303,197 @@ void prefill_pp_kernel(AttnParams p) {
         const char* Kb = (const char*)(smem + (t % NSTAGE) * STAGE) + k_lane;
         return *(const uint4*)(Kb + ((i & 1) * 2 * 16 * NC + (i >> 1) * 2 * 16) * 16);
     };
-
-    // Slot X(t): S^T = K Q^T of block t, with the weights of block t - 1 packed
-    // to P^T and summed in the gaps; then O^T += V^T P^T of block t - 1 (when PV
-    // is set).  Operands stream from LDS two products ahead of their use, in
-    // fenced order, so few are live at once.
     constexpr int NOP = 2 * NKK;  // products per half (16 at E = 128)
     static_assert(NOP == 4 * NDB, "one K operand read per P.V product");
-    auto slot_x = [&](int t, auto pv_tag) {
-        constexpr bool PV = decltype(pv_tag)::value;
+    constexpr int LA = 6;         // operand reads run this many products ahead
+
+    // S^T = K Q^T of block t into s_out, operands streamed from LDS.
+    auto scores = [&](int t, f32x16_t* s_out) {
         uint4 kop[NOP];
-        uint4 pb[4];
-        float p8[8];
-        kop[0] = read_k(t, 0);
-        kop[1] = read_k(t, 1);
-        s[0] = f32x16_t{};
-        s[1] = f32x16_t{};
+#pragma unroll
+        for (int j = 0; j < LA; ++j) kop[j] = read_k(t, j);
         fence();
 #pragma unroll
         for (int j = 0; j < NOP; ++j) {
-            if (j + 2 < NOP) kop[j + 2] = read_k(t, j + 2);
+            if (j + LA < NOP) kop[j + LA] = read_k(t, j + LA);
             fence();
-            s[j & 1] = Tr::mfma32(as_vec8<Tr>(kop[j]), as_vec8<Tr>(qreg[j >> 1]), s[j & 1]);
-            if (PV) {
-                // vector work of block t - 1 between the products: 13 items
-                // (4 packs, 8 partial sums, the row-sum update) spread evenly
-                // over the NOP products
-#pragma unroll
-                for (int w = (j * 13) / NOP; w < ((j + 1) * 13) / NOP; ++w) {
-                    if (w < 4) {
-                        const int kb = w >> 1, c = w & 1;
-                        uint4 u;
-                        u.x = Tr::pack2(e[kb][c * 8 + 0], e[kb][c * 8 + 1]);
-                        u.y = Tr::pack2(e[kb][c * 8 + 2], e[kb][c * 8 + 3]);
-                        u.z = Tr::pack2(e[kb][c * 8 + 4], e[kb][c * 8 + 5]);
-                        u.w = Tr::pack2(e[kb][c * 8 + 6], e[kb][c * 8 + 7]);
-                        pb[kb * 2 + c] = u;
-                    } else if (w < 12) {
-                        const int i = w - 4;
-                        p8[i] = (e[i >> 2][(i & 3) * 4 + 0] + e[i >> 2][(i & 3) * 4 + 1]) +
-                                (e[i >> 2][(i & 3) * 4 + 2] + e[i >> 2][(i & 3) * 4 + 3]);
-                    } else {
-                        const float tsum = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
-                        l_run = fmaf(l_run, alpha_e, tsum);
-                    }
-                }
-            }
+            s_out[j & 1] = Tr::mfma32(as_vec8<Tr>(kop[j]), as_vec8<Tr>(qreg[j >> 1]), j < 2 ? f32x16_t{} : s_out[j & 1]);
             fence();
-        }
-        if (PV) {
-            uint4 vop[NOP];
-            vop[0] = read_v(t - 1, 0);
-            vop[1] = read_v(t - 1, 1);
-            fence();
-#pragma unroll
-            for (int j = 0; j < NOP; ++j) {
-                if (j + 2 < NOP) vop[j + 2] = read_v(t - 1, j + 2);
-                fence();
-                acc[j % NDB] = Tr::mfma32(as_vec8<Tr>(vop[j]), as_vec8<Tr>(pb[j / NDB]), acc[j % NDB]);
-                fence();
-            }
         }
     };
 
-    // Slot Y(t): row max and shift of block t, its unnormalised weights e;
-    // the O rescale when the shift moved.  Exponentials are issued 16 at a time
-    // on independent operands (fenced groups).
-    auto slot_y = [&](int t) {
+    // One iteration for block t: the scores of block t + 1 on the matrix core
+    // with the softmax of block t between the products, then O^T += V^T P^T of
+    // block t with its row sum between the products.
+    // Scores of keys outside the block's kept range (past the last key, or past
+    // the causal diagonal) become -inf in place; their weights then come out
+    // as exp2(-inf) = 0 (the scale is positive here).
+    auto mask_scores = [&](int t, f32x16_t* s_cur) {
         const int key0 = t * BN;
-        // s[kb][8c + j] is the score of key key0 + 32kb + 16c + 8hh + j for query my_row.
-        const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
+        // s_cur[kb][8c + j] is the score of key key0 + 32kb + 16c + 8hh + j for query my_row.
         int lim = Sb - (key0 + hh * 8);
         if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
-        float alpha = 1.f;
-        auto softmax = [&](auto masked_tag) {
-            constexpr bool MASKED = decltype(masked_tag)::value;
-            if (MASKED) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int li = kb * 32 + (r >> 3) * 16 + (r & 7);
-                        s[kb][r] = li < lim ? s[kb][r] : kNegInf;
-                    }
+            for (int r = 0; r < 16; ++r) {
+                const int li = kb * 32 + (r >> 3) * 16 + (r & 7);
+                s_cur[kb][r] = li < lim ? s_cur[kb][r] : kNegInf;
             }
-            float m4[4];
+    };
+    auto iteration = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
+        uint4 pb[4];
+        float m4[4];
+        float alpha = 1.f, shift = 0.f;
+        // the 16 steps of the softmax, one after each score product (E = 128;
+        // smaller head dims run several steps per product)
+        auto soft_step = [&](auto step_tag) {
+            constexpr int st = decltype(step_tag)::value;
+            if constexpr (st < 4) {
+                const int kb = st >> 1, r0 = (st & 1) * 8;
+                const float a = pp_max3(s_cur[kb][r0 + 0], s_cur[kb][r0 + 1], s_cur[kb][r0 + 2]);
+                const float b = pp_max3(s_cur[kb][r0 + 3], s_cur[kb][r0 + 4], s_cur[kb][r0 + 5]);
+                m4[st] = pp_max3(a, b, pp_max3(s_cur[kb][r0 + 6], s_cur[kb][r0 + 7], s_cur[kb][r0 + 7]));
+            } else if constexpr (st == 4) {
+                float mx = pp_max3(pp_max3(m4[0], m4[1], m4[2]), m4[3], m4[3]);
+                mx = pair32_max(mx);
+                const float mxs = mx * cfac;
+                const bool raise = mxs > sh_run + kLazyRescale;
+                const float sh_new = raise ? mxs : sh_run;
+                alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
+                sh_run = sh_new;
+                shift = (sh_new == kNegInf) ? 0.f : sh_new;
+            } else if constexpr (st < 13) {
+                // four weights per step, in place
+                const int base = (st - 5) * 4, kb = base >> 4, r0 = base & 15;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kb = i >> 1, r0 = (i & 1) * 8;
-                float m = fmaxf(s[kb][r0 + 0], s[kb][r0 + 1]);
+                for (int r = r0; r < r0 + 4; ++r) s_cur[kb][r] = fmaf(s_cur[kb][r], cfac, -shift);
 #pragma unroll
-                for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
-                m4[i] = m;
-            }
-            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-            mx = pair32_max(mx);
-            const float mxs = mx * cfac;
-            const bool raise = mxs > sh_run + kLazyRescale;
-            const float sh_new = raise ? mxs : sh_run;
-            alpha = raise ? fast_exp2(sh_run - sh_new) : 1.f;
-            sh_run = sh_new;
-            const float shift = (sh_new == kNegInf) ? 0.f : sh_new;
-            fence();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) e[kb][r] = fmaf(s[kb][r], cfac, -shift);
-                fence();
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float w = fast_exp2(e[kb][r]);
-                    // masked keys by index (not by the score)
-                    if (MASKED) w = (kb * 32 + (r >> 3) * 16 + (r & 7)) < lim ? w : 0.f;
-                    e[kb][r] = w;
+                for (int r = r0; r < r0 + 4; ++r) {
+                    float e = fast_exp2(s_cur[kb][r]);
+                    pp_pin(e);
+                    s_cur[kb][r] = e;
                 }
-                fence();
+            } else {
+                // pack P^T: steps 13, 14, 15 cover chunks 0-1, 2, 3
+#pragma unroll
+                for (int q = (st == 13 ? 0 : st - 12); q <= (st == 13 ? 1 : st - 12); ++q) {
+                    const int kb = q >> 1, c = q & 1;
+                    uint4 u;
+                    u.x = Tr::pack2(s_cur[kb][c * 8 + 0], s_cur[kb][c * 8 + 1]);
+                    u.y = Tr::pack2(s_cur[kb][c * 8 + 2], s_cur[kb][c * 8 + 3]);
+                    u.z = Tr::pack2(s_cur[kb][c * 8 + 4], s_cur[kb][c * 8 + 5]);
+                    u.w = Tr::pack2(s_cur[kb][c * 8 + 6], s_cur[kb][c * 8 + 7]);
+                    pp_pin(u.x);
+                    pp_pin(u.y);
+                    pp_pin(u.z);
+                    pp_pin(u.w);
+                    pb[q] = u;
+                }
             }
         };
-        if (edge)
-            softmax(std::integral_constant<bool, true>{});
-        else
-            softmax(std::integral_constant<bool, false>{});
-        alpha_e = alpha;
+        // One stream of 2 NOP operand reads per iteration, LA ahead of use: the
+        // K operands of block t + 1 (score products), then the V^T operands of
+        // block t (P.V products).  The first reads are covered by the row-max
+        // steps of the softmax, which do not wait for them.
+        uint4 opq[2 * NOP];
+        auto issue = [&](auto it) {
+            constexpr int i = decltype(it)::value;
+            if constexpr (i < NOP)
+                opq[i] = read_k(t + 1, i);
+            else if constexpr (i < 2 * NOP)
+                opq[i] = read_v(t, i - NOP);
+        };
+        static_for<LA>([&](auto it) { issue(it); });
+        fence();
+        static_for<4>([&](auto st) { soft_step(st); });
+        fence();
+        // section 1: score products of block t + 1, softmax steps 4-15 of block t between them
+        static_for<NOP>([&](auto jt) {
+            constexpr int j = decltype(jt)::value;
+            issue(std::integral_constant<int, j + LA>{});
+            fence();
+            // the first product of each chain starts from the constant 0
+            s_next[j & 1] = Tr::mfma32(as_vec8<Tr>(opq[j]), as_vec8<Tr>(qreg[j >> 1]), j < 2 ? f32x16_t{} : s_next[j & 1]);
+            static_for<(12 * (j + 1)) / NOP - (12 * j) / NOP>([&](auto kt) {
+                soft_step(std::integral_constant<int, 4 + (12 * j) / NOP + decltype(kt)::value>{});
+            });
+            fence();
+        });
         // O rescale, only when some lane raised its shift (rare with the lazy max)
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
             // in place, so the accumulators keep their registers on both paths;
-            // their last writer, the final P.V product of the previous X slot,
-            // is more than 64 instructions back
+            // their last writer, the final P.V product of the previous
+            // iteration, is more than 16 matrix instructions back
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) asm volatile("v_mul_f32 %0, %1, %0" : "+v"(acc[db][i]) : "v"(alpha));
         }
+        fence();
+        // section 2: O^T += V^T P^T of block t, row sum between the products
+        {
+            float p8[8];
+            static_for<NOP>([&](auto jt) {
+                constexpr int j = decltype(jt)::value;
+                issue(std::integral_constant<int, NOP + j + LA>{});
+                fence();
+                acc[j % NDB] = Tr::mfma32(as_vec8<Tr>(opq[NOP + j]), as_vec8<Tr>(pb[j / NDB]), acc[j % NDB]);
+                // row-sum items [9 j / NOP, 9 (j + 1) / NOP): 8 partial sums and the update
+                static_for<(9 * (j + 1)) / NOP - (9 * j) / NOP>([&](auto it) {
+                    constexpr int w = (9 * j) / NOP + decltype(it)::value;
+                    if constexpr (w < 8) {
+                        p8[w] = (s_cur[w >> 2][(w & 3) * 4 + 0] + s_cur[w >> 2][(w & 3) * 4 + 1]) +
+                                (s_cur[w >> 2][(w & 3) * 4 + 2] + s_cur[w >> 2][(w & 3) * 4 + 3]);
+                        pp_pin(p8[w]);
+                    } else {
+                        const float tsum = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
+                        l_run = fmaf(l_run, alpha, tsum);
+                        pp_pin(l_run);
+                    }
+                });
+                fence();
+            });
+        }
     };
 
-    // Prologue: blocks 0-2 into the ring, Q^T into registers.
+    // Prologue: blocks 0-2 into the ring, Q^T into registers (issued after the
+    // ring loads so that the two latencies overlap; negated when the scale is
+    // negative, after both have landed), scores of block 0.
     for (int t = 0; t < 3 && t < ntiles; ++t) load_block(t);
+    {
+        const int q_rs = (int)(p.q_sr * 2);
+        const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
+    }
     pp_barrier<0>();
-    if (grp == 1) pp_barrier_lds();
-
-    // X(0)
-    if (last_tile >= 0) slot_x(0, std::integral_constant<bool, false>{});
-    pp_barrier_lds();
-    // Blocks this wave takes part in: Y(t), X(t + 1).  Reads and uses of the
-    // operand arrays are unconditional here, so none stays live across the loop.
-    for (int t = 0; t <= last_tile; ++t) {
-        slot_y(t);
+    if (p.neg) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
+    }
+    if (last_tile >= 0) scores(0, sA);
+    // Blocks this wave takes part in, two per trip so the score buffers swap
+    // roles without copies.  Reads and uses of the operand arrays are
+    // unconditional here, so none stays live across the loop (after the last
+    // block the next scores are computed from a stale stage and unused).
+    auto step = [&](int t, f32x16_t* sc, f32x16_t* sn) {
+        const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0);
+        if (edge) mask_scores(t, sc);
+        iteration(t, sc, sn);
         if (t + 3 < ntiles) load_block(t + 3);
-        barrier_y(t);
-        slot_x(t + 1, std::integral_constant<bool, true>{});  // after the last block: stale scores, unused
-        pp_barrier_lds();
+        barrier_iter(t);
+    };
+    for (int t = 0; t <= last_tile; t += 2) {
+        step(t, sA, sB);
+        if (t + 1 > last_tile) break;
+        step(t + 1, sB, sA);
     }
     // Blocks past this wave's rows: loads and barriers only.
     for (int t = last_tile + 1; t < ntiles; ++t) {
         if (t + 3 < ntiles) load_block(t + 3);
-        barrier_y(t);
-        pp_barrier_lds();
+        barrier_iter(t);
     }
-    if (grp == 0) pp_barrier_lds();
 
     // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
     const float l_tot = pair32_sum(l_run);
