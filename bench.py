@@ -167,8 +167,8 @@ def bench_varlen(steps, warmup, device="cuda"):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workloads", default="all",
                     help="all | main | decode | neox | varlen | fp32 | copy (comma separated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
