@@ -409,8 +409,8 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
             // the eight-wave kernel masks scores with -inf and needs a positive
             // scale for exp2(-inf * scale) = 0; a zero scale stays here
             if (p.scale_log2 > 0.f)
-                return causal ? launch_prefill_pp<Tr, D, true, false>(p, s)
-                              : launch_prefill_pp<Tr, D, false, false>(p, s);
+                return causal ? launch_prefill_pp<Tr, D, true>(p, s)
+                              : launch_prefill_pp<Tr, D, false>(p, s);
             return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, false>(p, s)
                           : launch_prefill_one<Tr, D, false, MASK_NONE, false>(p, s);
         case MASK_FLOAT:

@@ -1,6 +1,7 @@
 // Single-pass attention forward for bf16 / fp16 inputs on gfx950: eight
-// wavefronts per workgroup, each owning 32 query rows, all running the same
-// software-pipelined program over 64-key blocks.
+// wavefronts per workgroup, each owning 32 query rows of a 256-row tile, all
+// running the same software-pipelined program over 64-key blocks; one
+// resident workgroup per compute unit works through a list of tiles.
 //
 // Method: the blocked, online-softmax form of exact attention described on the
 // khchao.com NN Lab page ("FlashAttention Tiling & Online Softmax Algorithm");
@@ -21,7 +22,7 @@
 //   (rare)     O rescale when some lane raised its shift
 //   section 2  O^T += V^T(t) P^T(t) (16 products) with the row sum of block t
 //              between them
-//   end        direct-to-LDS loads of block t + 3, one workgroup barrier
+//   end        direct-to-LDS load of one block into the ring, one barrier
 //
 // Matrix operands are read from LDS six products ahead of their use, in one
 // stream (K of block t + 1, then V of block t).  Scores are transposed (one
@@ -30,9 +31,18 @@
 // work is pinned in place with empty volatile statements: without them the
 // compiler sinks it past the rescale branch into section 2 in one block.
 //
+// Work list.  Workgroup g takes pairs of tiles (the causal tile with the most
+// key blocks and the one with the fewest, so pairs cost alike), pairs g, g + G,
+// ...; its key blocks form one stream over all its tiles, so the ring and the
+// loads run on across tile boundaries, and the next tile's Q^T is loaded into
+// a 64 KB LDS area while the current tile computes.  A tile start then costs
+// its first scores only, not the latency of its first loads.
+//
 // Key and value blocks travel HBM -> LDS by direct-to-LDS buffer loads (no
-// staging registers, no LDS write instructions) into a ring of 4 stages, three
-// blocks ahead: waves 0-3 load K, waves 4-7 load V.  Each lane of a load
+// staging registers, no LDS write instructions) into a ring of 3 stages:
+// waves 0-3 load K blocks three ahead of the compute, waves 4-7 V blocks two
+// ahead, each at the end of a step into the stage read one step earlier (K of
+// block t + 1 is read in step t, V of block t in step t).  Each lane of a load
 // chooses which global 16-byte chunk lands in its LDS slot, so the layouts are
 // free permutations of chunks, picked to make every operand read free of bank
 // conflicts (64 banks; 16-byte reads serviced 16 lanes at a time, 8-byte reads
@@ -46,9 +56,10 @@
 //      is read with ds_read_b64_tr_b16: within 16 lanes, lane i receives
 //      column i of a 4 x 16 block assembled from four lanes' 8-byte reads, so
 //      each lane gets 4 consecutive keys of one head-dimension column.
-// The barrier ending iteration t follows each wave's wait for its loads of
-// block t + 2, so block t + 3 may overwrite the stage of block t - 1, whose
-// last reader (the P.V products of iteration t - 1) is behind that barrier.
+// The barrier ending step t follows each wave's wait for its older loads (K of
+// block t + 2, V of block t + 1: what step t + 1 reads); the load just issued
+// may stay in flight.  The first scores of a tile read its K block 0 in the
+// tile's first step, so there the barrier precedes the load that refills it.
 // Buffer resources turn reads past the last key into zeros; keys past the
 // last key or past the causal diagonal get the score -inf (edge blocks only).
 #pragma once
@@ -150,81 +161,79 @@ __device__ __forceinline__ u32x4_t pp_rsrc(const void* base, int bytes) {
     return r;
 }
 
-template <typename Tr, int D, bool CAUSAL, bool VARLEN>
+// Work of one workgroup: pairs of 256-row query tiles of one (batch, head),
+// the tile with the most key blocks together with the one with the fewest
+// (tiles nq - 1 - i and i), so that every pair costs about the same under the
+// causal mask.  Workgroup g takes pairs g, g + G, g + 2G, ... (G workgroups,
+// at most one per compute unit, all resident at once).  Pair P belongs to
+// (batch, head) P % nbh, so with nbh and G multiples of 8 all tiles of a head
+// run on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share
+// its L2.
+struct PPWork {
+    int nbh;       // batch * heads
+    int nq;        // query tiles per head
+    int n_pairs;   // nbh * ceil(nq / 2)
+};
+
+template <typename Tr, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_pp_kernel(AttnParams p) {
+void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr int BM = kPPBlockM;
     constexpr int BN = 64;
     constexpr int NC = D / 8;          // 16-byte chunks per row
     constexpr int KTILE = BN * D;      // one K or V block, 16-bit words
-    constexpr int NSTAGE = 4;          // ring of K/V stages
+    constexpr int NSTAGE = 3;          // ring of K/V stages
     constexpr int STAGE = 2 * KTILE;   // K block then V block
+    constexpr int QAREA = BM * D;      // Q^T of the next tile, 16-bit words
     constexpr int NKK = D / 16;        // k-steps of the score product
     constexpr int NDB = D / 32;        // 32-row blocks of O^T
     constexpr int NDMA = NC / 4;       // direct-to-LDS loads per wave per block
+    constexpr int NQDMA = NC / 2;      // direct-to-LDS loads per wave per Q tile
     static_assert(D == 64 || D == 96 || D == 128, "head dim must be 64, 96 or 128");
     static_assert(2 * NKK == 4 * NDB, "one K operand read per P.V product");
+    static_assert((NSTAGE * STAGE + QAREA) * 2 <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE + QAREA];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int grp = wave >> 2;     // 0: group A, 1: group B (one slot behind)
+    const int grp = wave >> 2;     // 0: loads K, 1: loads V
     const int wg = wave & 3;
     const int lq = lane & 31;
     const int hh = lane >> 5;
+    const int G = (int)gridDim.x;
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-    const int nbh = p.Hq * p.B;
-    const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);
-    const int bh = (int)(blockIdx.x % nbh);
-    const int h = bh % p.Hq;
-    const int b = bh / p.Hq;
-    const int kvh = h / p.group;
+    // Items of this workgroup: (pair P, half s); s = 0 is the tile with more
+    // key blocks.  A pair whose two tiles coincide (odd nq) has one item.
+    auto pair_qt = [&](int P, int s) {
+        const int pp = P / w.nbh;
+        return s == 0 ? w.nq - 1 - pp : pp;
+    };
+    auto next_item = [&](int& P, int& s) {
+        const int pp = P / w.nbh;
+        if (s == 0 && w.nq - 1 - pp != pp) {
+            s = 1;
+        } else {
+            P += G;
+            s = 0;
+        }
+    };
+    // Key blocks of tile qt (at least one, so that every item takes one step
+    // of the ring; an empty causal range gives a block of zeros and no work).
+    auto kend_of = [&](int qt) { return CAUSAL ? min(p.S, min(qt * BM + BM, p.L)) : p.S; };
+    auto steps_of = [&](int qt) { return max(1, (kend_of(qt) + BN - 1) / BN); };
+    auto head_of = [&](int P, int& b, int& h, int& kvh) {
+        const int bh = P % w.nbh;
+        h = bh % p.Hq;
+        b = bh / p.Hq;
+        kvh = h / p.group;
+    };
 
-    int Lb, Sb;
-    int64_t qo, ko, vo, oo, lo;
-    if (VARLEN) {
-        const int64_t a = min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
-        const int64_t e = min(max((int64_t)p.cu_q[b + 1], a), p.total_q);
-        const int64_t c = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
-        const int64_t d = min(max((int64_t)p.cu_k[b + 1], c), p.total_k);
-        Lb = (int)min(e - a, (int64_t)p.L);
-        Sb = (int)(d - c);
-        qo = a * p.q_sr + (int64_t)h * p.q_sh;
-        ko = c * p.k_sr + (int64_t)kvh * p.k_sh;
-        vo = c * p.v_sr + (int64_t)kvh * p.v_sh;
-        oo = a * p.o_sr + (int64_t)h * p.o_sh;
-        lo = (int64_t)h * p.lse_sh + a;
-    } else {
-        Lb = p.L;
-        Sb = p.S;
-        qo = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-        ko = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-        vo = (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
-        oo = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
-        lo = (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
-    }
-    const int q0 = qt * BM;
-    if (q0 >= Lb) return;  // whole workgroup, before any barrier
-    const int kend = CAUSAL ? min(Sb, min(q0 + BM, Lb)) : Sb;
-    const int ntiles = (kend + BN - 1) / BN;
-    const int qrows = min(BM, Lb - q0);
-    const int wrow0 = wave * 32;
-    const int lrow = wrow0 + lq;
-    const int my_row = q0 + lrow;
-    const bool wave_has_rows = wrow0 < qrows;
-    // last key block this wave takes part in (causal: its last row's block)
-    const int last_tile = !wave_has_rows ? -1
-                          : CAUSAL ? min(ntiles - 1, (q0 + wrow0 + 31) / BN)
-                                   : ntiles - 1;
-
-
-    uint4 qreg[NKK];  // Q^T operand, resident for the whole loop (loaded in the prologue)
-
-    // Direct-to-LDS loads of a block: group A moves K, group B moves V, NDMA
-    // loads of 64 chunks per wave.  g_off[i] is the global byte offset (within
-    // the block) of the chunk this lane places for load i.
+    // Direct-to-LDS loads of a K/V block: waves 0-3 move K, waves 4-7 move V,
+    // NDMA loads of 64 chunks per wave.  g_off[i] is the global byte offset
+    // (within the block) of the chunk this lane places for load i.
     const int k_rs = (int)(p.k_sr * 2);
     const int v_rs = (int)(p.v_sr * 2);
     int g_off[NDMA];
@@ -242,28 +251,71 @@ void prefill_pp_kernel(AttnParams p) {
     }
     const int g_rs = grp == 0 ? k_rs : v_rs;
     const int64_t g_sr = grp == 0 ? p.k_sr : p.v_sr;
-    const uint16_t* g_base = (const uint16_t*)(grp == 0 ? p.k : p.v) + (grp == 0 ? ko : vo);
-    const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-    auto load_block = [&](int t) {
-        const int key0 = t * BN;
-        const int rows = min(BN, Sb - key0);
-        const u32x4_t rs = pp_rsrc(g_base + (int64_t)key0 * g_sr, (rows - 1) * g_rs + D * 2);
-        const uint32_t dst = smem_addr + (uint32_t)(((t % NSTAGE) * STAGE + grp * KTILE) * 2 + wg * NDMA * 1024);
+    const int64_t g_sb = grp == 0 ? p.k_sb : p.v_sb;
+    const int64_t g_sh = grp == 0 ? p.k_sh : p.v_sh;
+    const uint16_t* g_ptr = (const uint16_t*)(grp == 0 ? p.k : p.v);
+
+    // The load cursor of a wave walks the workgroup's key blocks in processing
+    // order (all items, every block of each): waves 0-3 move K blocks three
+    // ahead of the compute, waves 4-7 V blocks two ahead.  Returns whether a
+    // load was issued.
+    // Per-item quantities (head pointer, block count) are set when the cursor
+    // enters an item; a block costs a few scalar instructions.
+    int lP = (int)blockIdx.x, ls = 0, lt = 0, lsteps = 0, lstage = 0;
+    const uint16_t* lptr = g_ptr;  // K or V of the cursor's head, at block lt
+    auto load_enter = [&] {
+        if (lP < w.n_pairs) {
+            int b, h, kvh;
+            head_of(lP, b, h, kvh);
+            lptr = g_ptr + (int64_t)b * g_sb + (int64_t)kvh * g_sh;
+            lsteps = steps_of(pair_qt(lP, ls));
+        }
+    };
+    load_enter();
+    auto load_next = [&] {
+        if (lP >= w.n_pairs) return false;
+        const int rows = min(BN, p.S - lt * BN);
+        const u32x4_t rs = pp_rsrc(lptr, (rows - 1) * g_rs + D * 2);
+        const uint32_t dst = smem_addr + (uint32_t)((lstage * STAGE + grp * KTILE) * 2 + wg * NDMA * 1024);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) pp_dma16(rs, g_off[i], dst + i * 1024);
+        lstage = lstage == NSTAGE - 1 ? 0 : lstage + 1;
+        lptr += (int64_t)BN * g_sr;
+        if (++lt == lsteps) {
+            next_item(lP, ls);
+            lt = 0;
+            load_enter();
+        }
+        return true;
     };
-    // End of iteration t: the loads of block t + 2 (issued in iteration t - 1,
-    // or in the prologue) must have landed; those of block t + 3, issued in
-    // iteration t when it exists, may still be in flight.
-    auto barrier_iter = [&](int t) {
-        if (t + 3 < ntiles)
-            pp_barrier<NDMA>();
-        else
-            pp_barrier<0>();
+
+    // Q^T of a tile: each wave moves its own 32 rows into its own part of the
+    // Q area (chunk layout as for K), so it alone reads them and no barrier
+    // guards the area.
+    const uint32_t q_lds = smem_addr + (uint32_t)((NSTAGE * STAGE + wave * 32 * D) * 2);
+    const int q_rs = (int)(p.q_sr * 2);
+    auto load_q = [&](int P, int s) {
+        int b, h, kvh;
+        head_of(P, b, h, kvh);
+        const int q0 = pair_qt(P, s) * BM;
+        const int rows = min(32, p.L - q0 - wave * 32);
+        const u32x4_t rs = pp_rsrc((const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh +
+                                       (int64_t)(q0 + wave * 32) * p.q_sr,
+                                   (rows - 1) * q_rs + D * 2);
+        // lane index made opaque here, so that the per-lane offsets below are
+        // computed per tile and not kept in registers across the whole loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < NQDMA; ++i) {
+            const int P2 = i * 64 + ln;
+            const int r = (P2 / (16 * NC)) * 16 + P2 % 16, c = (P2 % (16 * NC)) / 16;
+            pp_dma16(rs, r * q_rs + c * 16, q_lds + i * 1024);
+        }
     };
 
     // K operand: LDS row kb*32 + lq, chunk kk*2 + hh -> position
-    // (row/16)*16*NC + chunk*16 + row%16.
+    // (row/16)*16*NC + chunk*16 + row%16.  The Q area uses the same layout.
     const int k_lane = ((lq >> 4) * 16 * NC + hh * 16 + (lq & 15)) * 16;  // bytes
     // V^T operand of chunk ch (keys ch*16 + 8hh + 0..7), rows db*32 + 0..31:
     // two transposing reads of 4 keys each.  Lane i of a 16-lane group reads
@@ -271,21 +323,22 @@ void prefill_pp_kernel(AttnParams p) {
     const int vi = lane & 15;
     const int v_lane = ((hh * 2) * 4 * NC + (2 * ((lane >> 4) & 1) + (vi & 3) / 2) * 4 + vi / 4) * 16 + (vi & 1) * 8;
 
+    uint4 qreg[NKK];  // Q^T operand of the current tile
     f32x16_t acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
-    float sh_run = kNegInf;  // running shift, log2 units (-inf until a kept key)
-    float l_run = 0.f;       // this lane's share of the row sum relative to it
+    float sh_run;     // running shift, log2 units (-inf until a kept key)
+    float l_run;      // this lane's share of the row sum relative to it
     const float cfac = p.scale_log2;
     f32x16_t sA[2], sB[2];   // scores of block t and t + 1, roles swapping each iteration
+    // current item
+    int Sb = p.S, q0 = 0, wrow0 = wave * 32, my_row = 0;
 
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    // V^T operand j = (chunk ch, 32 rows db) of block t: keys ch*16 + 8hh + 0..7,
-    // two transposing reads of 4 keys each.
-    auto read_v = [&](int t, int j) {
+    // V^T operand j = (chunk ch, 32 rows db) of the block in stage st: keys
+    // ch*16 + 8hh + 0..7, two transposing reads of 4 keys each.
+    auto read_v = [&](int st, int j) {
         const int ch = j / NDB, db = j % NDB;
-        const char* Vb = (const char*)(smem + (t % NSTAGE) * STAGE + KTILE) + v_lane;
+        const char* Vb = (const char*)(smem + st * STAGE + KTILE) + v_lane;
         const char* a0 = Vb + ((ch * 4 + 0) * 4 * NC + db * 16) * 16;
         const char* a1 = Vb + ((ch * 4 + 1) * 4 * NC + db * 16) * 16;
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -299,32 +352,29 @@ void prefill_pp_kernel(AttnParams p) {
         u.w = __builtin_bit_cast(uint2, hi4).y;
         return u;
     };
-    auto read_k = [&](int t, int i) {  // K operand i = (kk = i/2, kb = i%2) of block t
-        const char* Kb = (const char*)(smem + (t % NSTAGE) * STAGE) + k_lane;
+    auto read_k = [&](int st, int i) {  // K operand i = (kk = i/2, kb = i%2) of the block in stage st
+        const char* Kb = (const char*)(smem + st * STAGE) + k_lane;
         return *(const uint4*)(Kb + ((i & 1) * 2 * 16 * NC + (i >> 1) * 2 * 16) * 16);
     };
     constexpr int NOP = 2 * NKK;  // products per half (16 at E = 128)
     static_assert(NOP == 4 * NDB, "one K operand read per P.V product");
     constexpr int LA = 6;         // operand reads run this many products ahead
 
-    // S^T = K Q^T of block t into s_out, operands streamed from LDS.
-    auto scores = [&](int t, f32x16_t* s_out) {
+    // S^T = K Q^T of the block in stage st into s_out, operands streamed from LDS.
+    auto scores = [&](int st, f32x16_t* s_out) {
         uint4 kop[NOP];
 #pragma unroll
-        for (int j = 0; j < LA; ++j) kop[j] = read_k(t, j);
+        for (int j = 0; j < LA; ++j) kop[j] = read_k(st, j);
         fence();
 #pragma unroll
         for (int j = 0; j < NOP; ++j) {
-            if (j + LA < NOP) kop[j + LA] = read_k(t, j + LA);
+            if (j + LA < NOP) kop[j + LA] = read_k(st, j + LA);
             fence();
             s_out[j & 1] = Tr::mfma32(as_vec8<Tr>(kop[j]), as_vec8<Tr>(qreg[j >> 1]), j < 2 ? f32x16_t{} : s_out[j & 1]);
             fence();
         }
     };
 
-    // One iteration for block t: the scores of block t + 1 on the matrix core
-    // with the softmax of block t between the products, then O^T += V^T P^T of
-    // block t with its row sum between the products.
     // Scores of keys outside the block's kept range (past the last key, or past
     // the causal diagonal) become -inf in place; their weights then come out
     // as exp2(-inf) = 0 (the scale is positive here).
@@ -341,7 +391,12 @@ void prefill_pp_kernel(AttnParams p) {
                 s_cur[kb][r] = li < lim ? s_cur[kb][r] : kNegInf;
             }
     };
-    auto iteration = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
+
+    // One iteration for block t (its K/V in stage stc, the next block's in stn):
+    // the scores of block t + 1 on the matrix core with the softmax of block t
+    // between the products, then O^T += V^T P^T of block t with its row sum
+    // between the products.
+    auto iteration = [&](int stc, int stn, f32x16_t* s_cur, f32x16_t* s_next) {
         uint4 pb[4];
         float m4[4];
         float alpha = 1.f, shift = 0.f;
@@ -400,9 +455,9 @@ void prefill_pp_kernel(AttnParams p) {
         auto issue = [&](auto it) {
             constexpr int i = decltype(it)::value;
             if constexpr (i < NOP)
-                opq[i] = read_k(t + 1, i);
+                opq[i] = read_k(stn, i);
             else if constexpr (i < 2 * NOP)
-                opq[i] = read_v(t, i - NOP);
+                opq[i] = read_v(stc, i - NOP);
         };
         static_for<LA>([&](auto it) { issue(it); });
         fence();
@@ -457,73 +512,138 @@ void prefill_pp_kernel(AttnParams p) {
         }
     };
 
-    // Prologue: blocks 0-2 into the ring, Q^T into registers (issued after the
-    // ring loads so that the two latencies overlap; negated when the scale is
-    // negative, after both have landed), scores of block 0.
-    for (int t = 0; t < 3 && t < ntiles; ++t) load_block(t);
-    {
-        const int q_rs = (int)(p.q_sr * 2);
-        const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
-    }
+    // Prologue: Q^T of the first item, K blocks 0-2 and V blocks 0-1.
+    int P = (int)blockIdx.x, s = 0;
+    load_q(P, 0);
+    for (int i = 0; i < 3 - grp; ++i) load_next();
     pp_barrier<0>();
-    if (p.neg) {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
-    }
-    if (last_tile >= 0) scores(0, sA);
-    // Blocks this wave takes part in, two per trip so the score buffers swap
-    // roles without copies.  Reads and uses of the operand arrays are
-    // unconditional here, so none stays live across the loop (after the last
-    // block the next scores are computed from a stale stage and unused).
-    auto step = [&](int t, f32x16_t* sc, f32x16_t* sn) {
-        const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0);
-        if (edge) mask_scores(t, sc);
-        iteration(t, sc, sn);
-        if (t + 3 < ntiles) load_block(t + 3);
-        barrier_iter(t);
-    };
-    for (int t = 0; t <= last_tile; t += 2) {
-        step(t, sA, sB);
-        if (t + 1 > last_tile) break;
-        step(t + 1, sB, sA);
-    }
-    // Blocks past this wave's rows: loads and barriers only.
-    for (int t = last_tile + 1; t < ntiles; ++t) {
-        if (t + 3 < ntiles) load_block(t + 3);
-        barrier_iter(t);
-    }
+    int cur = 0;  // ring stage of the current block
+    auto advance = [](int st) { return st == NSTAGE - 1 ? 0 : st + 1; };
 
-    // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
-    const float l_tot = pair32_sum(l_run);
-    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
-    const int o_rs = (int)(p.o_sr * 2);
-    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + D * 2);
+    while (P < w.n_pairs) {
+        int b, h, kvh;
+        head_of(P, b, h, kvh);
+        q0 = pair_qt(P, s) * BM;
+        my_row = q0 + wrow0 + lq;
+        const int ntiles = (kend_of(q0 / BM) + BN - 1) / BN;  // 0 when no key is kept
+        const int nsteps = max(1, ntiles);
+        const int qrows = min(BM, p.L - q0);
+        const bool wave_has_rows = wrow0 < qrows;
+        // last key block this wave takes part in (causal: its last row's block)
+        const int last_tile = !wave_has_rows ? -1
+                              : CAUSAL ? min(ntiles - 1, (q0 + wrow0 + 31) / BN)
+                                       : ntiles - 1;
+        int nP = P, ns = s;
+        next_item(nP, ns);
+        const bool has_next = nP < w.n_pairs;
+
+        // Q^T from this wave's part of the Q area (every barrier so far waited
+        // for all of the wave's loads), negated when the scale is negative.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int kk = 0; kk < NKK; ++kk)
+            qreg[kk] = *(const uint4*)((const char*)smem + (q_lds - smem_addr) + k_lane + kk * 2 * 16 * 16);
+        if (p.neg) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d = db * 32 + g * 8 + hh * 4;
-            uint2 st;
-            st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
-            st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-            buf_store8(st, ors, lrow * o_rs + d * 2);
+            for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
         }
-    if (hh == 0) {
-        const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
-        const auto lrs = make_rsrc(p.lse + lo + q0, qrows * 4);
-        buf_store4(lse, lrs, lrow * 4);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+        sh_run = kNegInf;
+        l_run = 0.f;
+        if (has_next) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): Q area reads done
+            load_q(nP, ns);
+        }
+        scores(cur, sA);  // unconditional, so that no score register stays live across items
+
+        // End of step t: the wave's next block into the ring (a K block three
+        // ahead of the compute goes where the K block read in the previous step
+        // was, a V block two ahead where the V block of the previous step was;
+        // both readers are behind the last barrier), then the wait for the
+        // wave's older loads (the blocks the next step reads, and the next
+        // item's Q^T) and the barrier.  In the first step of an item the K block
+        // of the stage being refilled was also read in this step (the item's
+        // first scores), so the barrier comes first there.
+        auto step_end = [&](int t) {
+            if (t == 0) {
+                pp_barrier<0>();
+                load_next();
+            } else if (load_next()) {
+                pp_barrier<NDMA>();
+            } else {
+                pp_barrier<0>();
+            }
+            cur = advance(cur);
+        };
+        // Blocks this wave takes part in, two per trip so the score buffers swap
+        // roles without copies.  Reads and uses of the operand arrays are
+        // unconditional here, so none stays live across the loop (after the
+        // last block the next scores are computed from whatever the next stage
+        // holds and unused).
+        auto step = [&](int t, f32x16_t* sc, f32x16_t* sn) {
+            const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0);
+            if (edge) mask_scores(t, sc);
+            iteration(cur, advance(cur), sc, sn);
+            step_end(t);
+        };
+        for (int t = 0; t <= last_tile; t += 2) {
+            step(t, sA, sB);
+            if (t + 1 > last_tile) break;
+            step(t + 1, sB, sA);
+        }
+        // Blocks past this wave's rows: loads and barriers only.
+        for (int t = last_tile + 1; t < nsteps; ++t) step_end(t);
+
+        // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
+        const float l_tot = pair32_sum(l_run);
+        const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
+        const int o_rs = (int)(p.o_sr * 2);
+        int lrow = wrow0 + lq;
+        asm volatile("" : "+v"(lrow));  // per-lane store offsets computed here, not kept across the loop
+        const auto ors = make_rsrc((uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)q0 * p.o_sr,
+                                   (qrows - 1) * o_rs + D * 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + hh * 4;
+                uint2 st;
+                st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
+                st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+                buf_store8(st, ors, lrow * o_rs + d * 2);
+            }
+        if (hh == 0) {
+            const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
+            const auto lrs = make_rsrc(p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + q0, qrows * 4);
+            buf_store4(lse, lrs, lrow * 4);
+        }
+        P = nP;
+        s = ns;
     }
 }
 
-template <typename Tr, int D, bool CAUSAL, bool VARLEN>
+// Compute units of the current device (cached per device).
+inline int pp_device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <typename Tr, int D, bool CAUSAL>
 hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
-    AttnParams q = p;
-    q.n_qtiles = (p.L + kPPBlockM - 1) / kPPBlockM;
-    const long long grid = (long long)q.n_qtiles * q.Hq * q.B;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(512), 0, stream, q);
+    PPWork w;
+    w.nbh = p.Hq * p.B;
+    w.nq = (p.L + kPPBlockM - 1) / kPPBlockM;
+    w.n_pairs = w.nbh * ((w.nq + 1) / 2);
+    if (w.n_pairs <= 0) return hipSuccess;
+    const int grid = min(w.n_pairs, pp_device_cus());
+    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
     return hipGetLastError();
 }
 
