@@ -265,3 +265,24 @@ def test_prepared_call_matches_plain_call():
     o, l = S.PreparedSdpaFwd(qd, kd, vd, enable_gqa=True)()
     torch.cuda.synchronize()
     assert torch.equal(o, ref[0].reshape(o.shape)) and torch.equal(l.reshape(ref[1].shape), ref[1])
+
+
+# ------------------------------------------- multi-tile work lists (bf16/fp16)
+
+@pytest.mark.parametrize("dtype,E,causal,L,Sk,B,Hq,Hkv", [
+    ("bf16", 64, True, 700, 700, 3, 120, 40),     # odd tile count per head, GQA, > 1 pair per workgroup
+    ("fp16", 96, False, 520, 333, 2, 150, 150),   # keys shorter than queries, non-causal
+    ("bf16", 128, True, 1300, 1300, 2, 150, 50),  # six tiles per head, 450 pairs over the compute units
+])
+def test_tile_work_lists(dtype, E, causal, L, Sk, B, Hq, Hkv):
+    """Unmasked bf16/fp16 calls run as one resident workgroup per compute unit over
+    lists of query tiles; shapes with more tile pairs than compute units, an odd
+    tile count and GQA.  Parity on sampled (batch, head) slices."""
+    q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), dtype, seed=E + L)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal, enable_gqa=Hq != Hkv)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for b, h in [(0, 0), (0, Hq - 1), (B - 1, Hq // 2), (B - 1, Hq - 1), (B // 2, 7)]:
+        kh = h // g
+        ro, rl = O.sdpa(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1], is_causal=causal)
+        assert_parity(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl, dtype, f"b={b} h={h}")
