@@ -39,10 +39,14 @@ KERNEL_SOURCES = ["prefill_pp.h", "prefill_mfma.h", "device_utils.h", "attn_comm
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank lines removed, so that
+    the stored counter results stay tied to the code, not to its prose."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "transformer_attention_04_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "transformer_attention_04_amd", "csrc", name)) as f:
+            text = re.sub(r"//[^\n]*", "", f.read())
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // shift before the shift is raised.
 constexpr float kLazyRescale = 8.0f;
 
-// End of a slot: this wave's LDS accesses, and all but VM of its direct-to-LDS
+// End of a step: this wave's LDS accesses, and all but VM of its direct-to-LDS
 // loads, have completed; then all 8 waves meet.  The empty asm statements with
 // a memory clobber keep the compiler from moving memory accesses across, the
 // scheduling barriers keep it from moving any instruction across.
@@ -103,14 +103,6 @@ __device__ __forceinline__ void pp_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt(VM) expcnt(7) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void pp_barrier_lds() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
