@@ -178,7 +178,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         return 2
     import torch

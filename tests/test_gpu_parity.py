@@ -1,7 +1,7 @@
 """Parity of the HIP kernels (through the C interface) with the float64 CPU oracle.
 
 Both sides receive the same seeded inputs (the oracle gets an exact float64
-copy of the device bytes).  Bars, as the spec workload states them:
+copy of the device bytes).  Bars:
 max |GPU - oracle| <= 1e-5 for fp32 (output and lse); <= 2e-2 on the output
 and <= 1e-3 on lse for bf16 / fp16.  Rows the oracle calls special (NaN rows,
 rows with no kept key) are compared by class; elements are compared only
