@@ -286,3 +286,71 @@ def test_tile_work_lists(dtype, E, causal, L, Sk, B, Hq, Hkv):
         kh = h // g
         ro, rl = O.sdpa(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1], is_causal=causal)
         assert_parity(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl, dtype, f"b={b} h={h}")
+
+
+# ------------------------------------------------ float masks on the eight-wave kernel
+
+def _float_mask(shape, seed, neg_inf_frac=0.1):
+    g = torch.Generator().manual_seed(seed)
+    m = torch.randn(*shape, generator=g) * 2.0
+    m[torch.rand(shape, generator=g) < neg_inf_frac] = -math.inf
+    return m
+
+
+@pytest.mark.parametrize("dtype,E,causal,L,Sk,B,Hq,Hkv,mshape", [
+    ("bf16", 96, True, 700, 700, 2, 6, 2, "HLS"),     # ragged last tile, GQA, mask shared by the batch
+    ("fp16", 64, False, 520, 332, 2, 3, 3, "BHLS"),   # keys shorter than queries, a full mask
+    ("bf16", 128, True, 300, 300, 1, 4, 4, "LS"),     # one mask for every (batch, head); wave with no rows
+    ("bf16", 96, False, 256, 1000, 2, 2, 2, "B1LS"),  # one tile per head, many key blocks
+    ("fp16", 128, True, 513, 512, 1, 3, 1, "S"),      # one row of bias broadcast to every query row
+])
+def test_float_mask_tile_work_lists(dtype, E, causal, L, Sk, B, Hq, Hkv, mshape):
+    """Float masks with 16-byte-aligned rows run on the resident eight-wave kernel
+    (bias moved into LDS one key block ahead).  Several tiles per head, ragged
+    tails, -inf entries, mask broadcasts; full parity with the oracle."""
+    q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), dtype, seed=E + L + Sk)
+    shape = {"HLS": (Hq, L, Sk), "BHLS": (B, Hq, L, Sk), "LS": (L, Sk), "B1LS": (B, 1, L, Sk),
+             "S": (Sk,)}[mshape]
+    m = _float_mask(shape, seed=L + Sk)
+    assert_parity(*run_both(q, k, v, dtype, attn_mask=m, is_causal=causal, enable_gqa=Hq != Hkv),
+                  dtype, f"float mask {mshape}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_float_mask_scales_and_special_rows(dtype):
+    """Scale 0 and a negative scale (the logit is scale * s + bias, formed in fp32),
+    rows with no kept key (in every block, and only in their first block), and a NaN bias."""
+    E, L, Sk = 96, 300, 388
+    q, k, v = inputs.randn_qkv((1, 2, L, E), (1, 2, Sk, E), (1, 2, Sk, E), dtype, seed=31)
+    m = _float_mask((1, 2, L, Sk), seed=32)
+    m[0, 0, 5, :] = -math.inf          # no kept key at all
+    m[0, 1, 260, :70] = -math.inf      # first key block fully masked for this row
+    m[0, 1, 17, 10] = float("nan")     # NaN logit at a kept key: the row is NaN
+    # (a NaN above the causal diagonal is never read by the kernels, whose causal
+    # tiles skip those keys; the oracle, following the definition, would make the
+    # row NaN there, so the test keeps its NaN below the diagonal)
+    for scale in (None, 0.0, -0.3, 1.0):
+        assert_parity(*run_both(q, k, v, dtype, attn_mask=m, scale=scale), dtype, f"scale={scale}")
+        assert_parity(*run_both(q, k, v, dtype, attn_mask=m, scale=scale, is_causal=True), dtype,
+                      f"causal scale={scale}")
+
+
+def test_float_mask_same_result_on_both_kernels():
+    """A bias whose rows are not 16-byte aligned takes the four-wave kernel; an aligned
+    copy of the same values takes the eight-wave kernel.  Both meet the bar against the
+    oracle, and they agree with each other to within the bf16 output rounding."""
+    E, L, Sk = 128, 400, 400
+    q, k, v = inputs.randn_qkv((1, 2, L, E), (1, 2, Sk, E), (1, 2, Sk, E), "bf16", seed=41)
+    m = _float_mask((2, L, Sk), seed=42)
+    wide = torch.full((2, L, Sk + 1), 7.0)
+    wide[:, :, :Sk] = m
+    unaligned = wide.to(DEV)[:, :, :Sk]   # row stride Sk + 1 on the device: scalar bias loads
+    assert unaligned.stride(1) == Sk + 1
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = S.sdpa_fwd(qd, kd, vd, attn_mask=m.to(DEV), is_causal=True)
+    o2, l2 = S.sdpa_fwd(qd, kd, vd, attn_mask=unaligned, is_causal=True)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa(q, k, v, attn_mask=m, is_causal=True)
+    assert_parity(o1, l1, ro, rl, "bf16", "aligned bias")
+    assert_parity(o2, l2, ro, rl, "bf16", "unaligned bias")
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2

@@ -414,6 +414,10 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
             return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, false>(p, s)
                           : launch_prefill_one<Tr, D, false, MASK_NONE, false>(p, s);
         case MASK_FLOAT:
+            // the eight-wave kernel moves the bias with 16-byte loads
+            if (p.mask_vec)
+                return causal ? launch_prefill_pp<Tr, D, true, MASK_FLOAT>(p, s)
+                              : launch_prefill_pp<Tr, D, false, MASK_FLOAT>(p, s);
             return causal ? launch_prefill_one<Tr, D, true, MASK_FLOAT, false>(p, s)
                           : launch_prefill_one<Tr, D, false, MASK_FLOAT, false>(p, s);
         case MASK_BOOL:

@@ -62,6 +62,19 @@
 // tile's first step, so there the barrier precedes the load that refills it.
 // Buffer resources turn reads past the last key into zeros; keys past the
 // last key or past the causal diagonal get the score -inf (edge blocks only).
+//
+// Float mask (MASK_FLOAT).  The logit is one fp32 FMA, scale * s + bias, and
+// the shift and exponentials then work on logits (factor log2 e instead of
+// scale * log2 e), so any scale works.  Each wave moves the bias of its own 32
+// rows for one key block (8 KB) by direct-to-LDS loads into its own 8 KB of
+// LDS, one block ahead of use: the load is issued right after the wave has
+// read the previous block's bias, and the bias of block t + 1 is read and
+// added to the scores of block t + 1 in section 2 of iteration t (the first
+// block's at the start of its tile).  Each load moves four whole 256-byte
+// rows; chunk c of row r sits at position c ^ (r mod 16) of the row, so the
+// 16-byte reads of 16 rows fall in distinct banks.  The 64 KB this takes
+// come from the Q^T staging area: Q^T is loaded into registers at each tile
+// start instead.  Causal and edge masking are applied after the bias.
 #pragma once
 
 #include "attn_common.h"
@@ -167,25 +180,29 @@ struct PPWork {
     int n_pairs;   // nbh * ceil(nq / 2)
 };
 
-template <typename Tr, int D, bool CAUSAL>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_kernel(AttnParams p, PPWork w) {
+    constexpr bool FMASK = MASK == MASK_FLOAT;
     constexpr int BM = kPPBlockM;
     constexpr int BN = 64;
     constexpr int NC = D / 8;          // 16-byte chunks per row
     constexpr int KTILE = BN * D;      // one K or V block, 16-bit words
     constexpr int NSTAGE = 3;          // ring of K/V stages
     constexpr int STAGE = 2 * KTILE;   // K block then V block
-    constexpr int QAREA = BM * D;      // Q^T of the next tile, 16-bit words
+    constexpr int QAREA = FMASK ? 0 : BM * D;   // Q^T of the next tile, 16-bit words
+    constexpr int BAREA = FMASK ? 8 * 32 * BN * 2 : 0;  // bias of one block per wave (fp32), 16-bit words
     constexpr int NKK = D / 16;        // k-steps of the score product
     constexpr int NDB = D / 32;        // 32-row blocks of O^T
     constexpr int NDMA = NC / 4;       // direct-to-LDS loads per wave per block
     constexpr int NQDMA = NC / 2;      // direct-to-LDS loads per wave per Q tile
+    constexpr int NBDMA = 8;           // direct-to-LDS loads per wave per bias block
     static_assert(D == 64 || D == 96 || D == 128, "head dim must be 64, 96 or 128");
+    static_assert(MASK == MASK_NONE || MASK == MASK_FLOAT, "no boolean masks here");
     static_assert(2 * NKK == 4 * NDB, "one K operand read per P.V product");
-    static_assert((NSTAGE * STAGE + QAREA) * 2 <= 160 * 1024, "LDS budget");
+    static_assert((NSTAGE * STAGE + QAREA + BAREA) * 2 <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE + QAREA];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE + QAREA + BAREA];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -306,6 +323,90 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         }
     };
 
+    // Float mask: a second cursor walks the blocks this wave computes (all
+    // items, block 0 .. last of each; items where the wave has no rows are
+    // skipped) and loads the bias of one block into the wave's 8 KB area.
+    // Load i, lane m: row 4i + m/16 of the wave's 32, chunk (m%16) ^ (row%16)
+    // of the row's 16 chunks of 4 keys; relative to row 16(i/4), the lane's
+    // byte offset depends on i only through i%4.
+    const uint32_t b_lds = smem_addr + (uint32_t)((NSTAGE * STAGE + QAREA) * 2 + wave * 8192);
+    const int m_rs = (int)(p.m_sr * 4);
+    int b_off[4];
+    if constexpr (FMASK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            b_off[i] = row * m_rs + (((lane & 15) ^ (row & 15)) * 16);
+        }
+    }
+    int bP = (int)blockIdx.x, bs = 0, bt = 0, blast = -1;
+    const float* bptr = (const float*)p.mask;  // bias of the cursor's item, first row of this wave
+    int brows = 0;                              // rows of this wave in that item
+    auto bias_enter = [&] {
+        while (bP < w.n_pairs) {
+            int b, h, kvh;
+            head_of(bP, b, h, kvh);
+            const int qt = pair_qt(bP, bs);
+            const int qrows = min(BM, p.L - qt * BM);
+            const int ntl = (kend_of(qt) + BN - 1) / BN;
+            blast = wave * 32 >= qrows ? -1
+                    : CAUSAL ? min(ntl - 1, (qt * BM + wave * 32 + 31) / BN)
+                             : ntl - 1;
+            if (blast >= 0) {
+                brows = min(32, qrows - wave * 32);
+                bptr = (const float*)p.mask + (int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                       (int64_t)(qt * BM + wave * 32) * p.m_sr;
+                return;
+            }
+            next_item(bP, bs);
+        }
+    };
+    // Issues the cursor's block (NBDMA loads) and advances; false when no block
+    // is left.  Rows 0-15 and 16-31 get a buffer resource each, whose base is
+    // their first row at the block's first key and whose size ends at the last
+    // key of the wave's last row, so every byte read is range checked.
+    auto bias_next = [&] {
+        if (bP >= w.n_pairs) return false;
+        const float* base = bptr + bt * BN;
+        const int kbytes = (p.S - bt * BN) * 4;
+        const u32x4_t rs0 = pp_rsrc(base, (brows - 1) * m_rs + kbytes);
+        const u32x4_t rs1 = pp_rsrc((const char*)base + (int64_t)16 * m_rs, (brows - 17) * m_rs + kbytes);
+#pragma unroll
+        for (int i = 0; i < NBDMA; ++i) pp_dma16(i < 4 ? rs0 : rs1, b_off[i & 3], b_lds + i * 1024);
+        if (++bt > blast) {
+            next_item(bP, bs);
+            bt = 0;
+            bias_enter();
+        }
+        return true;
+    };
+    // Bias reads: lane (lq, hh), read i = (kb, c, half) -> keys kb*32 + c*16 +
+    // 8hh + 4half + 0..3 of row lq, i.e. chunk J + 2hh with J = 8kb + 4c + half;
+    // its position (J + 2hh) ^ (lq % 16) = J ^ z is one XOR away from a lane base.
+    // (byte offsets from smem; the area and each row are 256-byte aligned, so
+    // the XOR only touches bits 4-7)
+    int b_rd = 0;
+    if constexpr (FMASK) {
+        const int z = (2 * hh) ^ (lq & 15);
+        b_rd = ((NSTAGE * STAGE + QAREA) * 2 + wave * 8192 + lq * 256) ^ (z * 16);
+    }
+    auto bias_read = [&](int i) {
+        const int J = 8 * (i >> 2) + 4 * ((i >> 1) & 1) + (i & 1);
+        return *(const float4*)((const char*)smem + (b_rd ^ (J * 16)));
+    };
+    // Adds bias read i (4 keys) to the scores: logit = |scale| * s + bias.
+    auto bias_add = [&](f32x16_t* s, int i, float4 bv) {
+        const int kb = i >> 2, r0 = ((i >> 1) & 1) * 8 + (i & 1) * 4;
+        float l[4] = {fmaf(s[kb][r0 + 0], p.scale_abs, bv.x), fmaf(s[kb][r0 + 1], p.scale_abs, bv.y),
+                      fmaf(s[kb][r0 + 2], p.scale_abs, bv.z), fmaf(s[kb][r0 + 3], p.scale_abs, bv.w)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pp_pin(l[r]);
+            s[kb][r0 + r] = l[r];
+        }
+    };
+    bool kv_after_bias = false;  // direct-to-LDS K/V loads were issued after the latest bias load
+
     // K operand: LDS row kb*32 + lq, chunk kk*2 + hh -> position
     // (row/16)*16*NC + chunk*16 + row%16.  The Q area uses the same layout.
     const int k_lane = ((lq >> 4) * 16 * NC + hh * 16 + (lq & 15)) * 16;  // bytes
@@ -319,7 +420,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     f32x16_t acc[NDB];
     float sh_run;     // running shift, log2 units (-inf until a kept key)
     float l_run;      // this lane's share of the row sum relative to it
-    const float cfac = p.scale_log2;
+    const float cfac = FMASK ? kLog2e : p.scale_log2;  // log2-domain factor of a score (or logit)
     f32x16_t sA[2], sB[2];   // scores of block t and t + 1, roles swapping each iteration
     // current item
     int Sb = p.S, q0 = 0, wrow0 = wave * 32, my_row = 0;
@@ -478,9 +579,12 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                 for (int i = 0; i < 16; ++i) asm volatile("v_mul_f32 %0, %1, %0" : "+v"(acc[db][i]) : "v"(alpha));
         }
         fence();
-        // section 2: O^T += V^T P^T of block t, row sum between the products
+        // section 2: O^T += V^T P^T of block t, row sum between the products;
+        // float mask: the bias of block t + 1 added to its scores between the
+        // last NBDMA products (the wait for its load at the first of them)
         {
             float p8[8];
+            float4 bq;
             static_for<NOP>([&](auto jt) {
                 constexpr int j = decltype(jt)::value;
                 issue(std::integral_constant<int, NOP + j + LA>{});
@@ -499,14 +603,38 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                         pp_pin(l_run);
                     }
                 });
+                if constexpr (FMASK) {
+                    constexpr int J0 = NOP - NBDMA;
+                    if constexpr (j == J0) {
+                        // read addresses computed here, not kept in registers across the loop
+                        asm volatile("" : "+v"(b_rd));
+                        // vmcnt only (lgkmcnt left at its maximum: operand reads stay in flight)
+                        if (kv_after_bias)
+                            __builtin_amdgcn_s_waitcnt(0x0F70 | NDMA);
+                        else
+                            __builtin_amdgcn_s_waitcnt(0x0F70);
+                        bq = bias_read(0);
+                    } else if constexpr (j > J0) {
+                        const float4 cv = bq;
+                        bq = bias_read(j - J0);
+                        bias_add(s_next, j - J0 - 1, cv);
+                    }
+                }
                 fence();
             });
+            if constexpr (FMASK) bias_add(s_next, NBDMA - 1, bq);
         }
     };
 
-    // Prologue: Q^T of the first item, K blocks 0-2 and V blocks 0-1.
+    // Prologue: Q^T of the first item (float mask: the bias of the wave's
+    // first block instead), K blocks 0-2 and V blocks 0-1.
     int P = (int)blockIdx.x, s = 0;
-    load_q(P, 0);
+    if constexpr (FMASK) {
+        bias_enter();
+        bias_next();
+    } else {
+        load_q(P, 0);
+    }
     for (int i = 0; i < 3 - grp; ++i) load_next();
     pp_barrier<0>();
     int cur = 0;  // ring stage of the current block
@@ -530,10 +658,21 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         const bool has_next = nP < w.n_pairs;
 
         // Q^T from this wave's part of the Q area (every barrier so far waited
-        // for all of the wave's loads), negated when the scale is negative.
+        // for all of the wave's loads), or (float mask) straight from memory:
+        // lane (lq, hh) holds elements 16kk + 8hh .. +7 of its row.  Negated
+        // when the scale is negative.
+        if constexpr (FMASK) {
+            const int q_rows = max(0, min(32, qrows - wrow0));
+            const auto qrs = make_rsrc((const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh +
+                                           (int64_t)(q0 + wrow0) * p.q_sr,
+                                       (q_rows - 1) * q_rs + D * 2);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            qreg[kk] = *(const uint4*)((const char*)smem + (q_lds - smem_addr) + k_lane + kk * 2 * 16 * 16);
+            for (int kk = 0; kk < NKK; ++kk) qreg[kk] = buf_load16(qrs, lq * q_rs + (kk * 16 + hh * 8) * 2);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                qreg[kk] = *(const uint4*)((const char*)smem + (q_lds - smem_addr) + k_lane + kk * 2 * 16 * 16);
+        }
         if (p.neg) {
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) qreg[kk] = negate8(qreg[kk]);
@@ -542,11 +681,26 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
         sh_run = kNegInf;
         l_run = 0.f;
-        if (has_next) {
+        if (!FMASK && has_next) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): Q area reads done
             load_q(nP, ns);
         }
         scores(cur, sA);  // unconditional, so that no score register stays live across items
+        if (FMASK && last_tile >= 0) {
+            // the bias of block 0 (loaded after this wave's last bias read), then
+            // the next block's load into the area just read
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
+            float4 bv = bias_read(0);
+#pragma unroll
+            for (int i = 0; i < NBDMA; ++i) {
+                const float4 cv = bv;
+                if (i + 1 < NBDMA) bv = bias_read(i + 1);
+                bias_add(sA, i, cv);
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): bias reads done
+            bias_next();
+            kv_after_bias = false;
+        }
 
         // End of step t: the wave's next block into the ring (a K block three
         // ahead of the compute goes where the K block read in the previous step
@@ -556,14 +710,31 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // item's Q^T) and the barrier.  In the first step of an item the K block
         // of the stage being refilled was also read in this step (the item's
         // first scores), so the barrier comes first there.
-        auto step_end = [&](int t) {
+        // Float mask: a step that read a bias block (the next block is one this
+        // wave computes) first issues the cursor's next bias block, before the
+        // K/V load, so that section 2 of the next iteration waits for it with
+        // the K/V load still in flight.
+        auto step_end = [&](int t, bool bias_read_here) {
+            const bool bl = FMASK && bias_read_here;
             if (t == 0) {
                 pp_barrier<0>();
-                load_next();
-            } else if (load_next()) {
-                pp_barrier<NDMA>();
+                const bool bi = bl && bias_next();
+                const bool kv = load_next();
+                if (bi) kv_after_bias = kv;
             } else {
-                pp_barrier<0>();
+                const bool bi = bl && bias_next();
+                const bool kv = load_next();
+                if (bi) {
+                    kv_after_bias = kv;
+                    if (kv)
+                        pp_barrier<NDMA + NBDMA>();
+                    else
+                        pp_barrier<NBDMA>();
+                } else if (kv) {
+                    pp_barrier<NDMA>();
+                } else {
+                    pp_barrier<0>();
+                }
             }
             cur = advance(cur);
         };
@@ -576,7 +747,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0);
             if (edge) mask_scores(t, sc);
             iteration(cur, advance(cur), sc, sn);
-            step_end(t);
+            step_end(t, t + 1 <= last_tile);
         };
         for (int t = 0; t <= last_tile; t += 2) {
             step(t, sA, sB);
@@ -584,7 +755,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             step(t + 1, sB, sA);
         }
         // Blocks past this wave's rows: loads and barriers only.
-        for (int t = last_tile + 1; t < nsteps; ++t) step_end(t);
+        for (int t = last_tile + 1; t < nsteps; ++t) step_end(t, false);
 
         // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
         const float l_tot = pair32_sum(l_run);
@@ -627,7 +798,7 @@ inline int pp_device_cus() {
     return cache[dev];
 }
 
-template <typename Tr, int D, bool CAUSAL>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
 hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     PPWork w;
     w.nbh = p.Hq * p.B;
@@ -635,7 +806,7 @@ hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     w.n_pairs = w.nbh * ((w.nq + 1) / 2);
     if (w.n_pairs <= 0) return hipSuccess;
     const int grid = min(w.n_pairs, pp_device_cus());
-    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
+    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, MASK>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
     return hipGetLastError();
 }
 

@@ -308,8 +308,9 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
         p.m_sr = attn_mask->size[2] > 1 ? attn_mask->stride[2] : 0;
         const int64_t mvec = mask_dtype == SDPA_F32 ? 4 : 8;  // elements per vector load
         const int64_t mal = mask_dtype == SDPA_F32 ? 16 : 8;  // its alignment in bytes
+        // vector loads also need whole vectors at the end of each row
         p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 &&
-                     p.m_sh % mvec == 0 && p.m_sr % mvec == 0;
+                     p.m_sh % mvec == 0 && p.m_sr % mvec == 0 && s.S % mvec == 0;
     }
     p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
     p.L = (int)s.L; p.S = (int)s.S;
