@@ -1,4 +1,4 @@
-"""CPU oracle for exact scaled dot-product attention (forward), in float64.
+"""CPU oracle for exact scaled dot-product attention (forward and backward), in float64.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The HIP
@@ -49,7 +49,7 @@ import numpy as np
 
 __all__ = [
     "resolve_scale", "bias_from_mask", "causal_bias", "logits", "weights",
-    "sdpa", "block_diagonal_bias", "sdpa_varlen", "entropy",
+    "sdpa", "sdpa_backward", "block_diagonal_bias", "sdpa_varlen", "entropy",
 ]
 
 
@@ -189,6 +189,59 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scal
     lse = np.where(inf_row, np.inf, lse)
     lse = np.where(nan_row, np.nan, lse)
     return out, lse
+
+
+def _fold_copies(g, shape, enable_gqa):
+    """Sum a gradient over the copies that grouped-query expansion and broadcasting
+    made of an input of ``shape`` (Backward: "each summed over the copies")."""
+    if enable_gqa and g.ndim >= 3 and len(shape) >= 3 and g.shape[-3] != shape[-3] and shape[-3] > 0:
+        rep = g.shape[-3] // shape[-3]
+        g = g.reshape(g.shape[:-3] + (shape[-3], rep) + g.shape[-2:]).sum(axis=-3)
+    while g.ndim > len(shape):
+        g = g.sum(axis=0)
+    for ax, (n, m) in enumerate(zip(g.shape, shape)):
+        if m == 1 and n != 1:
+            g = g.sum(axis=ax, keepdims=True)
+    return g
+
+
+def sdpa_backward(query, key, value, grad, attn_mask=None, dropout_p=0.0, is_causal=False,
+                  scale=None, enable_gqa=False):
+    """Gradients (grad_query, grad_key, grad_value) of exact attention, float64.
+
+    exactref.ai ``scaled_dot_product_attention.backward``: with P the attention
+    weights (materialised as in the forward), dP = grad V^T, D_i = sum_j P_ij dP_ij,
+    dS = P * (dP - D); grad_value = P^T grad, grad_query = scale * dS K,
+    grad_key = scale * dS^T Q, each summed over the copies that grouped-query
+    expansion made of its input.  Non-finite values propagate as IEEE arithmetic
+    does: a NaN row of the forward makes every gradient it touches NaN, and a row
+    with no kept key has P = 0 and contributes 0.  A float mask gets no gradient.
+    """
+    if dropout_p != 0:
+        raise ValueError("dropout_p must be 0: a random dropout has no exact reference")
+    q, k, v, g = _f64(query), _f64(key), _f64(value), _f64(grad)
+    if k.shape[-1] != q.shape[-1]:
+        raise ValueError("query and key must share the last dimension E")
+    if k.shape[-2] != v.shape[-2]:
+        raise ValueError("key and value must share the sequence length S")
+    if not enable_gqa and q.ndim >= 3 and k.ndim >= 3 and q.shape[-3] != k.shape[-3] \
+            and k.shape[-3] != 1 and q.shape[-3] != 1:
+        raise ValueError("query and key heads differ: pass enable_gqa=True")
+    p = weights(q, k, attn_mask, is_causal, scale, enable_gqa)
+    kk, vv = _expand_kv(q, k, v, enable_gqa)
+    E = q.shape[-1]
+    sc = resolve_scale(E, scale) if E > 0 else 0.0  # with E = 0, grad_query and grad_key are empty
+    with np.errstate(invalid="ignore", over="ignore"):
+        dp = np.matmul(g, np.swapaxes(vv, -1, -2))
+        d = (p * dp).sum(axis=-1, keepdims=True)
+        ds = p * (dp - d)
+        gv = np.matmul(np.swapaxes(p, -1, -2), g)
+        gq = sc * np.matmul(ds, kk)
+        gk = sc * np.matmul(np.swapaxes(ds, -1, -2), q)
+    gq = _fold_copies(gq, q.shape, False)
+    gk = _fold_copies(gk, k.shape, enable_gqa)
+    gv = _fold_copies(gv, v.shape, enable_gqa)
+    return gq, gk, gv
 
 
 def block_diagonal_bias(lengths_q, lengths_k=None, causal=False):
