@@ -8,8 +8,9 @@ headline configuration).  The JSON line reports its attention TFLOP/s with
 the matrix-core roofline of the prefill kernel, the CPU oracle timed on the
 host cores on a bounded sample of the same workload, and (under "secondary")
 the other workloads: split-KV GQA decode in GB/s against the HBM roofline,
-the GPT-NeoX-shaped E=96 variants, packed variable-length fp16 and the
-single-head fp32 case.
+the GPT-NeoX-shaped E=96 variants, packed variable-length fp16, the
+single-head fp32 case and the backward of the headline workload (5 products
+per kept pair: 10 E flops).
 
 Algorithmic work (what the method must do, not what a kernel happens to do):
 flops = (2E + 2Ev) x kept (query, key) pairs; bytes = Q + K + V + O + lse
@@ -168,13 +169,34 @@ def bench_varlen(steps, warmup, device="cuda"):
             "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12, "total_tokens": sum(lengths)}
 
 
+def bench_backward(steps, warmup, device="cuda"):
+    """Gradients of the headline workload (sdpa_bwd: the D = dO . O pass, the dQ
+    kernel and the dK/dV kernel) for an N(0,1) output gradient (seed 99)."""
+    import torch
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    w = inputs.WORKLOADS["bf16_causal_e128"]
+    q, k, v = (t.to(device) for t in inputs.workload_inputs("bf16_causal_e128"))
+    g = inputs.randn_qkv(tuple(q.shape), (1, 1, 1, w["E"]), (1, 1, 1, w["E"]), "bf16", seed=99)[0].to(device)
+    out, lse = S.sdpa_fwd(q, k, v, is_causal=True)
+    ws = torch.empty(S.sdpa_bwd_workspace_size(q, k, v), dtype=torch.uint8, device=device)
+    fn = lambda: S.sdpa_bwd(q, k, v, out, lse, g, is_causal=True, workspace=ws)
+    wall, per = time_launches(fn, steps, warmup)
+    pairs = w["L"] * (w["L"] + 1) // 2
+    # five products per kept pair: S, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q
+    flops = 10 * w["E"] * pairs * w["B"] * w["Hq"]
+    kern_ms = sum(per) / len(per)
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "flops": flops,
+            "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | decode | neox | varlen | fp32 | copy (comma separated)")
+                    help="all | main | decode | neox | varlen | fp32 | bwd | copy (comma separated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -229,6 +251,16 @@ def main(argv=None):
         r = bench_prefill("fp32_single_head", max(5, a.steps // 2), min(a.warmup, 5))
         secondary["fp32_single_head"] = {"metric": "us per call", "value": round(r["kernel_ms"] * 1e3, 2),
                                          "tflops": round(r["kernel_tflops"], 3)}
+
+    if run_all or "bwd" in sel:
+        r = bench_backward(max(5, a.steps // 4), min(a.warmup, 5))
+        secondary["bf16_causal_e128 backward"] = {
+            "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+            "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "call_us": round(r["kernel_ms"] * 1e3, 1), "flop_per_call": r["flops"],
+            "kernels": "bwd_dot_kernel + bwd_dq_kernel + bwd_dkdv_kernel"}
+        print(f"# bf16_causal_e128 backward: {r['kernel_ms'] * 1e3:.1f} us/call, "
+              f"{r['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     if "copy" in sel:
         # calibration for the HBM byte counters: a plain device copy of a known size

@@ -154,6 +154,51 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
                             float* lse, int64_t lse_stride_head,
                             void* stream);
 
+/*
+ * sdpa_bwd -- gradients of batched attention (exactref.ai
+ * "scaled_dot_product_attention.backward").  With P the attention weights of
+ * the forward, dP = dout V^T, D_i = sum_j P_ij dP_ij and dS = P * (dP - D):
+ *
+ *     dv = P^T dout,   dq = scale * dS K,   dk = scale * dS^T Q,
+ *
+ * dk and dv summed over the query heads that share a key/value head.  P is
+ * recomputed from q, k and the forward's lse; D from the forward output
+ * (D_i = dout_i . out_i, the definition's sum up to the rounding of out).
+ *
+ *   dtype      SDPA_BF16 or SDPA_F16 (SDPA_F32 returns SDPA_ERR_UNSUPPORTED).
+ *   q, k, v    as for sdpa_fwd; E == Ev in {64, 96, 128}.
+ *   out, lse   the results of sdpa_fwd for the same q, k, v, is_causal,
+ *              scale and enable_gqa (no mask): out (B, Hq, L, Ev) dtype,
+ *              lse (B, Hq, L, 1) float32.
+ *   dout       (B, Hq, L, Ev), dtype: gradient of the loss with respect to out.
+ *   is_causal, scale, enable_gqa   as for sdpa_fwd.  There is no mask argument.
+ *   dq         (B, Hq, L, E), dk (B, Hkv, S, E), dv (B, Hkv, S, Ev), dtype;
+ *              written completely (rows no query reaches get 0), rounded to
+ *              nearest-even.  They must not alias any input.
+ *   workspace, workspace_bytes
+ *              device scratch of at least sdpa_bwd_workspace_size() bytes,
+ *              owned by the caller (the per-row D in float32).
+ *   stream     hipStream_t or NULL; the call is asynchronous on it.
+ *
+ * Errors as for sdpa_fwd: argument problems are found on the host before any
+ * launch; every tensor needs unit last stride, a 16-byte aligned base and
+ * strides that are multiples of 16 bytes (else SDPA_ERR_UNSUPPORTED).
+ */
+sdpa_status sdpa_bwd(sdpa_dtype dtype,
+                     const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* out, const sdpa_tensor4* lse, const sdpa_tensor4* dout,
+                     int is_causal, const double* scale, int enable_gqa,
+                     const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_bwd_workspace_size -- bytes of workspace sdpa_bwd needs for these
+ * shapes (B * Hq * L float32 values, plus alignment).  Host only.
+ */
+sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype,
+                                    const sdpa_tensor4* q, const sdpa_tensor4* k,
+                                    const sdpa_tensor4* v, int enable_gqa, size_t* bytes);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);
 

@@ -1,9 +1,10 @@
 // Shared declarations of the attention kernels and their host launchers.
 //
-// Internal to libsdpa: the public interface is include/sdpa.h.  Every kernel
-// computes the forward pass of exact attention as the exactref.ai
+// Internal to libsdpa: the public interface is include/sdpa.h.  The forward
+// kernels compute exact attention as the exactref.ai
 // "scaled_dot_product_attention" page specifies it (section "Full
-// specification"): softmax(scale * Q K^T + mask) V plus the per-row logsumexp.
+// specification"): softmax(scale * Q K^T + mask) V plus the per-row logsumexp;
+// the backward kernels its gradients (section "backward").
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,6 +68,35 @@ struct DecodeParams {
     float scale_log2;   // |scale| * log2(e)
 };
 
+// One call of the backward kernels (bf16 / fp16).  dsum is the float32
+// workspace of the per-row D = dO . O, laid out (b, h, i) contiguously.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* dsum;
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int64_t o_sb, o_sh, o_sr;
+    int64_t do_sb, do_sh, do_sr;
+    int64_t dq_sb, dq_sh, dq_sr;
+    int64_t dk_sb, dk_sh, dk_sr;
+    int64_t dv_sb, dv_sh, dv_sr;
+    int64_t lse_sb, lse_sh;
+    int B, Hq, Hkv, group, L, S;
+    int n_qtiles;   // 128-row query tiles
+    int n_ktiles;   // 128-key tiles
+    int elem;       // ELEM_BF16 or ELEM_F16
+    float scale;    // signed
+};
+
 hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                                hipStream_t stream);
 hipError_t launch_prefill_f16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
@@ -74,6 +104,7 @@ hipError_t launch_prefill_f16(const AttnParams& p, int D, bool causal, int mask,
 hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int elem, int D, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, hipStream_t stream);
 
 // Tile sizes the host needs for grids and workspace.
 constexpr int kPrefillBlockM = 128;  // query rows per MFMA workgroup

@@ -1,0 +1,496 @@
+// Gradients of exact attention for bf16 / fp16 inputs on gfx950 (CDNA4).
+//
+// What is computed: the exactref.ai "scaled_dot_product_attention.backward"
+// section.  With P the attention weights, dP = dO V^T, D_i = sum_j P_ij dP_ij
+// and dS = P * (dP - D):  dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q,
+// dK and dV summed over the query heads that share a key/value head.  P is
+// recomputed from the scores and the forward's logsumexp (P_ij = exp(l_ij -
+// lse_i)), and D_i from the forward output (D_i = dO_i . O_i, equal to the
+// definition's sum up to the rounding of O), as the blocked algorithm on the
+// khchao.com NN Lab page keeps only O(N) state per row.
+//
+// Three kernels:
+//   bwd_dot_kernel    D_i = dO_i . O_i in fp32 (HBM-bound, one pass).
+//   bwd_dq_kernel     one workgroup per 128 query rows (4 wavefronts x 32):
+//                     for each 64-key block, S^T = K Q^T and dP^T = V dO^T on
+//                     the matrix cores (the transposed score layout of the
+//                     forward kernels, one query per lane), P^T and dS^T in
+//                     registers, then dQ^T += K^T dS^T with dS^T as the B
+//                     operand straight from the score registers and K^T read
+//                     from LDS with the transposing ds_read_b64_tr_b16.
+//   bwd_dkdv_kernel   one workgroup per 128 keys (4 wavefronts x 32), over the
+//                     query heads of the key/value head and their 64-row query
+//                     blocks: S = Q K^T and dP = dO V^T (one key per lane),
+//                     then dV^T += dO^T P and dK^T += Q^T dS with P and dS as
+//                     B operands from the score registers and dO^T, Q^T read
+//                     transposed from LDS.
+// No atomics: each gradient element has one owner.  The price is that S and
+// dP are computed twice (once per owner), 7 matrix products per kept
+// (query, key) pair and head dimension instead of the 5 of one shared pass.
+//
+// LDS tiles are row-major with 8 elements of padding per row (16-byte row
+// reads conflict-free).  Rows are stored at position swap23(r) within each
+// 32-row group (bits 2 and 3 of the row index swapped): then register r of
+// lane l of a 32x32 product tile holds row 16(r/8) + 8(l/32) + r%8 of its
+// group, which is exactly the k-slot order of a B operand, and each group of
+// 4 consecutive natural rows stays at 4 consecutive positions, as the
+// transposing reads need.
+#include "attn_common.h"
+#include "device_utils.h"
+
+namespace sdpa {
+
+namespace {
+
+__device__ __forceinline__ int bwd_swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ int bwd_pos(int r) { return (r & ~31) | bwd_swap23(r & 31); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// A operand X^T (32 columns of X as rows, 16 rows of X as k-slots) of one
+// 16-row chunk c of a row-major tile X[pos][RS] (16-bit words): lane l gets
+// column col0 + (l & 31) and natural rows 16c + 8(l/32) + 0..7, in two
+// transposing reads of 4 rows each.
+template <int RS>
+__device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int c, int col0, int lane) {
+    const int i = lane & 15, g = (lane >> 4) & 1, hh = lane >> 5;
+    const int col = col0 + 16 * g + 4 * (i & 3);
+    const uint16_t* a0 = tile + (16 * c + 4 * hh + (i >> 2)) * RS + col;
+    const uint16_t* a1 = tile + (16 * c + 8 + 4 * hh + (i >> 2)) * RS + col;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(uint32_t)(uintptr_t)a0);
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(uint32_t)(uintptr_t)a1);
+    uint4 u;
+    u.x = __builtin_bit_cast(uint2, lo).x;
+    u.y = __builtin_bit_cast(uint2, lo).y;
+    u.z = __builtin_bit_cast(uint2, hi).x;
+    u.w = __builtin_bit_cast(uint2, hi).y;
+    return u;
+}
+
+// ------------------------------------------------------------- D = dO . O
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
+    // 16 lanes per row, 16 rows per workgroup; row index over (b, h, i)
+    const int tid = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * 16 + tid / 16;
+    const int c = tid & 15;
+    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
+    float acc = 0.f;
+    if (row < nrows && c < D / 8) {
+        const int i = (int)(row % p.L);
+        const int64_t bh = row / p.L;
+        const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+        const uint4 o = *(const uint4*)((const uint16_t*)p.o + b * p.o_sb + h * p.o_sh + i * p.o_sr + c * 8);
+        const uint4 g = *(const uint4*)((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + i * p.do_sr + c * 8);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float o0, o1, g0, g1;
+            if (p.elem == ELEM_BF16) {
+                o0 = BF16::to_f32(ow[j] & 0xffff); o1 = BF16::to_f32(ow[j] >> 16);
+                g0 = BF16::to_f32(gw[j] & 0xffff); g1 = BF16::to_f32(gw[j] >> 16);
+            } else {
+                o0 = F16::to_f32(ow[j] & 0xffff); o1 = F16::to_f32(ow[j] >> 16);
+                g0 = F16::to_f32(gw[j] & 0xffff); g1 = F16::to_f32(gw[j] >> 16);
+            }
+            acc = fmaf(o0, g0, acc);
+            acc = fmaf(o1, g1, acc);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) acc += xor_lane(acc, m);
+    if (row < nrows && c == 0) p.dsum[row] = acc;
+}
+
+// ------------------------------------------------------------------- dQ
+
+template <typename Tr, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+    constexpr int BM = 128, BN = 64;
+    constexpr int RS = D + 8;            // LDS row stride, 16-bit words
+    constexpr int TILE = BN * RS;        // one K or V block
+    constexpr int STAGE = 2 * TILE;
+    constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr int NCH = BN * D / 8;      // 16-byte chunks per block
+    constexpr int NCH_T = NCH / 256;     // per thread
+    static_assert(NCH % 256 == 0, "chunks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hh = lane >> 5;
+    const int nbh = p.Hq * p.B;
+    const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest (causal) first
+    const int bh = (int)(blockIdx.x % nbh);
+    const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.group;
+    const int q0 = qt * BM;
+    if (q0 >= p.L) return;
+    const int qrows = min(BM, p.L - q0);
+    const int wrow0 = wave * 32;
+    const int my_row = q0 + wrow0 + lq;
+    const bool wave_has_rows = wrow0 < qrows;
+    const int kend = CAUSAL ? min(p.S, q0 + BM) : p.S;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    // Q^T and dO^T operands (lane: query lq, elements 16kk + 8hh .. +7)
+    const int q_rs = (int)(p.q_sr * 2), do_rs = (int)(p.do_sr * 2);
+    const auto qrs = make_rsrc((const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)q0 * p.q_sr,
+                               (qrows - 1) * q_rs + D * 2);
+    const auto gdrs = make_rsrc((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)q0 * p.do_sr,
+                                (qrows - 1) * do_rs + D * 2);
+    const int lrow = wrow0 + lq;
+    uint4 qreg[NKK], dreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
+        dreg[kk] = buf_load16(gdrs, lrow * do_rs + (kk * 16 + hh * 8) * 2);
+    }
+    const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
+    const bool row_ok = my_row < p.L;
+    const float lse2 = row_ok ? p.lse[b * p.lse_sb + h * p.lse_sh + my_row] * kLog2e : 0.f;
+    const float drow = row_ok ? p.dsum[rowid + my_row] : 0.f;
+    const float c2 = p.scale * kLog2e;  // signed
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+
+    const uint16_t* kbase = (const uint16_t*)p.k + b * p.k_sb + kvh * p.k_sh;
+    const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + kvh * p.v_sh;
+    const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
+    uint4 kbuf[NCH_T], vbuf[NCH_T];
+    auto load_tile = [&](int key0) {
+        const int rows = min(BN, p.S - key0);
+        const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
+        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + D * 2);
+#pragma unroll
+        for (int i = 0; i < NCH_T; ++i) {
+            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            kbuf[i] = buf_load16(kr, r * k_rs + col * 2);
+            vbuf[i] = buf_load16(vr, r * v_rs + col * 2);
+        }
+    };
+    auto store_tile = [&](int stage) {
+        uint16_t* Ks = smem + stage * STAGE;
+        uint16_t* Vs = Ks + TILE;
+#pragma unroll
+        for (int i = 0; i < NCH_T; ++i) {
+            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            *(uint4*)(Ks + bwd_pos(r) * RS + col) = kbuf[i];
+            *(uint4*)(Vs + bwd_pos(r) * RS + col) = vbuf[i];
+        }
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int key0 = t * BN;
+        if (t + 1 < ntiles) load_tile(key0 + BN);
+        const uint16_t* Ks = smem + (t & 1) * STAGE;
+        const uint16_t* Vs = Ks + TILE;
+        const bool active = wave_has_rows && (!CAUSAL || key0 <= q0 + wrow0 + 31);
+        if (active) {
+            f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint4 ka = *(const uint4*)(Ks + (kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    const uint4 va = *(const uint4*)(Vs + (kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    s[kb] = Tr::mfma32(as_vec8<Tr>(ka), as_vec8<Tr>(qreg[kk]), s[kb]);
+                    dp[kb] = Tr::mfma32(as_vec8<Tr>(va), as_vec8<Tr>(dreg[kk]), dp[kb]);
+                }
+            // register r of block kb: key key0 + 32kb + 16(r/8) + 8hh + r%8, query my_row
+            const bool edge = (key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
+            int lim = p.S - (key0 + hh * 8);
+            if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
+            uint4 pb[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float ds[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pv = fast_exp2(fmaf(s[kb][r], c2, -lse2));
+                    if (edge) pv = (kb * 32 + (r >> 3) * 16 + (r & 7) < lim) ? pv : 0.f;
+                    ds[r] = pv * (dp[kb][r] - drow);
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    pb[kb * 2 + c].x = Tr::pack2(ds[c * 8 + 0], ds[c * 8 + 1]);
+                    pb[kb * 2 + c].y = Tr::pack2(ds[c * 8 + 2], ds[c * 8 + 3]);
+                    pb[kb * 2 + c].z = Tr::pack2(ds[c * 8 + 4], ds[c * 8 + 5]);
+                    pb[kb * 2 + c].w = Tr::pack2(ds[c * 8 + 6], ds[c * 8 + 7]);
+                }
+            }
+            // dQ^T (rows e, columns queries) += K^T dS^T over the block's 4 key chunks
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const uint4 a = read_tr<RS>(Ks, c, db * 32, lane);
+                    acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb[c]), acc[db]);
+                }
+        }
+        // the other stage was last read a step ago, before the last barrier
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // dQ = scale * dQ^T, rounded to nearest-even; lane: query lrow, e = 32db + 8g + 4hh + 0..3
+    const int dq_rs = (int)(p.dq_sr * 2);
+    const auto ors = make_rsrc((uint16_t*)p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)q0 * p.dq_sr,
+                               (qrows - 1) * dq_rs + D * 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + hh * 4;
+            uint2 st;
+            st.x = Tr::pack2(acc[db][4 * g + 0] * p.scale, acc[db][4 * g + 1] * p.scale);
+            st.y = Tr::pack2(acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+            buf_store8(st, ors, lrow * dq_rs + d * 2);
+        }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <typename Tr, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+    constexpr int BK = 128, BN = 64;     // keys per workgroup, queries per step
+    constexpr int RS = D + 8;
+    constexpr int TILE = BN * RS;
+    constexpr int STAGE = 2 * TILE + 2 * BN * 2;  // Q, dO, then lse*log2e and D (fp32, natural order)
+    constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr int NCH = BN * D / 8;
+    constexpr int NCH_T = NCH / 256;
+    static_assert(NCH % 256 == 0, "chunks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hh = lane >> 5;
+    const int nbh = p.Hkv * p.B;
+    const int kt = (int)(blockIdx.x / nbh);   // lowest key tiles (most causal work) first
+    const int bkv = (int)(blockIdx.x % nbh);
+    const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
+    const int k0 = kt * BK;
+    if (k0 >= p.S) return;
+    const int krows = min(BK, p.S - k0);
+    const int wkey0 = k0 + wave * 32;          // first key of this wavefront
+    const int my_key = wkey0 + lq;
+    const bool wave_has_keys = wave * 32 < krows;
+
+    // K^T and V^T operands (lane: key lq, elements 16kk + 8hh .. +7)
+    const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
+    const auto krs = make_rsrc((const uint16_t*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)k0 * p.k_sr,
+                               (krows - 1) * k_rs + D * 2);
+    const auto vrs = make_rsrc((const uint16_t*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)k0 * p.v_sr,
+                               (krows - 1) * v_rs + D * 2);
+    const int lkey = wave * 32 + lq;
+    uint4 kreg[NKK], vreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        kreg[kk] = buf_load16(krs, lkey * k_rs + (kk * 16 + hh * 8) * 2);
+        vreg[kk] = buf_load16(vrs, lkey * v_rs + (kk * 16 + hh * 8) * 2);
+    }
+    const float c2 = p.scale * kLog2e;
+
+    f32x16_t dv[NDB], dk[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dv[db] = f32x16_t{};
+        dk[db] = f32x16_t{};
+    }
+
+    // query blocks this workgroup visits: causal keeps query i >= key j
+    const int qb0 = CAUSAL ? k0 / BN : 0;
+    const int nqb = (p.L + BN - 1) / BN;
+    const int nsteps = p.group * max(0, nqb - qb0);  // (query head, query block) pairs
+
+    const int q_rs = (int)(p.q_sr * 2), do_rs = (int)(p.do_sr * 2);
+    uint4 qbuf[NCH_T], gbuf[NCH_T];
+    float lbuf = 0.f, dbuf = 0.f;
+    auto step_coords = [&](int st, int& h, int& qrow0) {
+        h = kvh * p.group + st / max(1, nqb - qb0);
+        qrow0 = (qb0 + st % max(1, nqb - qb0)) * BN;
+    };
+    auto load_tile = [&](int st) {
+        int h, qrow0;
+        step_coords(st, h, qrow0);
+        const int rows = min(BN, p.L - qrow0);
+        const auto qr = make_rsrc((const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qrow0 * p.q_sr,
+                                  (rows - 1) * q_rs + D * 2);
+        const auto gr = make_rsrc((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)qrow0 * p.do_sr,
+                                  (rows - 1) * do_rs + D * 2);
+#pragma unroll
+        for (int i = 0; i < NCH_T; ++i) {
+            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            qbuf[i] = buf_load16(qr, r * q_rs + col * 2);
+            gbuf[i] = buf_load16(gr, r * do_rs + col * 2);
+        }
+        if (tid < BN) {
+            const int i = qrow0 + tid;
+            const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
+            lbuf = i < p.L ? p.lse[b * p.lse_sb + h * p.lse_sh + i] * kLog2e : 0.f;
+            dbuf = i < p.L ? p.dsum[rowid + i] : 0.f;
+        }
+    };
+    auto store_tile = [&](int stage) {
+        uint16_t* Qs = smem + stage * STAGE;
+        uint16_t* Gs = Qs + TILE;
+        float* Ls = (float*)(Gs + TILE);
+#pragma unroll
+        for (int i = 0; i < NCH_T; ++i) {
+            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            *(uint4*)(Qs + bwd_pos(r) * RS + col) = qbuf[i];
+            *(uint4*)(Gs + bwd_pos(r) * RS + col) = gbuf[i];
+        }
+        if (tid < BN) {
+            Ls[tid] = lbuf;
+            Ls[BN + tid] = dbuf;
+        }
+    };
+
+    if (nsteps > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        if (st + 1 < nsteps) load_tile(st + 1);
+        int h, qrow0;
+        step_coords(st, h, qrow0);
+        const uint16_t* Qs = smem + (st & 1) * STAGE;
+        const uint16_t* Gs = Qs + TILE;
+        const float* Ls = (const float*)(Gs + TILE);
+        // causal: the wave's keys need queries >= wkey0
+        const bool active = wave_has_keys && (!CAUSAL || qrow0 + BN - 1 >= wkey0);
+        if (active) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const uint4 qa = *(const uint4*)(Qs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    const uint4 ga = *(const uint4*)(Gs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    s = Tr::mfma32(as_vec8<Tr>(qa), as_vec8<Tr>(kreg[kk]), s);
+                    dp = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(vreg[kk]), dp);
+                }
+                // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
+                const int qbase = qb * 32 + 8 * hh;
+                const float4 l0 = *(const float4*)(Ls + qbase), l1 = *(const float4*)(Ls + qbase + 4);
+                const float4 l2 = *(const float4*)(Ls + qbase + 16), l3 = *(const float4*)(Ls + qbase + 20);
+                const float4 d0 = *(const float4*)(Ls + BN + qbase), d1 = *(const float4*)(Ls + BN + qbase + 4);
+                const float4 d2 = *(const float4*)(Ls + BN + qbase + 16), d3 = *(const float4*)(Ls + BN + qbase + 20);
+                const float lv[16] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w,
+                                      l2.x, l2.y, l2.z, l2.w, l3.x, l3.y, l3.z, l3.w};
+                const float dvv[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                                       d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+                const bool edge = (qrow0 + BN > p.L) || (CAUSAL && qrow0 < wkey0 + 31);
+                float pv[16], ds[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float e = fast_exp2(fmaf(s[r], c2, -lv[r]));
+                    if (edge) {
+                        const int qi = qrow0 + qbase + (r >> 3) * 16 + (r & 7);
+                        const bool keep = qi < p.L && (!CAUSAL || qi >= my_key);
+                        e = keep ? e : 0.f;
+                    }
+                    pv[r] = e;
+                    ds[r] = e * (dp[r] - dvv[r]);
+                }
+                uint4 pp[2], pd[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    pp[c].x = Tr::pack2(pv[c * 8 + 0], pv[c * 8 + 1]);
+                    pp[c].y = Tr::pack2(pv[c * 8 + 2], pv[c * 8 + 3]);
+                    pp[c].z = Tr::pack2(pv[c * 8 + 4], pv[c * 8 + 5]);
+                    pp[c].w = Tr::pack2(pv[c * 8 + 6], pv[c * 8 + 7]);
+                    pd[c].x = Tr::pack2(ds[c * 8 + 0], ds[c * 8 + 1]);
+                    pd[c].y = Tr::pack2(ds[c * 8 + 2], ds[c * 8 + 3]);
+                    pd[c].z = Tr::pack2(ds[c * 8 + 4], ds[c * 8 + 5]);
+                    pd[c].w = Tr::pack2(ds[c * 8 + 6], ds[c * 8 + 7]);
+                }
+                // dV^T += dO^T P and dK^T += Q^T dS over the tile's two 16-query chunks
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const uint4 ga = read_tr<RS>(Gs, qb * 2 + c, db * 32, lane);
+                        const uint4 qa = read_tr<RS>(Qs, qb * 2 + c, db * 32, lane);
+                        dv[db] = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(pp[c]), dv[db]);
+                        dk[db] = Tr::mfma32(as_vec8<Tr>(qa), as_vec8<Tr>(pd[c]), dk[db]);
+                    }
+            }
+        }
+        if (st + 1 < nsteps) store_tile((st + 1) & 1);
+        __syncthreads();
+    }
+
+    // dK = scale * dK^T, dV = dV^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
+    const int dk_rs = (int)(p.dk_sr * 2), dv_rs = (int)(p.dv_sr * 2);
+    const auto krs_o = make_rsrc((uint16_t*)p.dk + b * p.dk_sb + kvh * p.dk_sh + (int64_t)k0 * p.dk_sr,
+                                 (krows - 1) * dk_rs + D * 2);
+    const auto vrs_o = make_rsrc((uint16_t*)p.dv + b * p.dv_sb + kvh * p.dv_sh + (int64_t)k0 * p.dv_sr,
+                                 (krows - 1) * dv_rs + D * 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + hh * 4;
+            uint2 a, c;
+            a.x = Tr::pack2(dk[db][4 * g + 0] * p.scale, dk[db][4 * g + 1] * p.scale);
+            a.y = Tr::pack2(dk[db][4 * g + 2] * p.scale, dk[db][4 * g + 3] * p.scale);
+            c.x = Tr::pack2(dv[db][4 * g + 0], dv[db][4 * g + 1]);
+            c.y = Tr::pack2(dv[db][4 * g + 2], dv[db][4 * g + 3]);
+            buf_store8(a, krs_o, lkey * dk_rs + d * 2);
+            buf_store8(c, vrs_o, lkey * dv_rs + d * 2);
+        }
+}
+
+template <typename Tr, int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
+    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
+    if (nrows > 0)
+        hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, p);
+    if (nrows > 0) {
+        const unsigned g = (unsigned)p.n_qtiles * p.Hq * p.B;
+        if (causal)
+            hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, true>), dim3(g), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, false>), dim3(g), dim3(256), 0, s, p);
+    }
+    if ((int64_t)p.S * p.Hkv * p.B > 0) {
+        const unsigned g = (unsigned)p.n_ktiles * p.Hkv * p.B;
+        if (causal)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, true>), dim3(g), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, false>), dim3(g), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tr>
+hipError_t launch_bwd_t(const BwdParams& p, int D, bool causal, hipStream_t s) {
+    switch (D) {
+        case 64: return launch_bwd_d<Tr, 64>(p, causal, s);
+        case 96: return launch_bwd_d<Tr, 96>(p, causal, s);
+        case 128: return launch_bwd_d<Tr, 128>(p, causal, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, hipStream_t stream) {
+    return p.elem == ELEM_BF16 ? launch_bwd_t<BF16>(p, D, causal, stream)
+                               : launch_bwd_t<F16>(p, D, causal, stream);
+}
+
+}  // namespace sdpa

@@ -188,11 +188,13 @@ hipError_t launch_single_pass(sdpa_dtype dtype, const sdpa::AttnParams& p, int D
     }
 }
 
+size_t bwd_workspace_bytes(const Shapes& s) { return (size_t)(s.B * s.Hq * s.L) * sizeof(float) + 256; }
+
 }  // namespace
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 1; }
+int sdpa_abi_version(void) { return 2; }
 
 const char* sdpa_last_error(void) { return g_err; }
 
@@ -385,6 +387,89 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     hipError_t e = launch_single_pass(dtype, p, E, is_causal != 0, sdpa::MASK_NONE, true,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
+                                    const sdpa_tensor4* v, int enable_gqa, size_t* bytes) {
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+    Shapes s;
+    sdpa_status st = check_shapes(dtype, q, k, v, nullptr, enable_gqa, &s);
+    if (st != SDPA_OK) return st;
+    *bytes = bwd_workspace_bytes(s);
+    return ok();
+}
+
+sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
+                     const sdpa_tensor4* v, const sdpa_tensor4* out, const sdpa_tensor4* lse,
+                     const sdpa_tensor4* dout, int is_causal, const double* scale, int enable_gqa,
+                     const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    Shapes s;
+    sdpa_status st = check_shapes(dtype, q, k, v, nullptr, enable_gqa, &s);
+    if (st != SDPA_OK) return st;
+    if (dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "the backward kernels take bf16 or fp16");
+    if (!out || !lse || !dout || !dq || !dk || !dv)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv descriptors must not be NULL");
+    const int64_t want_o[4] = {s.B, s.Hq, s.L, s.Ev};
+    const int64_t want_q[4] = {s.B, s.Hq, s.L, s.E};
+    const int64_t want_k[4] = {s.B, s.Hkv, s.S, s.E};
+    const int64_t want_v[4] = {s.B, s.Hkv, s.S, s.Ev};
+    for (int d = 0; d < 4; ++d) {
+        if (out->size[d] != want_o[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "out must be (B, Hq, L, Ev)");
+        if (dout->size[d] != want_o[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "dout must be (B, Hq, L, Ev)");
+        if (dq->size[d] != want_q[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "dq must be (B, Hq, L, E)");
+        if (dk->size[d] != want_k[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "dk must be (B, Hkv, S, E)");
+        if (dv->size[d] != want_v[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "dv must be (B, Hkv, S, Ev)");
+        if (d < 3 && lse->size[d] != want_o[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    }
+    if (lse->size[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    if (s.B * s.Hq * s.L == 0 && s.B * s.Hkv * s.S == 0) return ok();  // nothing to compute
+    if (s.E != s.Ev)
+        return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %lld and %lld)", (long long)s.E,
+                    (long long)s.Ev);
+    if (!supported_head_dim(s.E))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not one of 64, 96, 128", (long long)s.E);
+    const int eb = elem_bytes(dtype);
+    const sdpa_tensor4* vec_t[8] = {q, k, v, out, dout, dq, dk, dv};
+    const char* vec_n[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+    for (int i = 0; i < 8; ++i) {
+        const bool empty = vec_t[i]->size[0] * vec_t[i]->size[1] * vec_t[i]->size[2] == 0;
+        if (!empty && (st = check_vector_layout(*vec_t[i], eb, vec_n[i])) != SDPA_OK) return st;
+    }
+    if (s.L > 0 && !lse->data) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse data must not be NULL");
+    const int64_t lse_sr = lse->size[2] > 1 ? lse->stride[2] : 1;
+    if (lse_sr != 1) return fail(SDPA_ERR_UNSUPPORTED, "lse: the query dimension must have stride 1");
+    double sc;
+    if ((st = resolve_scale(scale, s.E, &sc)) != SDPA_OK) return st;
+    const size_t need = bwd_workspace_bytes(s);
+    if (workspace_bytes < need || !workspace)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes needed, %zu given", need,
+                    workspace_bytes);
+
+    sdpa::BwdParams p{};
+    p.q = q->data; p.k = k->data; p.v = v->data; p.o = out->data; p.dout = dout->data;
+    p.lse = (const float*)lse->data;
+    p.dsum = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    p.dq = dq->data; p.dk = dk->data; p.dv = dv->data;
+    p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sr = q->stride[2];
+    p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sr = k->stride[2];
+    p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_sr = v->stride[2];
+    p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_sr = out->stride[2];
+    p.do_sb = dout->stride[0]; p.do_sh = dout->stride[1]; p.do_sr = dout->stride[2];
+    p.dq_sb = dq->stride[0]; p.dq_sh = dq->stride[1]; p.dq_sr = dq->stride[2];
+    p.dk_sb = dk->stride[0]; p.dk_sh = dk->stride[1]; p.dk_sr = dk->stride[2];
+    p.dv_sb = dv->stride[0]; p.dv_sh = dv->stride[1]; p.dv_sr = dv->stride[2];
+    p.lse_sb = lse->size[0] > 1 ? lse->stride[0] : 0;
+    p.lse_sh = lse->size[1] > 1 ? lse->stride[1] : 0;
+    p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
+    p.L = (int)s.L; p.S = (int)s.S;
+    p.n_qtiles = (int)((s.L + 127) / 128);
+    p.n_ktiles = (int)((s.S + 127) / 128);
+    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16;
+    p.scale = (float)sc;
+    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -20,8 +20,8 @@ SDPA_OK, SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED, SDPA_ERR_DEVICE = 0, 1
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 _DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
 
-EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_last_error",
-            "sdpa_abi_version")
+EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_bwd",
+            "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_abi_version")
 
 
 class SdpaTensor4(ctypes.Structure):
@@ -68,6 +68,12 @@ def load_library():
                                     dbl, ctypes.c_int, ctypes.POINTER(dbl), ctypes.c_int,
                                     vp, i64, i64, vp, i64, vp]
     lib.sdpa_fwd_varlen.restype = ctypes.c_int
+    lib.sdpa_bwd.argtypes = [ctypes.c_int, P, P, P, P, P, P, ctypes.c_int, ctypes.POINTER(dbl),
+                             ctypes.c_int, P, P, P, vp, ctypes.c_size_t, vp]
+    lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int, P, P, P, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.sdpa_bwd_workspace_size.restype = ctypes.c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_abi_version.argtypes = []
@@ -206,6 +212,52 @@ def sdpa_fwd(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, 
                             int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), do, dl,
                             ws_ptr, nbytes.value, int(num_splits), _stream(dev)))
     return o4.reshape(*query.shape[:-1], Ev), l4.reshape(*query.shape[:-1])
+
+
+def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
+    """Workspace bytes sdpa_bwd needs for these shapes (host only)."""
+    lib = load_library()
+    q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+    n = ctypes.c_size_t(0)
+    _check(lib.sdpa_bwd_workspace_size(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4),
+                                       int(bool(enable_gqa)), ctypes.byref(n)))
+    return n.value
+
+
+def sdpa_bwd(query, key, value, out, lse, grad, is_causal=False, scale=None, enable_gqa=False,
+             workspace=None):
+    """Gradients of exact attention on the GPU: returns (grad_query, grad_key, grad_value).
+
+    ``out`` and ``lse`` are sdpa_fwd's results for the same arguments and
+    ``grad`` the gradient with respect to ``out`` (exactref.ai
+    "scaled_dot_product_attention.backward"; no mask).  The outputs have the
+    shapes and dtype of query, key and value.
+    """
+    lib = load_library()
+    _require_gpu(query, key, value, out, lse, grad)
+    if query.dtype not in (torch.float16, torch.bfloat16) or any(
+            t.dtype != query.dtype for t in (key, value, out, grad)):
+        raise ValueError("the backward takes float16 or bfloat16 query, key, value, out and grad")
+    q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+    if k4.shape[0] != q4.shape[0] or v4.shape[0] != q4.shape[0]:
+        raise ValueError("query, key and value must share the batch dimensions")
+    B, Hq, L, E = q4.shape
+    Hkv, S, Ev = k4.shape[1], v4.shape[2], v4.shape[3]
+    o4, g4 = _as4d(out), _as4d(grad)
+    l4 = lse.reshape(B, Hq, L, 1)
+    dev = query.device
+    dq4 = torch.empty((B, Hq, L, E), dtype=query.dtype, device=dev)
+    dk4 = torch.empty((B, Hkv, S, E), dtype=query.dtype, device=dev)
+    dv4 = torch.empty((B, Hkv, S, Ev), dtype=query.dtype, device=dev)
+    with torch.cuda.device(dev):
+        nbytes = sdpa_bwd_workspace_size(q4, k4, v4, enable_gqa)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _check(lib.sdpa_bwd(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4), _desc(o4), _desc(l4),
+                            _desc(g4), int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)),
+                            _desc(dq4), _desc(dk4), _desc(dv4), workspace.data_ptr(), nbytes,
+                            _stream(dev)))
+    return dq4.reshape(query.shape), dk4.reshape(key.shape), dv4.reshape(value.shape)
 
 
 def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
