@@ -18,15 +18,17 @@
 //                     registers, then dQ^T += K^T dS^T with dS^T as the B
 //                     operand straight from the score registers and K^T read
 //                     from LDS with the transposing ds_read_b64_tr_b16.
-//   bwd_dkdv_kernel   one workgroup per 128 keys (4 wavefronts x 32), over the
-//                     query heads of the key/value head and their 64-row query
-//                     blocks: S = Q K^T and dP = dO V^T (one key per lane),
-//                     then dV^T += dO^T P and dK^T += Q^T dS with P and dS as
-//                     B operands from the score registers and dO^T, Q^T read
+//   bwd_dkdv_kernel   one workgroup per 128 keys, over the query heads of the
+//                     key/value head and their 64-row query blocks, with two
+//                     roles per 32-key slice: one wavefront computes S = Q K^T
+//                     and dP = dO V^T (one key per lane) and dK^T += Q^T dS,
+//                     another S and dV^T += dO^T P; P and dS are B operands
+//                     from the score registers, dO^T and Q^T are read
 //                     transposed from LDS.
-// No atomics: each gradient element has one owner.  The price is that S and
-// dP are computed twice (once per owner), 7 matrix products per kept
-// (query, key) pair and head dimension instead of the 5 of one shared pass.
+// No atomics: each gradient element has one owner.  The price is that S is
+// computed three times and dP twice, 8 matrix products per kept (query, key)
+// pair and head dimension instead of the 5 of one shared pass; in exchange
+// every wavefront fits in 256 registers (two per SIMD).
 //
 // LDS tiles are row-major with 8 elements of padding per row (16-byte row
 // reads conflict-free).  Rows are stored at position swap23(r) within each
@@ -153,6 +155,10 @@ void bwd_dq_kernel(BwdParams p) {
     const float lse2 = row_ok ? p.lse[b * p.lse_sb + h * p.lse_sh + my_row] * kLog2e : 0.f;
     const float drow = row_ok ? p.dsum[rowid + my_row] : 0.f;
     const float c2 = p.scale * kLog2e;  // signed
+    // All of the above has landed before the loop: otherwise the first uses in
+    // the loop would wait (in every iteration) for the loads issued after them,
+    // the next block's prefetch included.
+    wait_vmem_all();
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -260,20 +266,26 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// Eight wavefronts per 128 keys, two roles over the same 32-key slices:
+// wavefronts 0-3 own dK (S, dP, dS, dK^T += Q^T dS), wavefronts 4-7 own dV
+// (S, P, dV^T += dO^T P).  Each role fits two wavefronts per SIMD; S is
+// computed by both roles.
 template <typename Tr, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BK = 128, BN = 64;     // keys per workgroup, queries per step
+    constexpr int NT = 512;
     constexpr int RS = D + 8;
     constexpr int TILE = BN * RS;
     constexpr int STAGE = 2 * TILE + 2 * BN * 2;  // Q, dO, then lse*log2e and D (fp32, natural order)
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int NCH = BN * D / 8;
-    constexpr int NCH_T = NCH / 256;
-    static_assert(NCH % 256 == 0, "chunks per thread");
+    constexpr int NCH_T = (NCH + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int role = __builtin_amdgcn_readfirstlane(wave >> 2);  // 0: dK, 1: dV
+    const int kw = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
     const int nbh = p.Hkv * p.B;
     const int kt = (int)(blockIdx.x / nbh);   // lowest key tiles (most causal work) first
@@ -282,31 +294,29 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int k0 = kt * BK;
     if (k0 >= p.S) return;
     const int krows = min(BK, p.S - k0);
-    const int wkey0 = k0 + wave * 32;          // first key of this wavefront
+    const int wkey0 = k0 + kw * 32;            // first key of this wavefront
     const int my_key = wkey0 + lq;
-    const bool wave_has_keys = wave * 32 < krows;
+    const bool wave_has_keys = kw * 32 < krows;
 
-    // K^T and V^T operands (lane: key lq, elements 16kk + 8hh .. +7)
+    // K^T (and for dK, V^T) operands (lane: key lq, elements 16kk + 8hh .. +7)
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
     const auto krs = make_rsrc((const uint16_t*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)k0 * p.k_sr,
                                (krows - 1) * k_rs + D * 2);
     const auto vrs = make_rsrc((const uint16_t*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)k0 * p.v_sr,
                                (krows - 1) * v_rs + D * 2);
-    const int lkey = wave * 32 + lq;
+    const int lkey = kw * 32 + lq;
     uint4 kreg[NKK], vreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         kreg[kk] = buf_load16(krs, lkey * k_rs + (kk * 16 + hh * 8) * 2);
-        vreg[kk] = buf_load16(vrs, lkey * v_rs + (kk * 16 + hh * 8) * 2);
+        vreg[kk] = role == 0 ? buf_load16(vrs, lkey * v_rs + (kk * 16 + hh * 8) * 2) : zero4();
     }
     const float c2 = p.scale * kLog2e;
+    wait_vmem_all();  // as in the dQ kernel: no wait for these inside the loop
 
-    f32x16_t dv[NDB], dk[NDB];
+    f32x16_t acc[NDB];  // dK^T (role 0) or dV^T (role 1): rows e, columns keys
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dv[db] = f32x16_t{};
-        dk[db] = f32x16_t{};
-    }
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
     // query blocks this workgroup visits: causal keeps query i >= key j
     const int qb0 = CAUSAL ? k0 / BN : 0;
@@ -330,15 +340,20 @@ void bwd_dkdv_kernel(BwdParams p) {
                                   (rows - 1) * do_rs + D * 2);
 #pragma unroll
         for (int i = 0; i < NCH_T; ++i) {
-            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-            qbuf[i] = buf_load16(qr, r * q_rs + col * 2);
-            gbuf[i] = buf_load16(gr, r * do_rs + col * 2);
+            const int ch = tid + NT * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            if (NCH % NT == 0 || ch < NCH) {
+                qbuf[i] = buf_load16(qr, r * q_rs + col * 2);
+                gbuf[i] = buf_load16(gr, r * do_rs + col * 2);
+            }
         }
         if (tid < BN) {
-            const int i = qrow0 + tid;
+            // raw values (range-checked loads read 0 past the last row); scaled
+            // when stored, so that nothing here waits for the loads
             const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
-            lbuf = i < p.L ? p.lse[b * p.lse_sb + h * p.lse_sh + i] * kLog2e : 0.f;
-            dbuf = i < p.L ? p.dsum[rowid + i] : 0.f;
+            const auto lr = make_rsrc(p.lse + b * p.lse_sb + h * p.lse_sh + qrow0, rows * 4);
+            const auto dr = make_rsrc(p.dsum + rowid + qrow0, rows * 4);
+            lbuf = __uint_as_float(buf_load4(lr, tid * 4));
+            dbuf = __uint_as_float(buf_load4(dr, tid * 4));
         }
     };
     auto store_tile = [&](int stage) {
@@ -347,12 +362,14 @@ void bwd_dkdv_kernel(BwdParams p) {
         float* Ls = (float*)(Gs + TILE);
 #pragma unroll
         for (int i = 0; i < NCH_T; ++i) {
-            const int ch = tid + 256 * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-            *(uint4*)(Qs + bwd_pos(r) * RS + col) = qbuf[i];
-            *(uint4*)(Gs + bwd_pos(r) * RS + col) = gbuf[i];
+            const int ch = tid + NT * i, r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+            if (NCH % NT == 0 || ch < NCH) {
+                *(uint4*)(Qs + bwd_pos(r) * RS + col) = qbuf[i];
+                *(uint4*)(Gs + bwd_pos(r) * RS + col) = gbuf[i];
+            }
         }
         if (tid < BN) {
-            Ls[tid] = lbuf;
+            Ls[tid] = lbuf * kLog2e;
             Ls[BN + tid] = dbuf;
         }
     };
@@ -378,54 +395,59 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
                     const uint4 qa = *(const uint4*)(Qs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
-                    const uint4 ga = *(const uint4*)(Gs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
                     s = Tr::mfma32(as_vec8<Tr>(qa), as_vec8<Tr>(kreg[kk]), s);
-                    dp = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(vreg[kk]), dp);
+                }
+                if (role == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const uint4 ga = *(const uint4*)(Gs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
+                        dp = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(vreg[kk]), dp);
+                    }
                 }
                 // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
                 const int qbase = qb * 32 + 8 * hh;
-                const float4 l0 = *(const float4*)(Ls + qbase), l1 = *(const float4*)(Ls + qbase + 4);
-                const float4 l2 = *(const float4*)(Ls + qbase + 16), l3 = *(const float4*)(Ls + qbase + 20);
-                const float4 d0 = *(const float4*)(Ls + BN + qbase), d1 = *(const float4*)(Ls + BN + qbase + 4);
-                const float4 d2 = *(const float4*)(Ls + BN + qbase + 16), d3 = *(const float4*)(Ls + BN + qbase + 20);
-                const float lv[16] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w,
-                                      l2.x, l2.y, l2.z, l2.w, l3.x, l3.y, l3.z, l3.w};
-                const float dvv[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
-                                       d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
                 const bool edge = (qrow0 + BN > p.L) || (CAUSAL && qrow0 < wkey0 + 31);
-                float pv[16], ds[16];
+                float w[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float e = fast_exp2(fmaf(s[r], c2, -lv[r]));
-                    if (edge) {
-                        const int qi = qrow0 + qbase + (r >> 3) * 16 + (r & 7);
-                        const bool keep = qi < p.L && (!CAUSAL || qi >= my_key);
-                        e = keep ? e : 0.f;
+                for (int half = 0; half < 2; ++half) {
+                    const float4 la = *(const float4*)(Ls + qbase + 16 * half);
+                    const float4 lb = *(const float4*)(Ls + qbase + 16 * half + 4);
+                    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+                    float dv8[8];
+                    if (role == 0) {
+                        const float4 da = *(const float4*)(Ls + BN + qbase + 16 * half);
+                        const float4 db4 = *(const float4*)(Ls + BN + qbase + 16 * half + 4);
+                        dv8[0] = da.x; dv8[1] = da.y; dv8[2] = da.z; dv8[3] = da.w;
+                        dv8[4] = db4.x; dv8[5] = db4.y; dv8[6] = db4.z; dv8[7] = db4.w;
                     }
-                    pv[r] = e;
-                    ds[r] = e * (dp[r] - dvv[r]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 8 * half + j;
+                        float e = fast_exp2(fmaf(s[r], c2, -lv[j]));
+                        if (edge) {
+                            const int qi = qrow0 + qbase + 16 * half + j;
+                            const bool keep = qi < p.L && (!CAUSAL || qi >= my_key);
+                            e = keep ? e : 0.f;
+                        }
+                        w[r] = role == 0 ? e * (dp[r] - dv8[j]) : e;  // dS or P
+                    }
                 }
-                uint4 pp[2], pd[2];
+                uint4 pw[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    pp[c].x = Tr::pack2(pv[c * 8 + 0], pv[c * 8 + 1]);
-                    pp[c].y = Tr::pack2(pv[c * 8 + 2], pv[c * 8 + 3]);
-                    pp[c].z = Tr::pack2(pv[c * 8 + 4], pv[c * 8 + 5]);
-                    pp[c].w = Tr::pack2(pv[c * 8 + 6], pv[c * 8 + 7]);
-                    pd[c].x = Tr::pack2(ds[c * 8 + 0], ds[c * 8 + 1]);
-                    pd[c].y = Tr::pack2(ds[c * 8 + 2], ds[c * 8 + 3]);
-                    pd[c].z = Tr::pack2(ds[c * 8 + 4], ds[c * 8 + 5]);
-                    pd[c].w = Tr::pack2(ds[c * 8 + 6], ds[c * 8 + 7]);
+                    pw[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
+                    pw[c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
+                    pw[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
+                    pw[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
                 }
-                // dV^T += dO^T P and dK^T += Q^T dS over the tile's two 16-query chunks
+                // dK^T += Q^T dS (role 0) or dV^T += dO^T P (role 1) over two 16-query chunks
+                const uint16_t* Xs = role == 0 ? Qs : Gs;
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const uint4 ga = read_tr<RS>(Gs, qb * 2 + c, db * 32, lane);
-                        const uint4 qa = read_tr<RS>(Qs, qb * 2 + c, db * 32, lane);
-                        dv[db] = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(pp[c]), dv[db]);
-                        dk[db] = Tr::mfma32(as_vec8<Tr>(qa), as_vec8<Tr>(pd[c]), dk[db]);
+                        const uint4 xa = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
+                        acc[db] = Tr::mfma32(as_vec8<Tr>(xa), as_vec8<Tr>(pw[c]), acc[db]);
                     }
             }
         }
@@ -433,24 +455,23 @@ void bwd_dkdv_kernel(BwdParams p) {
         __syncthreads();
     }
 
-    // dK = scale * dK^T, dV = dV^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
-    const int dk_rs = (int)(p.dk_sr * 2), dv_rs = (int)(p.dv_sr * 2);
-    const auto krs_o = make_rsrc((uint16_t*)p.dk + b * p.dk_sb + kvh * p.dk_sh + (int64_t)k0 * p.dk_sr,
-                                 (krows - 1) * dk_rs + D * 2);
-    const auto vrs_o = make_rsrc((uint16_t*)p.dv + b * p.dv_sb + kvh * p.dv_sh + (int64_t)k0 * p.dv_sr,
-                                 (krows - 1) * dv_rs + D * 2);
+    // dK = scale * dK^T or dV = dV^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
+    const float f = role == 0 ? p.scale : 1.f;
+    const int o_rs = (int)((role == 0 ? p.dk_sr : p.dv_sr) * 2);
+    void* obase = role == 0 ? p.dk : p.dv;
+    const int64_t o_sb = role == 0 ? p.dk_sb : p.dv_sb, o_sh = role == 0 ? p.dk_sh : p.dv_sh;
+    const int64_t o_sr = role == 0 ? p.dk_sr : p.dv_sr;
+    const auto ors = make_rsrc((uint16_t*)obase + b * o_sb + kvh * o_sh + (int64_t)k0 * o_sr,
+                               (krows - 1) * o_rs + D * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = db * 32 + g * 8 + hh * 4;
-            uint2 a, c;
-            a.x = Tr::pack2(dk[db][4 * g + 0] * p.scale, dk[db][4 * g + 1] * p.scale);
-            a.y = Tr::pack2(dk[db][4 * g + 2] * p.scale, dk[db][4 * g + 3] * p.scale);
-            c.x = Tr::pack2(dv[db][4 * g + 0], dv[db][4 * g + 1]);
-            c.y = Tr::pack2(dv[db][4 * g + 2], dv[db][4 * g + 3]);
-            buf_store8(a, krs_o, lkey * dk_rs + d * 2);
-            buf_store8(c, vrs_o, lkey * dv_rs + d * 2);
+            uint2 st;
+            st.x = Tr::pack2(acc[db][4 * g + 0] * f, acc[db][4 * g + 1] * f);
+            st.y = Tr::pack2(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f);
+            buf_store8(st, ors, lkey * o_rs + d * 2);
         }
 }
 
@@ -469,9 +490,9 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
     if ((int64_t)p.S * p.Hkv * p.B > 0) {
         const unsigned g = (unsigned)p.n_ktiles * p.Hkv * p.B;
         if (causal)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, true>), dim3(g), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, true>), dim3(g), dim3(512), 0, s, p);
         else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, false>), dim3(g), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, false>), dim3(g), dim3(512), 0, s, p);
     }
     return hipGetLastError();
 }
