@@ -49,7 +49,7 @@ import numpy as np
 
 __all__ = [
     "resolve_scale", "bias_from_mask", "causal_bias", "logits", "weights",
-    "sdpa", "sdpa_backward", "block_diagonal_bias", "sdpa_varlen", "entropy",
+    "sdpa", "sdpa_backward", "block_diagonal_bias", "sdpa_varlen", "sdpa_paged", "entropy",
 ]
 
 
@@ -292,6 +292,49 @@ def sdpa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, is_causal=False, scale
                      enable_gqa=enable_gqa)
         out[a:b] = np.swapaxes(o, 0, 1)
         lse[:, a:b] = l_
+    return out, lse
+
+
+def sdpa_paged(q, k_cache, v_cache, block_table, seq_lens, is_causal=False, scale=None,
+               enable_gqa=False):
+    """Attention of new query rows against a paged key/value cache, float64.
+
+    q (B, Hq, L, E); k_cache (n_pages, Hkv, page_size, E) and v_cache
+    (n_pages, Hkv, page_size, Ev); block_table (B, max_blocks) ints: logical
+    block j of sequence b lives in page block_table[b][j]; seq_lens (B,): the
+    cached length n_b of each sequence (the L new rows' own keys included).
+    Sequence b attends to its first n_b cached keys, gathered page by page
+    (the paged KV cache the pages mention for vLLM/FlashInfer-style serving).
+    is_causal aligns bottom-right: new row i (0-based of L) is the sequence's
+    position n_b - L + i and keeps key j iff j <= n_b - L + i.  Returns out
+    (B, Hq, L, Ev) and lse (B, Hq, L).  A table entry outside [0, n_pages) for
+    a needed block raises ValueError (nothing is read from outside the cache).
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    bt = np.asarray(block_table)
+    lens = [int(x) for x in np.asarray(seq_lens).ravel()]
+    B, Hq, L, E = q.shape
+    n_pages, Hkv, ps, _ = kc.shape
+    Ev = vc.shape[-1]
+    out = np.zeros((B, Hq, L, Ev))
+    lse = np.full((B, Hq, L), -np.inf)
+    for b in range(B):
+        n = lens[b]
+        nblk = (n + ps - 1) // ps
+        if nblk > bt.shape[1]:
+            raise ValueError(f"sequence {b}: {n} keys need {nblk} blocks, the table has {bt.shape[1]}")
+        pages = [int(x) for x in bt[b, :nblk]]
+        if any(pg < 0 or pg >= n_pages for pg in pages):
+            raise ValueError(f"sequence {b}: block table entry outside [0, {n_pages})")
+        kb = np.concatenate([kc[pg] for pg in pages], axis=1)[:, :n] if nblk else np.zeros((Hkv, 0, E))
+        vb = np.concatenate([vc[pg] for pg in pages], axis=1)[:, :n] if nblk else np.zeros((Hkv, 0, Ev))
+        bias = None
+        if is_causal:
+            i = np.arange(L)[:, None]
+            j = np.arange(n)[None, :]
+            bias = np.where(j <= n - L + i, 0.0, -np.inf)
+        o, l_ = sdpa(q[b], kb, vb, attn_mask=bias, scale=scale, enable_gqa=enable_gqa)
+        out[b], lse[b] = o, l_
     return out, lse
 
 

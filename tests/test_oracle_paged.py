@@ -1,0 +1,106 @@
+"""Pins of the oracle's paged-cache attention (CPU, float64).
+
+oracle.sdpa_paged gathers each sequence's keys and values page by page and
+runs the (separately pinned) dense attention.  What fixes it:
+  * an in-order block table over a contiguous cache = the dense oracle on
+    that cache, and a shuffled page pool = the dense oracle on the keys
+    gathered independently with numpy fancy indexing;
+  * ragged cached lengths = dense attention on each sequence's prefix;
+  * bottom-right causal alignment: with L equal to the cached length it is
+    the ordinary (top-left) causal mask; a brute-force loop fixes the general
+    case; L = 1 is the same as no mask;
+  * table entries outside the page pool are refused.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import sdpa_oracle as O
+
+
+def _pool(rng, n_pages, hkv, ps, e):
+    return rng.standard_normal((n_pages, hkv, ps, e)), rng.standard_normal((n_pages, hkv, ps, e))
+
+
+def test_in_order_table_is_the_dense_cache():
+    rng = np.random.default_rng(1)
+    B, Hq, Hkv, L, E, ps, nblk = 2, 4, 2, 1, 8, 16, 5
+    kc, vc = _pool(rng, B * nblk, Hkv, ps, E)
+    q = rng.standard_normal((B, Hq, L, E))
+    bt = np.arange(B * nblk).reshape(B, nblk)
+    S = nblk * ps
+    out, lse = O.sdpa_paged(q, kc, vc, bt, [S, S], enable_gqa=True)
+    kd = kc.reshape(B, nblk, Hkv, ps, E).transpose(0, 2, 1, 3, 4).reshape(B, Hkv, S, E)
+    vd = vc.reshape(B, nblk, Hkv, ps, E).transpose(0, 2, 1, 3, 4).reshape(B, Hkv, S, E)
+    ro, rl = O.sdpa(q, kd, vd, enable_gqa=True)
+    assert np.abs(out - ro).max() < 1e-13 and np.abs(lse - rl).max() < 1e-13
+
+
+def test_shuffled_pool_and_ragged_lengths():
+    rng = np.random.default_rng(2)
+    B, Hq, Hkv, L, E, ps, maxb = 3, 2, 2, 2, 8, 16, 6
+    n_pages = 40
+    kc, vc = _pool(rng, n_pages, Hkv, ps, E)
+    q = rng.standard_normal((B, Hq, L, E))
+    bt = rng.permutation(n_pages)[:B * maxb].reshape(B, maxb)
+    lens = [1, 37, 96]
+    out, lse = O.sdpa_paged(q, kc, vc, bt, lens)
+    for b, n in enumerate(lens):
+        rows = np.arange(n)
+        kb = kc[bt[b, rows // ps], :, rows % ps, :].transpose(1, 0, 2)   # (Hkv, n, E), gathered directly
+        vb = vc[bt[b, rows // ps], :, rows % ps, :].transpose(1, 0, 2)
+        ro, rl = O.sdpa(q[b], kb, vb)
+        assert np.abs(out[b] - ro).max() < 1e-13 and np.abs(lse[b] - rl).max() < 1e-13
+
+
+def test_bottom_right_causal():
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, E, ps = 2, 2, 1, 4, 16
+    kc, vc = _pool(rng, 8, Hkv, ps, E)
+    bt = np.array([[3, 1, 6, 0], [2, 5, 7, 4]])
+    # L equal to the cached length: the ordinary causal mask
+    n = 21
+    q = rng.standard_normal((B, Hq, n, E))
+    out, lse = O.sdpa_paged(q, kc, vc, bt, [n, n], is_causal=True, enable_gqa=True)
+    for b in range(B):
+        rows = np.arange(n)
+        kb = kc[bt[b, rows // ps], :, rows % ps, :].transpose(1, 0, 2)
+        vb = vc[bt[b, rows // ps], :, rows % ps, :].transpose(1, 0, 2)
+        ro, rl = O.sdpa(q[b], kb, vb, is_causal=True, enable_gqa=True)
+        assert np.abs(out[b] - ro).max() < 1e-13
+    # general case against a pure-Python loop
+    L, lens = 3, [40, 9]
+    q = rng.standard_normal((B, Hq, L, E))
+    out, lse = O.sdpa_paged(q, kc, vc, bt, lens, is_causal=True, enable_gqa=True)
+    for b, n in enumerate(lens):
+        for h in range(Hq):
+            for i in range(L):
+                keep = [j for j in range(n) if j <= n - L + i]
+                sc = [sum(q[b, h, i, e] * kc[bt[b, j // ps], 0, j % ps, e] for e in range(E)) / math.sqrt(E)
+                      for j in keep]
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                tot = sum(w)
+                for e in range(E):
+                    ref = sum(wj * vc[bt[b, j // ps], 0, j % ps, e] for wj, j in zip(w, keep)) / tot
+                    assert abs(out[b, h, i, e] - ref) < 1e-12
+                assert abs(lse[b, h, i] - (m + math.log(tot))) < 1e-12
+    # one new row: causal keeps every cached key
+    q1 = q[:, :, :1]
+    a = O.sdpa_paged(q1, kc, vc, bt, lens, is_causal=True, enable_gqa=True)
+    c = O.sdpa_paged(q1, kc, vc, bt, lens, is_causal=False, enable_gqa=True)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_out_of_range_pages_refused():
+    rng = np.random.default_rng(4)
+    kc, vc = _pool(rng, 4, 1, 16, 4)
+    q = rng.standard_normal((1, 1, 1, 4))
+    with pytest.raises(ValueError):
+        O.sdpa_paged(q, kc, vc, np.array([[0, 4]]), [20])
+    with pytest.raises(ValueError):
+        O.sdpa_paged(q, kc, vc, np.array([[0, 1]]), [40])   # more keys than the table covers
+    # entries past the needed blocks are never looked at
+    out, _ = O.sdpa_paged(q, kc, vc, np.array([[2, 99]]), [16])
+    assert np.isfinite(out).all()
