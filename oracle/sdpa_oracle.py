@@ -143,7 +143,7 @@ def _softmax_parts(ell):
     """Row max m, unnormalised weights w = exp(l - m), row sum, and row classes."""
     nan_row, inf_row, empty_row, normal = _row_classes(ell)
     with np.errstate(invalid="ignore", over="ignore"):
-        m = np.where(normal, np.max(np.where(np.isnan(ell), -np.inf, ell), axis=-1), 0.0)
+        m = np.where(normal, np.max(np.where(np.isnan(ell), -np.inf, ell), axis=-1, initial=-np.inf), 0.0)
         w = np.exp(ell - m[..., None])
     w = np.where(normal[..., None], w, 0.0)
     rowsum = w.sum(axis=-1)

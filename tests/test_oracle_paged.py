@@ -104,3 +104,16 @@ def test_out_of_range_pages_refused():
     # entries past the needed blocks are never looked at
     out, _ = O.sdpa_paged(q, kc, vc, np.array([[2, 99]]), [16])
     assert np.isfinite(out).all()
+
+
+def test_no_cached_keys_is_an_empty_row():
+    """Full specification: a row with no kept key has weight 0 on every key, so
+    its output is 0 and its lse is log(0) = -inf (here: nothing cached)."""
+    rng = np.random.default_rng(5)
+    kc, vc = _pool(rng, 3, 1, 16, 4)
+    q = rng.standard_normal((2, 1, 1, 4))
+    out, lse = O.sdpa_paged(q, kc, vc, np.array([[0], [1]]), [0, 5])
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+    assert np.isfinite(out[1]).all()
+    o, l_ = O.sdpa(q[0], np.zeros((1, 0, 4)), np.zeros((1, 0, 4)))
+    assert o.shape == (1, 1, 4) and (o == 0).all() and np.isneginf(l_).all()
