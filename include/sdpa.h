@@ -155,6 +155,50 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
                             void* stream);
 
 /*
+ * sdpa_fwd_paged -- attention of a few new query rows per sequence against a
+ * paged key/value cache (the serving layout of vLLM-style engines the pages
+ * mention): the cached keys of a sequence live in fixed-size pages of a shared
+ * pool, listed in order by the sequence's row of a block table.
+ *
+ *   dtype       SDPA_BF16 or SDPA_F16.
+ *   q           (B, Hq, L, E): the new rows; L * Hq / Hkv <= 16.
+ *   k_cache     (n_pages, Hkv, page_size, E), v_cache (n_pages, Hkv, page_size, Ev):
+ *               the page pool; page_size a power of two >= 16; E == Ev in
+ *               {64, 96, 128}.
+ *   block_table DEVICE int32, B rows of bt_stride entries; entry (b, j) is the
+ *               page holding keys j*page_size .. (j+1)*page_size - 1 of sequence
+ *               b; max_blocks entries per row are valid.
+ *   seq_lens    DEVICE int32 (B): keys cached for each sequence (the new rows'
+ *               own keys included); clamped to max_seq_len and to
+ *               max_blocks * page_size on the device.
+ *   max_seq_len host upper bound of seq_lens (sizes the launch).
+ *   is_causal   non-zero: new row i (0-based of L) is position n - L + i of its
+ *               sequence (n its cached length) and keeps key j iff
+ *               j <= n - L + i (bottom-right alignment); with L = 1 it keeps
+ *               every cached key.
+ *   scale, enable_gqa, out (B, Hq, L, Ev), lse (B, Hq, L, 1) float32,
+ *   workspace (size from sdpa_fwd_paged_workspace_size), num_splits (0 auto,
+ *   k >= 1 splits) and stream: as for sdpa_fwd.
+ *
+ * A table entry outside [0, n_pages) for a kept key is never dereferenced:
+ * the rows that would read it come out NaN (output and lse) instead of
+ * silently using other memory.
+ */
+sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q,
+                           const sdpa_tensor4* k_cache, const sdpa_tensor4* v_cache,
+                           const int32_t* block_table, int64_t bt_stride, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t max_seq_len,
+                           int is_causal, const double* scale, int enable_gqa,
+                           const sdpa_tensor4* out, const sdpa_tensor4* lse,
+                           void* workspace, size_t workspace_bytes, int num_splits, void* stream);
+
+/* Workspace bytes sdpa_fwd_paged needs for these shapes (host only). */
+sdpa_status sdpa_fwd_paged_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q,
+                                          const sdpa_tensor4* k_cache, const sdpa_tensor4* v_cache,
+                                          int32_t max_seq_len, int enable_gqa, int num_splits,
+                                          size_t* bytes);
+
+/*
  * sdpa_bwd -- gradients of batched attention (exactref.ai
  * "scaled_dot_product_attention.backward").  With P the attention weights of
  * the forward, dP = dout V^T, D_i = sum_j P_ij dP_ij and dS = P * (dP - D):

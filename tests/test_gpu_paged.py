@@ -1,0 +1,106 @@
+"""Parity of the paged-cache decode (sdpa_fwd_paged, through the C interface)
+with the float64 oracle (oracle.sdpa_paged) on the same bf16/fp16 values.
+
+Bars as for the forward: max |GPU - oracle| <= 2e-2 on the output and 1e-3 on
+lse for bf16 / fp16.  Inputs: a shuffled page pool, ragged cached lengths
+(0, 1, page and split boundaries), GQA, bottom-right causal for several new
+rows, and table entries outside the pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_oracle as O
+from transformer_attention_04_amd import inputs
+from transformer_attention_04_amd import sdpa as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"bf16": (2e-2, 1e-3), "fp16": (2e-2, 1e-3)}
+
+
+def make_cache(B, Hq, Hkv, L, E, ps, lens, dtype, seed, extra_pages=7, extra_blocks=0):
+    """Query rows, a shuffled page pool holding every sequence's blocks, the
+    table (with ``extra_blocks`` spare columns past the longest sequence)."""
+    maxb = max(1, max((n + ps - 1) // ps for n in lens)) + extra_blocks
+    n_pages = B * maxb + extra_pages
+    q, kc, vc = inputs.randn_qkv((B, Hq, L, E), (n_pages, Hkv, ps, E), (n_pages, Hkv, ps, E), dtype, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    perm = torch.randperm(n_pages, generator=g)[:B * maxb]
+    bt = perm.reshape(B, maxb).to(torch.int32)
+    return q, kc, vc, bt, torch.tensor(lens, dtype=torch.int32)
+
+
+def run(q, kc, vc, bt, lens, dtype, **kw):
+    out, lse = S.sdpa_fwd_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), lens.to(DEV),
+                                max_seq_len=int(lens.max()) if lens.numel() else 0, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def check(gpu, ref, dtype, what):
+    (out, lse), (ro, rl) = gpu, ref
+    tol_o, tol_l = TOL[dtype]
+    empty = np.isneginf(rl)
+    assert np.isneginf(lse[empty]).all() and (out[empty] == 0).all(), f"{what}: empty rows"
+    fin = np.isfinite(rl)
+    eo = np.abs(out[fin] - ro[fin]).max(initial=0.0)
+    el = np.abs(lse[fin] - rl[fin]).max(initial=0.0)
+    assert eo <= tol_o and el <= tol_l, f"{what}: out err {eo:.3e}, lse err {el:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [64, 96, 128])
+@pytest.mark.parametrize("ps", [16, 64])
+def test_paged_ragged_lengths(dtype, E, ps):
+    lens = [0, 1, 15, 16, 17, 64, 129, 700, 1000]
+    B = len(lens)
+    q, kc, vc, bt, ln = make_cache(B, 8, 2, 1, E, ps, lens, dtype, seed=E + ps)
+    ref = O.sdpa_paged(q, kc, vc, bt, ln, enable_gqa=True)
+    check(run(q, kc, vc, bt, ln, dtype, enable_gqa=True), ref, dtype, f"E={E} ps={ps}")
+    # several splits per sequence
+    check(run(q, kc, vc, bt, ln, dtype, enable_gqa=True, num_splits=5), ref, dtype, f"E={E} ps={ps} 5 splits")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_paged_bottom_right_causal(dtype):
+    lens = [2, 33, 300, 513]
+    q, kc, vc, bt, ln = make_cache(len(lens), 4, 2, 2, 128, 32, lens, dtype, seed=21)
+    for causal in (False, True):
+        ref = O.sdpa_paged(q, kc, vc, bt, ln, is_causal=causal, enable_gqa=True)
+        check(run(q, kc, vc, bt, ln, dtype, is_causal=causal, enable_gqa=True, num_splits=3), ref, dtype,
+              f"L=2 causal={causal}")
+    # one new row with causal: every cached key is kept
+    ref = O.sdpa_paged(q[:, :, :1], kc, vc, bt, ln, is_causal=True, enable_gqa=True)
+    check(run(q[:, :, :1].contiguous(), kc, vc, bt, ln, dtype, is_causal=True, enable_gqa=True), ref, dtype,
+          "L=1 causal")
+
+
+def test_paged_bad_table_entry_gives_nan_rows():
+    lens = [100, 100]   # blocks 0..6 of 16 keys; the table has 2 spare columns
+    q, kc, vc, bt, ln = make_cache(2, 2, 2, 1, 64, 16, lens, "bf16", seed=31, extra_blocks=2)
+    bt = bt.clone()
+    bt[1, 3] = kc.shape[0] + 5     # outside the pool, inside sequence 1's kept range
+    out, lse = run(q, kc, vc, bt, ln, "bf16")
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    ref = O.sdpa_paged(q[:1], kc, vc, bt[:1], ln[:1])
+    check((out[:1], lse[:1]), ref, "bf16", "good sequence beside a bad one")
+    # entries past the cached length are never read
+    bt2 = bt.clone()
+    bt2[1, 3] = bt[0, 3]
+    bt2[1, 7] = -1
+    bt2[1, 8] = 1 << 30
+    out, lse = run(q, kc, vc, bt2, ln, "bf16")
+    assert np.isfinite(out).all()
+    check((out, lse), O.sdpa_paged(q, kc, vc, bt2[:, :7], ln), "bf16", "spare table columns")
+
+
+def test_paged_full_decode_shape_sampled():
+    """B=64, Hq=32, Hkv=8, 32768 cached keys each, E=128, 64-key pages in a
+    shuffled pool; four sequences checked against the oracle."""
+    B, Hq, Hkv, E, ps, S = 64, 32, 8, 128, 64, 32768
+    q, kc, vc, bt, ln = make_cache(B, Hq, Hkv, 1, E, ps, [S] * B, "bf16", seed=0, extra_pages=0)
+    out, lse = run(q, kc, vc, bt, ln, "bf16", enable_gqa=True)
+    for b in (0, 9, 31, 63):
+        ref = O.sdpa_paged(q[b:b + 1], kc, vc, bt[b:b + 1], ln[b:b + 1], enable_gqa=True)
+        check((out[b:b + 1], lse[b:b + 1]), ref, "bf16", f"sequence {b}")

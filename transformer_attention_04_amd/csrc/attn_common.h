@@ -66,6 +66,19 @@ struct DecodeParams {
     int keys_per_split; // multiple of 128
     int neg;
     float scale_log2;   // |scale| * log2(e)
+    // Paged cache (block_table non-null): k and v point at page pools with
+    // k_sb / v_sb = page stride, k_sh / v_sh = head stride, k_sr / v_sr = row
+    // stride; key j of sequence b is row j mod 2^page_shift of page
+    // block_table[b * bt_stride + (j >> page_shift)]; sequence b holds
+    // seq_lens[b] keys (clamped to S and to the table).  causal: the L new rows
+    // are the sequence's last L positions (bottom-right alignment).
+    const int* block_table;
+    const int* seq_lens;
+    int64_t bt_stride;
+    int page_shift;
+    int n_pages;
+    int max_blocks;
+    int causal;
 };
 
 // One call of the backward kernels (bf16 / fp16).  dsum is the float32

@@ -35,7 +35,7 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename Tr, int D, int NR>
+template <typename Tr, int D, int NR, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     constexpr int NKK = D / 32;   // k-steps of the 16x16x32 score product
     constexpr int NDC = D / 8;    // 16-byte chunks of a V row
@@ -56,9 +56,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int split = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
+    int seq = p.S;  // keys of this sequence
+    if (PAGED) seq = max(0, min(p.S, min(p.seq_lens[b], p.max_blocks << p.page_shift)));
     const int ks = split * p.keys_per_split;
-    const int ke = min(p.S, ks + p.keys_per_split);
+    const int ke = min(seq, ks + p.keys_per_split);
     const float c2 = p.scale_log2;
+    // Last key + 1 kept for this lane's query column: all of the split, or
+    // (paged, causal) up to the row's own position seq - L + i.
+    int lim = ke;
+    if (PAGED && p.causal && n < p.rows) lim = min(ke, seq - p.L + n / p.group + 1);
+    // Paged: lane l holds the page of the split's l-th block (the host keeps a
+    // split within 64 blocks).
+    int pgv = 0;
+    if (PAGED && ke > ks) {
+        const int pb0 = ks >> p.page_shift;
+        const int npg = ((ke - 1) >> p.page_shift) - pb0 + 1;
+        if (lane < npg) pgv = p.block_table[(int64_t)b * p.bt_stride + pb0 + lane];
+    }
 
     uint4 qreg[NKK];
     {
@@ -90,19 +104,51 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
     const auto kr = make_rsrc(kp + (int64_t)ks * p.k_sr, (nk - 1) * k_rs + D * 2);
     const auto vr = make_rsrc(vp + (int64_t)ks * p.v_sr, (nk - 1) * v_rs + D * 2);
-    auto load = [&](int key0, uint4 (&ka)[2][NKK], uint4 (&va)[8]) {
-        const int lk = key0 - ks;
+    // bad (paged): bit h set when keys key0 + 16h .. +15 include kept keys whose
+    // table entry lies outside the page pool; nothing is read for them.
+    auto load = [&](int key0, uint4 (&ka)[2][NKK], uint4 (&va)[8], int& bad) {
+        bad = 0;
+        if constexpr (!PAGED) {
+            const int lk = key0 - ks;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                ka[kb][kk] = buf_load16(kr, (lk + kb * 16 + n) * k_rs + (kk * 32 + grp * 8) * 2);
+                for (int kk = 0; kk < NKK; ++kk)
+                    ka[kb][kk] = buf_load16(kr, (lk + kb * 16 + n) * k_rs + (kk * 32 + grp * 8) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            va[i] = buf_load16(vr, n < NDC ? (lk + grp + 4 * i) * v_rs + n * 16 : 0x7ffffff0);
+            for (int i = 0; i < 8; ++i)
+                va[i] = buf_load16(vr, n < NDC ? (lk + grp + 4 * i) * v_rs + n * 16 : 0x7ffffff0);
+        } else {
+            // each half of the 32-key sub-tile lies in one page (pages hold >= 16 keys)
+            __amdgpu_buffer_rsrc_t krh[2], vrh[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k16 = key0 + 16 * h;
+                int nv = min(16, ke - k16);
+                const int slot = min(63, max(0, (k16 >> p.page_shift) - (ks >> p.page_shift)));
+                const int pg = __builtin_amdgcn_readlane(pgv, slot);
+                const bool okp = (unsigned)pg < (unsigned)p.n_pages;
+                if (!okp && nv > 0) bad |= 1 << h;
+                if (!okp) nv = 0;
+                const int64_t row0 = (int64_t)(okp ? pg : 0) * p.k_sb + (int64_t)kvh * p.k_sh +
+                                     (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.k_sr;
+                const int64_t vrow0 = (int64_t)(okp ? pg : 0) * p.v_sb + (int64_t)kvh * p.v_sh +
+                                      (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.v_sr;
+                krh[h] = make_rsrc((const uint16_t*)p.k + row0, (nv - 1) * k_rs + D * 2);
+                vrh[h] = make_rsrc((const uint16_t*)p.v + vrow0, (nv - 1) * v_rs + D * 2);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+                    ka[kb][kk] = buf_load16(krh[kb], n * k_rs + (kk * 32 + grp * 8) * 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                va[i] = buf_load16(vrh[i >> 2], n < NDC ? (grp + 4 * (i & 3)) * v_rs + n * 16 : 0x7ffffff0);
+        }
     };
     // One 32-key sub-tile: scores, online softmax, P V.
-    auto compute = [&](int key0, const uint4 (&ka)[2][NKK], const uint4 (&va)[8]) {
+    auto compute = [&](int key0, const uint4 (&ka)[2][NKK], const uint4 (&va)[8], int bad) {
         f32x4_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -117,7 +163,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (key0 + kb * 16 + grp * 4 + i >= ke) s[kb][i] = kNegInf;
+                const bool kept = key0 + kb * 16 + grp * 4 + i < lim;
+                if (!kept) s[kb][i] = kNegInf;
+                if (PAGED && ((bad >> kb) & 1) && kept) s[kb][i] = __builtin_nanf("");
                 mx = fmaxf(mx, s[kb][i]);
             }
         mx = fmaxf(mx, xor_lane(mx, 16));
@@ -132,7 +180,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int kl = kb * 16 + grp * 4 + i;
-                const float e = (key0 + kl < ke) ? fast_exp2(fmaf(s[kb][i], c2, -shift)) : 0.f;
+                const float e = (key0 + kl < lim) ? fast_exp2(fmaf(s[kb][i], c2, -shift)) : 0.f;
                 tsum += e;
                 if (n < NR) Pl[wave][kl * NR + n] = e;
             }
@@ -176,14 +224,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     // Each wavefront takes every fourth 32-key sub-tile; the next one's K and V
     // are in flight while the current one is computed.
     uint4 kaA[2][NKK], vaA[8], kaB[2][NKK], vaB[8];
+    int badA = 0, badB = 0;
     int key0 = ks + wave * 32;
-    if (key0 < ke) load(key0, kaA, vaA);
+    if (key0 < ke) load(key0, kaA, vaA, badA);
     for (; key0 < ke; key0 += 256) {
-        if (key0 + 128 < ke) load(key0 + 128, kaB, vaB);
-        compute(key0, kaA, vaA);
+        if (key0 + 128 < ke) load(key0 + 128, kaB, vaB, badB);
+        compute(key0, kaA, vaA, badA);
         if (key0 + 128 >= ke) break;
-        if (key0 + 256 < ke) load(key0 + 256, kaA, vaA);
-        compute(key0 + 128, kaB, vaB);
+        if (key0 + 256 < ke) load(key0 + 256, kaA, vaA, badA);
+        compute(key0 + 128, kaB, vaB, badB);
     }
 
     // Combine the 4 lane groups (same column chunk, different keys) ...
@@ -262,12 +311,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
 template <typename Tr, int D>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t s) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
-    if (p.rows <= 4)
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 4>), grid, dim3(256), 0, s, p);
-    else if (p.rows <= 8)
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 8>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 16>), grid, dim3(256), 0, s, p);
+    if (p.block_table) {
+        if (p.rows <= 4)
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 4, true>), grid, dim3(256), 0, s, p);
+        else if (p.rows <= 8)
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 8, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 16, true>), grid, dim3(256), 0, s, p);
+    } else if (p.rows <= 4) {
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 4, false>), grid, dim3(256), 0, s, p);
+    } else if (p.rows <= 8) {
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 8, false>), grid, dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 16, false>), grid, dim3(256), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nrows = (long long)p.B * p.Hq * p.L;

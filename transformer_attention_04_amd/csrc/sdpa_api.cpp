@@ -190,11 +190,85 @@ hipError_t launch_single_pass(sdpa_dtype dtype, const sdpa::AttnParams& p, int D
 
 size_t bwd_workspace_bytes(const Shapes& s) { return (size_t)(s.B * s.Hq * s.L) * sizeof(float) + 256; }
 
+// Shapes and launch plan of a paged-cache call (host only).
+struct PagedPlan {
+    int64_t B, Hq, Hkv, L, E, Ev, n_pages, page_size;
+    int page_shift;
+    Plan plan;
+};
+
+sdpa_status paged_plan(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* kc,
+                       const sdpa_tensor4* vc, int32_t max_seq_len, int enable_gqa, int num_splits,
+                       PagedPlan* out) {
+    if (dtype != SDPA_BF16 && dtype != SDPA_F16)
+        return fail(SDPA_ERR_UNSUPPORTED, "the paged-cache kernel takes bf16 or fp16");
+    if (!q || !kc || !vc) return fail(SDPA_ERR_INVALID_ARGUMENT, "q, k_cache and v_cache must not be NULL");
+    for (int d = 0; d < 4; ++d)
+        if (q->size[d] < 0 || kc->size[d] < 0 || vc->size[d] < 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    PagedPlan pp;
+    pp.B = q->size[0]; pp.Hq = q->size[1]; pp.L = q->size[2]; pp.E = q->size[3];
+    pp.n_pages = kc->size[0]; pp.Hkv = kc->size[1]; pp.page_size = kc->size[2]; pp.Ev = vc->size[3];
+    if (kc->size[3] != pp.E) return fail(SDPA_ERR_INVALID_ARGUMENT, "q and k_cache must share E");
+    if (vc->size[0] != pp.n_pages || vc->size[1] != pp.Hkv || vc->size[2] != pp.page_size)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must share pages, heads and page size");
+    if (pp.Hq != pp.Hkv) {
+        if (!enable_gqa)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query has %lld heads and the cache %lld: pass enable_gqa",
+                        (long long)pp.Hq, (long long)pp.Hkv);
+        if (pp.Hkv == 0 || pp.Hq % pp.Hkv != 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query heads must be a multiple of cache heads");
+    }
+    if (max_seq_len < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "max_seq_len must be non-negative");
+    int shift = 0;
+    while (shift < 30 && ((int64_t)1 << shift) < pp.page_size) ++shift;
+    if (pp.page_size < 16 || ((int64_t)1 << shift) != pp.page_size)
+        return fail(SDPA_ERR_UNSUPPORTED, "page_size must be a power of two >= 16 (got %lld)",
+                    (long long)pp.page_size);
+    pp.page_shift = shift;
+    const int64_t group = pp.Hkv > 0 ? pp.Hq / pp.Hkv : 1;
+    if (pp.L * group > sdpa::kDecodeMaxRows)
+        return fail(SDPA_ERR_UNSUPPORTED, "the paged-cache kernel takes L * Hq / Hkv <= %d new rows per cache head",
+                    sdpa::kDecodeMaxRows);
+    if (pp.E != pp.Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev");
+    if (!supported_head_dim(pp.E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim must be 64, 96 or 128");
+    // Splits as for the dense split-KV path (about 2048 workgroups), each a
+    // multiple of 128 keys spanning at most 64 pages (a split's pages sit in
+    // the 64 lanes of a wavefront).  At least one split, so that rows with no cached
+    // key still get output 0 and lse -inf from the merge.
+    if (num_splits < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits must be 0 or positive");
+    const int64_t quantum = sdpa::kDecodeKeyQuantum;
+    const int64_t S = max_seq_len;
+    int64_t splits = num_splits;
+    if (splits == 0) {
+        const int64_t units = pp.B * pp.Hkv > 0 ? pp.B * pp.Hkv : 1;
+        splits = (2048 + units - 1) / units;
+        const int64_t max_by_len = (S + 255) / 256;
+        if (splits > max_by_len) splits = max_by_len;
+        if (splits < 1) splits = 1;
+    }
+    int64_t per = S > 0 ? (S + splits - 1) / splits : quantum;
+    per = ((per + quantum - 1) / quantum) * quantum;
+    // 63 pages of keys: a split that starts inside a page then spans at most 64
+    const int64_t cap = (63 * pp.page_size / quantum) * quantum;
+    if (per > cap) per = cap;
+    if (per < quantum) per = quantum;
+    Plan pl;
+    pl.decode = true;
+    pl.n_splits = (int)(S > 0 ? (S + per - 1) / per : 1);
+    pl.keys_per_split = (int)per;
+    const int64_t nrow = pp.B * pp.Hq * pp.L * pl.n_splits;
+    pl.workspace = (size_t)(((nrow + 63) / 64) * 64 + nrow * pp.Ev) * sizeof(float) + 256;
+    pp.plan = pl;
+    *out = pp;
+    return SDPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 2; }
+int sdpa_abi_version(void) { return 3; }
 
 const char* sdpa_last_error(void) { return g_err; }
 
@@ -387,6 +461,87 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     hipError_t e = launch_single_pass(dtype, p, E, is_causal != 0, sdpa::MASK_NONE, true,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sdpa_status sdpa_fwd_paged_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q,
+                                          const sdpa_tensor4* k_cache, const sdpa_tensor4* v_cache,
+                                          int32_t max_seq_len, int enable_gqa, int num_splits,
+                                          size_t* bytes) {
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+    PagedPlan pp;
+    sdpa_status st = paged_plan(dtype, q, k_cache, v_cache, max_seq_len, enable_gqa, num_splits, &pp);
+    if (st != SDPA_OK) return st;
+    *bytes = pp.plan.workspace;
+    return ok();
+}
+
+sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k_cache,
+                           const sdpa_tensor4* v_cache, const int32_t* block_table, int64_t bt_stride,
+                           int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                           int is_causal, const double* scale, int enable_gqa,
+                           const sdpa_tensor4* out, const sdpa_tensor4* lse, void* workspace,
+                           size_t workspace_bytes, int num_splits, void* stream) {
+    PagedPlan pp;
+    sdpa_status st = paged_plan(dtype, q, k_cache, v_cache, max_seq_len, enable_gqa, num_splits, &pp);
+    if (st != SDPA_OK) return st;
+    if (!out || !lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "out and lse descriptors must not be NULL");
+    const int64_t want_o[4] = {pp.B, pp.Hq, pp.L, pp.Ev};
+    for (int d = 0; d < 4; ++d) {
+        if (out->size[d] != want_o[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "out must be (B, Hq, L, Ev)");
+        if (d < 3 && lse->size[d] != want_o[d]) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    }
+    if (lse->size[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
+    if (pp.B * pp.Hq * pp.L == 0) return ok();
+    if (max_blocks < 0 || bt_stride < max_blocks)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "need 0 <= max_blocks <= bt_stride");
+    if (!block_table || !seq_lens) return fail(SDPA_ERR_INVALID_ARGUMENT, "block_table and seq_lens must not be NULL");
+    if ((int64_t)max_blocks * pp.page_size > INT32_MAX || pp.n_pages > INT32_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "cache too large for 32-bit key indices");
+    const int eb = elem_bytes(dtype);
+    if ((st = check_vector_layout(*q, eb, "q")) != SDPA_OK) return st;
+    if (pp.n_pages > 0) {
+        if ((st = check_vector_layout(*k_cache, eb, "k_cache")) != SDPA_OK) return st;
+        if ((st = check_vector_layout(*v_cache, eb, "v_cache")) != SDPA_OK) return st;
+    }
+    if ((st = check_vector_layout(*out, eb, "out")) != SDPA_OK) return st;
+    if (!lse->data) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse data must not be NULL");
+    const int64_t lse_sr = lse->size[2] > 1 ? lse->stride[2] : 1;
+    if (lse_sr != 1) return fail(SDPA_ERR_UNSUPPORTED, "lse: the query dimension must have stride 1");
+    double sc;
+    if ((st = resolve_scale(scale, pp.E, &sc)) != SDPA_OK) return st;
+    if (pp.plan.workspace > workspace_bytes || !workspace)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes needed, %zu given",
+                    pp.plan.workspace, workspace_bytes);
+    sdpa::DecodeParams p{};
+    p.q = q->data; p.k = k_cache->data; p.v = v_cache->data; p.o = out->data; p.lse = (float*)lse->data;
+    float* ws = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    p.part_lse = ws;
+    const int64_t nrow = pp.B * pp.Hq * pp.L * pp.plan.n_splits;
+    p.part_o = ws + ((nrow + 63) / 64) * 64;
+    p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sr = q->stride[2];
+    p.k_sb = k_cache->stride[0]; p.k_sh = k_cache->stride[1]; p.k_sr = k_cache->stride[2];
+    p.v_sb = v_cache->stride[0]; p.v_sh = v_cache->stride[1]; p.v_sr = v_cache->stride[2];
+    p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_sr = out->stride[2];
+    p.lse_sb = lse->size[0] > 1 ? lse->stride[0] : 0;
+    p.lse_sh = lse->size[1] > 1 ? lse->stride[1] : 0;
+    p.B = (int)pp.B; p.Hq = (int)pp.Hq; p.Hkv = (int)pp.Hkv; p.group = (int)(pp.Hq / pp.Hkv);
+    p.L = (int)pp.L; p.S = max_seq_len;
+    p.rows = (int)(pp.L * p.group);
+    p.n_splits = pp.plan.n_splits;
+    p.keys_per_split = pp.plan.keys_per_split;
+    p.neg = sc < 0;
+    p.scale_log2 = (float)(std::fabs(sc) * 1.4426950408889634);
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.bt_stride = bt_stride;
+    p.page_shift = pp.page_shift;
+    p.n_pages = (int)pp.n_pages;
+    p.max_blocks = max_blocks;
+    p.causal = is_causal != 0;
+    hipError_t e = sdpa::launch_decode(p, dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16, (int)pp.E,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "paged decode launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -20,8 +20,9 @@ SDPA_OK, SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED, SDPA_ERR_DEVICE = 0, 1
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 _DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
 
-EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_bwd",
-            "sdpa_bwd_workspace_size", "sdpa_last_error", "sdpa_abi_version")
+EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_fwd_paged",
+            "sdpa_fwd_paged_workspace_size", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_last_error",
+            "sdpa_abi_version")
 
 
 class SdpaTensor4(ctypes.Structure):
@@ -68,6 +69,13 @@ def load_library():
                                     dbl, ctypes.c_int, ctypes.POINTER(dbl), ctypes.c_int,
                                     vp, i64, i64, vp, i64, vp]
     lib.sdpa_fwd_varlen.restype = ctypes.c_int
+    lib.sdpa_fwd_paged.argtypes = [ctypes.c_int, P, P, P, vp, i64, i32, vp, i32, ctypes.c_int,
+                                   ctypes.POINTER(dbl), ctypes.c_int, P, P, vp, ctypes.c_size_t,
+                                   ctypes.c_int, vp]
+    lib.sdpa_fwd_paged.restype = ctypes.c_int
+    lib.sdpa_fwd_paged_workspace_size.argtypes = [ctypes.c_int, P, P, P, i32, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.sdpa_fwd_paged_workspace_size.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [ctypes.c_int, P, P, P, P, P, P, ctypes.c_int, ctypes.POINTER(dbl),
                              ctypes.c_int, P, P, P, vp, ctypes.c_size_t, vp]
     lib.sdpa_bwd.restype = ctypes.c_int
@@ -212,6 +220,48 @@ def sdpa_fwd(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, 
                             int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), do, dl,
                             ws_ptr, nbytes.value, int(num_splits), _stream(dev)))
     return o4.reshape(*query.shape[:-1], Ev), l4.reshape(*query.shape[:-1])
+
+
+def sdpa_fwd_paged(query, k_cache, v_cache, block_table, seq_lens, max_seq_len=None, is_causal=False,
+                   scale=None, enable_gqa=False, num_splits=0, workspace=None):
+    """Attention of new rows against a paged key/value cache on the GPU.
+
+    query (B, Hq, L, E); k_cache / v_cache (n_pages, Hkv, page_size, E);
+    block_table (B, max_blocks) int32 and seq_lens (B,) int32 on the device;
+    ``max_seq_len`` bounds seq_lens (read from the device when None, which
+    synchronizes).  is_causal aligns the L new rows bottom-right.  Returns
+    (out (B, Hq, L, Ev), lse (B, Hq, L) float32).
+    """
+    lib = load_library()
+    _require_gpu(query, k_cache, v_cache, block_table, seq_lens)
+    if query.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != query.dtype \
+            or v_cache.dtype != query.dtype:
+        raise ValueError("the paged-cache kernel takes float16 or bfloat16 query and cache")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be a 2-D int32 tensor and seq_lens int32")
+    if block_table.stride(1) != 1:
+        block_table = block_table.contiguous()
+    seq_lens = seq_lens.contiguous()
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    B, Hq, L, E = query.shape
+    Ev = v_cache.shape[3]
+    dev = query.device
+    out = torch.empty((B, Hq, L, Ev), dtype=query.dtype, device=dev)
+    lse = torch.empty((B, Hq, L, 1), dtype=torch.float32, device=dev)
+    dq, dk, dv = _desc(query), _desc(k_cache), _desc(v_cache)
+    with torch.cuda.device(dev):
+        n = ctypes.c_size_t(0)
+        _check(lib.sdpa_fwd_paged_workspace_size(_DTYPE[query.dtype], dq, dk, dv, int(max_seq_len),
+                                                 int(bool(enable_gqa)), int(num_splits), ctypes.byref(n)))
+        if workspace is None or workspace.numel() < n.value:
+            workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        _check(lib.sdpa_fwd_paged(_DTYPE[query.dtype], dq, dk, dv, block_table.data_ptr(),
+                                  block_table.stride(0), block_table.shape[1], seq_lens.data_ptr(),
+                                  int(max_seq_len), int(bool(is_causal)), _scale_arg(scale),
+                                  int(bool(enable_gqa)), _desc(out), _desc(lse), workspace.data_ptr(),
+                                  n.value, int(num_splits), _stream(dev)))
+    return out, lse.reshape(B, Hq, L)
 
 
 def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
