@@ -7,7 +7,8 @@ sdpa_fwd call on the causal bf16 workload B=4, H=16, L=S=2048, E=128 (the
 headline configuration).  The JSON line reports its attention TFLOP/s with
 the matrix-core roofline of the prefill kernel, the CPU oracle timed on the
 host cores on a bounded sample of the same workload, and (under "secondary")
-the other workloads: split-KV GQA decode in GB/s against the HBM roofline,
+the other workloads: split-KV GQA decode in GB/s against the HBM roofline
+(dense, and with the cache in 64-key pages of a shuffled pool),
 the GPT-NeoX-shaped E=96 variants, packed variable-length fp16, the
 single-head fp32 case and the backward of the headline workload (5 products
 per kept pair: 10 E flops).
@@ -152,6 +153,36 @@ def bench_decode(steps, warmup, device="cuda"):
             "workspace_bytes": nws}
 
 
+def bench_paged(steps, warmup, device="cuda", page=64):
+    """The decode workload with its cache in 64-key pages of a shuffled pool,
+    read through a block table (sdpa_fwd_paged)."""
+    import torch
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    q, k, v = (t.to(device) for t in inputs.workload_inputs("bf16_gqa_decode"))
+    B, Hkv, Sk, E = k.shape
+    nb = Sk // page
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(B * nb, generator=g).to(device)
+    def pool(x):  # page j of sequence b goes to slot perm[b * nb + j]
+        pages = x.reshape(B, Hkv, nb, page, E).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, page, E)
+        out = torch.empty_like(pages)
+        out[perm] = pages
+        return out
+    kc, vc = pool(k), pool(v)
+    del k, v
+    bt = perm.reshape(B, nb).to(torch.int32)
+    lens = torch.full((B,), Sk, dtype=torch.int32, device=device)
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device=device)
+    fn = lambda: S.sdpa_fwd_paged(q, kc, vc, bt, lens, max_seq_len=Sk, enable_gqa=True, workspace=ws)
+    wall, per = time_launches(fn, steps, warmup)
+    out_numel = q.numel()
+    nbytes = 2 * (q.numel() + kc.numel() + vc.numel() + out_numel) + 4 * (q.numel() // E)
+    kern_ms = sum(per) / len(per)
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "bytes": nbytes,
+            "gbs": nbytes / (kern_ms * 1e-3) / 1e9, "frac_hbm": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def bench_varlen(steps, warmup, device="cuda"):
     from transformer_attention_04_amd import inputs
     from transformer_attention_04_amd import sdpa as S
@@ -196,7 +227,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | decode | neox | varlen | fp32 | bwd | copy (comma separated)")
+                    help="all | main | decode | paged | neox | varlen | fp32 | bwd | copy (comma separated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -228,6 +259,15 @@ def main(argv=None):
                                         "traffic": load_traffic("decode_split_kernel"),
                                         "kernels": "decode_split_kernel + decode_merge_kernel"}
         print(f"# bf16_gqa_decode: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    if run_all or "paged" in sel:
+        d = bench_paged(max(5, a.steps // 2), min(a.warmup, 5))
+        secondary["bf16_gqa_decode paged"] = {"metric": "GB/s", "value": round(d["gbs"], 1),
+                                              "frac_hbm_peak": round(d["frac_hbm"], 4),
+                                              "kernel_us": round(d["kernel_ms"] * 1e3, 1),
+                                              "bytes_per_call": d["bytes"], "page_size": 64,
+                                              "kernels": "decode_split_kernel (paged) + decode_merge_kernel"}
+        print(f"# bf16_gqa_decode paged: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr,
+              flush=True)
     if run_all or "neox" in sel:
         for tag, sc in (("1/sqrt96", None), ("1/96", 1 / 96), ("1.0", 1.0)):
             r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), scale=sc)
