@@ -354,3 +354,33 @@ def test_float_mask_same_result_on_both_kernels():
     assert_parity(o1, l1, ro, rl, "bf16", "aligned bias")
     assert_parity(o2, l2, ro, rl, "bf16", "unaligned bias")
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+
+
+# ------------------------------------------------------- xFormers layouts (strided views)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bmhk_and_bmghk_layouts(causal):
+    """BMHK (B, M, H, K) and the 5-D grouped-query BMGHK (B, M, G, Hq, K) with
+    key/value (B, M, G, 1, K) of the insureai360 tutorial (section 5), passed
+    to the kernels as strided views; parity with the oracle on the same values
+    laid out (B, heads, M, K)."""
+    B, M, G, Hq, K = 2, 256, 2, 4, 64
+    g = torch.Generator().manual_seed(55)
+    qg = torch.randn(B, M, G, Hq, K, generator=g).to(torch.float16)
+    kg = torch.randn(B, M, G, 1, K, generator=g).to(torch.float16)
+    vg = torch.randn(B, M, G, 1, K, generator=g).to(torch.float16)
+    out, lse = S.sdpa_fwd_bmhk(qg.to(DEV), kg.to(DEV), vg.to(DEV), is_causal=causal)
+    torch.cuda.synchronize()
+    assert out.shape == (B, M, G, Hq, K) and lse.shape == (B, G * Hq, M)
+    q4 = qg.reshape(B, M, G * Hq, K).permute(0, 2, 1, 3)
+    k4, v4 = kg[:, :, :, 0].permute(0, 2, 1, 3), vg[:, :, :, 0].permute(0, 2, 1, 3)
+    ro, rl = O.sdpa(q4, k4, v4, is_causal=causal, enable_gqa=True)
+    assert_parity(out.reshape(B, M, G * Hq, K).permute(0, 2, 1, 3), lse, ro, rl, "fp16", "BMGHK")
+    # 4-D BMHK, same heads for query and key/value
+    qh = torch.randn(B, M, 3, K, generator=g).to(torch.float16)
+    kh = torch.randn(B, 300, 3, K, generator=g).to(torch.float16)
+    vh = torch.randn(B, 300, 3, K, generator=g).to(torch.float16)
+    out, lse = S.sdpa_fwd_bmhk(qh.to(DEV), kh.to(DEV), vh.to(DEV), is_causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa(qh.permute(0, 2, 1, 3), kh.permute(0, 2, 1, 3), vh.permute(0, 2, 1, 3), is_causal=causal)
+    assert_parity(out.permute(0, 2, 1, 3), lse, ro, rl, "fp16", "BMHK")

@@ -310,6 +310,42 @@ def sdpa_bwd(query, key, value, out, lse, grad, is_causal=False, scale=None, ena
     return dq4.reshape(query.shape), dk4.reshape(key.shape), dv4.reshape(value.shape)
 
 
+def sdpa_fwd_bmhk(query, key, value, is_causal=False, scale=None, num_splits=0):
+    """Attention in the xFormers layouts of the insureai360 tutorial: BMHK
+    (B, M, H, K) with the sequence before the heads, or the 5-D grouped-query
+    BMGHK (B, M, G, Hq, K) with key/value (B, M, G, 1, K) shared by the Hq
+    query heads of each of the G groups (tutorial section 5).
+
+    No copies: the tensors are handed to sdpa_fwd as strided (B, heads, M, K)
+    views, query head g*Hq + j reading key/value head g (contiguous groups).
+    Returns the output in the query's layout and lse (B, heads, M) float32.
+    """
+    if query.dim() == 4:
+        q4, k4, v4 = (t.permute(0, 2, 1, 3) for t in (query, key, value))
+        gqa = q4.shape[1] != k4.shape[1]
+    elif query.dim() == 5:
+        B, M, G, Hq, K = query.shape
+        if key.dim() != 5 or key.shape[2] != G or key.shape[3] != 1 or value.shape[3] != 1:
+            raise ValueError("BMGHK: key and value must be (B, M, G, 1, K) with the query's G")
+        if query.stride(2) != Hq * query.stride(3):
+            raise ValueError("BMGHK: the group and head axes of the query must be packed (G outer)")
+        q4 = query.reshape(B, M, G * Hq, K).permute(0, 2, 1, 3) if query.is_contiguous() else \
+            query.as_strided((B, G * Hq, M, K), (query.stride(0), query.stride(3), query.stride(1), query.stride(4)))
+        k4 = key[:, :, :, 0].permute(0, 2, 1, 3)
+        v4 = value[:, :, :, 0].permute(0, 2, 1, 3)
+        gqa = Hq != 1
+    else:
+        raise ValueError("expected a 4-D BMHK or a 5-D BMGHK query")
+    B, H, M = q4.shape[:3]
+    Ev = v4.shape[3]
+    out = torch.empty(query.shape[:-1] + (Ev,), dtype=query.dtype, device=query.device)
+    o4 = out.permute(0, 2, 1, 3) if out.dim() == 4 else out.reshape(B, M, H, Ev).permute(0, 2, 1, 3)
+    lse = torch.empty((B, H, M, 1), dtype=torch.float32, device=query.device)
+    sdpa_fwd(q4, k4, v4, is_causal=is_causal, scale=scale, enable_gqa=gqa, num_splits=num_splits,
+             out=o4, lse=lse)
+    return out, lse.reshape(B, H, M)
+
+
 def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
                     dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False):
     """Packed variable-length attention with a block-diagonal (optionally causal) mask.
