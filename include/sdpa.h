@@ -29,7 +29,10 @@
  *  - Argument errors are detected on the host before anything is enqueued:
  *    the call returns a non-zero status and sdpa_last_error() describes it.
  *    No C++ exception crosses this interface.
- *  - Head dims supported by the kernels: E == Ev, E in {64, 96, 128}.
+ *  - Head dims supported by the kernels: E and Ev each in {64, 96, 128}.
+ *    E != Ev (value rows of another width than query/key rows, which the
+ *    operation allows) is handled for bf16/fp16 inputs without attn_mask by
+ *    sdpa_fwd; every other entry point and combination needs E == Ev.
  *    E = 0 (an empty score sum) is valid for the operation but not handled by
  *    the kernels: it returns SDPA_ERR_UNSUPPORTED.
  */

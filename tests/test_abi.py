@@ -109,8 +109,13 @@ def test_gqa_rules(lib):
 def test_unsupported_head_dims(lib):
     st, _ = call(lib, *qkv(E=80))
     assert st == S.SDPA_ERR_UNSUPPORTED
-    st, _ = call(lib, *qkv(E=64, Ev=128))
+    st, _ = call(lib, *qkv(E=64, Ev=80))
     assert st == S.SDPA_ERR_UNSUPPORTED
+    # E != Ev runs on the 16-bit kernels without a mask only
+    st, msg = call(lib, *qkv(E=64, Ev=128), dtype=S.SDPA_F32)
+    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
+    st, msg = call(lib, *qkv(E=128, Ev=64), mask=t4((1, 1, 16, 32)))
+    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
     st, _ = call(lib, *qkv(E=0))
     assert st == S.SDPA_ERR_UNSUPPORTED
 

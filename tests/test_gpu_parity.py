@@ -384,3 +384,22 @@ def test_bmhk_and_bmghk_layouts(causal):
     torch.cuda.synchronize()
     ro, rl = O.sdpa(qh.permute(0, 2, 1, 3), kh.permute(0, 2, 1, 3), vh.permute(0, 2, 1, 3), is_causal=causal)
     assert_parity(out.permute(0, 2, 1, 3), lse, ro, rl, "fp16", "BMHK")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E,Ev", [(64, 128), (128, 64), (96, 64), (64, 96), (96, 128), (128, 96)])
+def test_value_dim_differs(dtype, E, Ev):
+    """Value rows of another width than query/key rows (the operation's V is
+    (..., S, Ev)): the batched kernel over several tiles with ragged tails,
+    causal and not, with GQA; the split-KV decode over several splits."""
+    q, k, v = inputs.randn_qkv((2, 4, 200, E), (2, 2, 333, E), (2, 2, 333, Ev), dtype, seed=E + 3 * Ev)
+    for causal in (False, True):
+        r = run_both(q, k, v, dtype, is_causal=causal, enable_gqa=True)
+        assert r[0].shape == (2, 4, 200, Ev)
+        assert_parity(*r, dtype, f"E={E} Ev={Ev} causal={causal}")
+    r = run_both(q[:, :, :150], k, v, dtype, scale=-0.2, enable_gqa=True)
+    assert_parity(*r, dtype, f"E={E} Ev={Ev} negative scale")
+    qd, kd, vd = inputs.randn_qkv((3, 8, 1, E), (3, 2, 1000, E), (3, 2, 1000, Ev), dtype, seed=E * Ev)
+    for splits in (0, 3):
+        r = run_both(qd, kd, vd, dtype, enable_gqa=True, num_splits=splits)
+        assert_parity(*r, dtype, f"decode E={E} Ev={Ev} splits={splits}")

@@ -41,6 +41,7 @@ struct AttnParams {
     int n_qtiles;
     int mask_vec;           // mask rows are 16-byte aligned (vector loads allowed)
     int neg;                // the scale is negative: q is negated on load
+    int dv;                 // value head dim Ev (== E except on the four-wave batched path)
     float scale_abs;        // |scale|
     float scale_log2;       // |scale| * log2(e)
     float scale;            // signed scale (fp32 kernel)
@@ -79,6 +80,7 @@ struct DecodeParams {
     int n_pages;
     int max_blocks;
     int causal;
+    int dv;             // value head dim Ev (dense cache: may differ from E)
 };
 
 // One call of the backward kernels (bf16 / fp16).  dsum is the float32

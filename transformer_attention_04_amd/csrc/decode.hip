@@ -35,16 +35,16 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename Tr, int D, int NR, bool PAGED>
+template <typename Tr, int D, int DV, int NR, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     constexpr int NKK = D / 32;   // k-steps of the 16x16x32 score product
-    constexpr int NDC = D / 8;    // 16-byte chunks of a V row
+    constexpr int NDC = DV / 8;   // 16-byte chunks of a V row
     static_assert(NDC <= 16, "one chunk per lane of a 16-lane group");
     static_assert(NR % 4 == 0 && NR <= 16, "rows padded to 4, 8 or 16");
 
     __shared__ __attribute__((aligned(16))) float Pl[4][32 * NR];
     __shared__ __attribute__((aligned(16))) float Al[4][NR];
-    __shared__ __attribute__((aligned(16))) float Ow[4][NR * D];
+    __shared__ __attribute__((aligned(16))) float Ow[4][NR * DV];
     __shared__ float Mw[4][NR];
     __shared__ float Lw[4][NR];
 
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int nk = max(ke - ks, 0);
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
     const auto kr = make_rsrc(kp + (int64_t)ks * p.k_sr, (nk - 1) * k_rs + D * 2);
-    const auto vr = make_rsrc(vp + (int64_t)ks * p.v_sr, (nk - 1) * v_rs + D * 2);
+    const auto vr = make_rsrc(vp + (int64_t)ks * p.v_sr, (nk - 1) * v_rs + DV * 2);
     // bad (paged): bit h set when keys key0 + 16h .. +15 include kept keys whose
     // table entry lies outside the page pool; nothing is read for them.
     auto load = [&](int key0, uint4 (&ka)[2][NKK], uint4 (&va)[8], int& bad) {
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 const int64_t vrow0 = (int64_t)(okp ? pg : 0) * p.v_sb + (int64_t)kvh * p.v_sh +
                                       (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.v_sr;
                 krh[h] = make_rsrc((const uint16_t*)p.k + row0, (nv - 1) * k_rs + D * 2);
-                vrh[h] = make_rsrc((const uint16_t*)p.v + vrow0, (nv - 1) * v_rs + D * 2);
+                vrh[h] = make_rsrc((const uint16_t*)p.v + vrow0, (nv - 1) * v_rs + DV * 2);
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
             for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) Ow[wave][r * D + n * 8 + e] = acc[r][e];
+                for (int e = 0; e < 8; ++e) Ow[wave][r * DV + n * 8 + e] = acc[r][e];
         }
         if (n < NR) {
             Mw[wave][n] = m_run;
@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     __syncthreads();
 
     // ... then the 4 wavefronts, into one normalised partial per query row.
-    for (int idx = tid; idx < p.rows * D; idx += 256) {
-        const int r = idx / D, d = idx % D;
+    for (int idx = tid; idx < p.rows * DV; idx += 256) {
+        const int r = idx / DV, d = idx % DV;
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < 4; ++w) M = fmaxf(M, Mw[w][r]);
@@ -273,12 +273,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int w = 0; w < 4; ++w) {
             const float a = (Mw[w][r] == kNegInf) ? 0.f : fast_exp2(Mw[w][r] * c2 - shift);
             L = fmaf(a, Lw[w][r], L);
-            o = fmaf(a, Ow[w][r * D + d], o);
+            o = fmaf(a, Ow[w][r * DV + d], o);
         }
         const int i = r / p.group, g = r % p.group;
         const int hq = kvh * p.group + g;
         const int64_t prow = (((int64_t)b * p.Hq + hq) * p.L + i) * p.n_splits + split;
-        p.part_o[prow * D + d] = (L == 0.f) ? 0.f : o / L;
+        p.part_o[prow * DV + d] = (L == 0.f) ? 0.f : o / L;
         if (d == 0) p.part_lse[prow] = (L == 0.f) ? kNegInf : (shift + fast_log2(L)) * kLn2;
     }
 }
@@ -308,36 +308,52 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
             (W == 0.f) ? kNegInf : fmaf(fast_log2(W), kLn2, shift);
 }
 
-template <typename Tr, int D>
+template <typename Tr, int D, int DV>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t s) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
-    if (p.block_table) {
-        if (p.rows <= 4)
-            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 4, true>), grid, dim3(256), 0, s, p);
-        else if (p.rows <= 8)
-            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 8, true>), grid, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((decode_split_kernel<Tr, D, 16, true>), grid, dim3(256), 0, s, p);
-    } else if (p.rows <= 4) {
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 4, false>), grid, dim3(256), 0, s, p);
-    } else if (p.rows <= 8) {
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 8, false>), grid, dim3(256), 0, s, p);
+    if constexpr (D == DV) {
+        if (p.block_table) {
+            if (p.rows <= 4)
+                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 4, true>), grid, dim3(256), 0, s, p);
+            else if (p.rows <= 8)
+                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 8, true>), grid, dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 16, true>), grid, dim3(256), 0, s, p);
+            goto merge;
+        }
     } else {
-        hipLaunchKernelGGL((decode_split_kernel<Tr, D, 16, false>), grid, dim3(256), 0, s, p);
+        if (p.block_table) return hipErrorInvalidValue;  // paged caches have E == Ev
     }
+    if (p.rows <= 4)
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 4, false>), grid, dim3(256), 0, s, p);
+    else if (p.rows <= 8)
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 8, false>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 16, false>), grid, dim3(256), 0, s, p);
+merge:
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nrows = (long long)p.B * p.Hq * p.L;
-    hipLaunchKernelGGL((decode_merge_kernel<Tr, D>), dim3((unsigned)nrows), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((decode_merge_kernel<Tr, DV>), dim3((unsigned)nrows), dim3(64), 0, s, p);
     return hipGetLastError();
+}
+
+template <typename Tr, int D>
+static hipError_t launch_decode_dv(const DecodeParams& p, hipStream_t s) {
+    switch (p.dv) {
+        case 64: return launch_decode_d<Tr, D, 64>(p, s);
+        case 96: return launch_decode_d<Tr, D, 96>(p, s);
+        case 128: return launch_decode_d<Tr, D, 128>(p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename Tr>
 static hipError_t launch_decode_t(const DecodeParams& p, int D, hipStream_t s) {
     switch (D) {
-        case 64: return launch_decode_d<Tr, 64>(p, s);
-        case 96: return launch_decode_d<Tr, 96>(p, s);
-        case 128: return launch_decode_d<Tr, 128>(p, s);
+        case 64: return launch_decode_dv<Tr, 64>(p, s);
+        case 96: return launch_decode_dv<Tr, 96>(p, s);
+        case 128: return launch_decode_dv<Tr, 128>(p, s);
     }
     return hipErrorInvalidValue;
 }

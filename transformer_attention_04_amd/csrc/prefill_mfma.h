@@ -58,7 +58,7 @@
 
 namespace sdpa {
 
-template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(AttnParams p) {
     constexpr int BM = kPrefillBlockM;
@@ -66,14 +66,14 @@ void prefill_mfma_kernel(AttnParams p) {
     constexpr int KS = D + 8;      // LDS row stride of the K tile, in 16-bit words
     constexpr int VS = BN + 8;     // LDS row stride of the V^T tile
     constexpr int KTILE = BN * KS;
-    constexpr int VTILE = D * VS;
+    constexpr int VTILE = DV * VS;
     constexpr int STAGE = KTILE + VTILE;
     constexpr int NKK = D / 16;    // k-steps of the score product
-    constexpr int NDB = D / 32;    // 32-row blocks of O^T
+    constexpr int NDB = DV / 32;   // 32-row blocks of O^T
     constexpr int KCH = BN * D / 8;          // 16-byte chunks of a K tile
     constexpr int KCH_T = KCH / 256;         // per thread
-    constexpr int VIT = (D / 8) * (BN / 4);  // V items: 8 columns x 4 keys
-    static_assert(D % 32 == 0 && KCH % 256 == 0, "head dim must be a multiple of 32");
+    constexpr int VIT = (DV / 8) * (BN / 4);  // V items: 8 columns x 4 keys
+    static_assert(D % 32 == 0 && DV % 32 == 0 && KCH % 256 == 0, "head dims must be multiples of 32");
     static_assert(VIT <= 256, "one V item per thread");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -148,7 +148,7 @@ void prefill_mfma_kernel(AttnParams p) {
     auto load_tile = [&](int key0) {
         const int rows = min(BN, Sb - key0);
         const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
-        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + D * 2);
+        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + DV * 2);
 #pragma unroll
         for (int i = 0; i < KCH_T; ++i) {
             const int c = tid + 256 * i;
@@ -367,7 +367,7 @@ void prefill_mfma_kernel(AttnParams p) {
     const float l_tot = pair32_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const int o_rs = (int)(p.o_sr * 2);
-    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + D * 2);
+    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + DV * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -385,24 +385,43 @@ void prefill_mfma_kernel(AttnParams p) {
     }
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN>
 hipError_t launch_prefill_one(const AttnParams& p, hipStream_t stream) {
     const long long grid = (long long)p.n_qtiles * p.Hq * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, DV, CAUSAL, MASK, VARLEN>), dim3((unsigned)grid),
                        dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+// Value head dim DV != D: the four-wave kernel, unmasked batched calls only.
+template <typename Tr, int D>
+hipError_t launch_prefill_dv(const AttnParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
+    if (mask != MASK_NONE || varlen) return hipErrorInvalidValue;
+    switch (p.dv) {
+        case 64: if constexpr (D != 64) return causal ? launch_prefill_one<Tr, D, 64, true, MASK_NONE, false>(p, s)
+                                                      : launch_prefill_one<Tr, D, 64, false, MASK_NONE, false>(p, s);
+                 break;
+        case 96: if constexpr (D != 96) return causal ? launch_prefill_one<Tr, D, 96, true, MASK_NONE, false>(p, s)
+                                                      : launch_prefill_one<Tr, D, 96, false, MASK_NONE, false>(p, s);
+                 break;
+        case 128: if constexpr (D != 128) return causal ? launch_prefill_one<Tr, D, 128, true, MASK_NONE, false>(p, s)
+                                                        : launch_prefill_one<Tr, D, 128, false, MASK_NONE, false>(p, s);
+                  break;
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename Tr, int D>
 hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool varlen,
                             hipStream_t s) {
+    if (p.dv != D) return launch_prefill_dv<Tr, D>(p, causal, mask, varlen, s);
     if (varlen) {
         // packed segments keep the 128-row kernel: 256-row tiles waste more
         // rows on short segments
         if (mask != MASK_NONE) return hipErrorInvalidValue;
-        return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, true>(p, s)
-                      : launch_prefill_one<Tr, D, false, MASK_NONE, true>(p, s);
+        return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, true>(p, s)
+                      : launch_prefill_one<Tr, D, D, false, MASK_NONE, true>(p, s);
     }
     switch (mask) {
         case MASK_NONE:
@@ -411,18 +430,18 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
             if (p.scale_log2 > 0.f)
                 return causal ? launch_prefill_pp<Tr, D, true>(p, s)
                               : launch_prefill_pp<Tr, D, false>(p, s);
-            return causal ? launch_prefill_one<Tr, D, true, MASK_NONE, false>(p, s)
-                          : launch_prefill_one<Tr, D, false, MASK_NONE, false>(p, s);
+            return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, false>(p, s)
+                          : launch_prefill_one<Tr, D, D, false, MASK_NONE, false>(p, s);
         case MASK_FLOAT:
             // the eight-wave kernel moves the bias with 16-byte loads
             if (p.mask_vec)
                 return causal ? launch_prefill_pp<Tr, D, true, MASK_FLOAT>(p, s)
                               : launch_prefill_pp<Tr, D, false, MASK_FLOAT>(p, s);
-            return causal ? launch_prefill_one<Tr, D, true, MASK_FLOAT, false>(p, s)
-                          : launch_prefill_one<Tr, D, false, MASK_FLOAT, false>(p, s);
+            return causal ? launch_prefill_one<Tr, D, D, true, MASK_FLOAT, false>(p, s)
+                          : launch_prefill_one<Tr, D, D, false, MASK_FLOAT, false>(p, s);
         case MASK_BOOL:
-            return causal ? launch_prefill_one<Tr, D, true, MASK_BOOL, false>(p, s)
-                          : launch_prefill_one<Tr, D, false, MASK_BOOL, false>(p, s);
+            return causal ? launch_prefill_one<Tr, D, D, true, MASK_BOOL, false>(p, s)
+                          : launch_prefill_one<Tr, D, D, false, MASK_BOOL, false>(p, s);
     }
     return hipErrorInvalidValue;
 }

@@ -310,11 +310,13 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
     if (s.B * s.Hq * s.L == 0) return ok();  // nothing to compute
-    if (s.E != s.Ev)
-        return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %lld and %lld)", (long long)s.E,
+    if (!supported_head_dim(s.E) || !supported_head_dim(s.Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be one of 64, 96, 128",
+                    (long long)s.E, (long long)s.Ev);
+    if (s.E != s.Ev && (dtype == SDPA_F32 || attn_mask))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "E != Ev (%lld and %lld) needs bf16/fp16 inputs and no attn_mask", (long long)s.E,
                     (long long)s.Ev);
-    if (!supported_head_dim(s.E))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not one of 64, 96, 128", (long long)s.E);
     const int eb = elem_bytes(dtype);
     if ((st = check_vector_layout(*q, eb, "q")) != SDPA_OK) return st;
     if (s.S > 0) {
@@ -358,6 +360,7 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
         p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
         p.L = (int)s.L; p.S = (int)s.S;
         p.rows = (int)(s.L * p.group);
+        p.dv = (int)s.Ev;
         p.n_splits = pl.n_splits;
         p.keys_per_split = pl.keys_per_split;
         p.neg = sc < 0;
@@ -390,6 +393,7 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     }
     p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
     p.L = (int)s.L; p.S = (int)s.S;
+    p.dv = (int)s.Ev;
     const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
     p.n_qtiles = (int)((s.L + bm - 1) / bm);
     fill_scale(p, sc);
@@ -455,6 +459,7 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     p.total_q = total_q; p.total_k = total_k;
     p.B = n_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
     p.L = max_seqlen_q; p.S = max_seqlen_k;
+    p.dv = Ev;
     const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
     p.n_qtiles = (max_seqlen_q + bm - 1) / bm;
     fill_scale(p, sc);
@@ -528,6 +533,7 @@ sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_t
     p.B = (int)pp.B; p.Hq = (int)pp.Hq; p.Hkv = (int)pp.Hkv; p.group = (int)(pp.Hq / pp.Hkv);
     p.L = (int)pp.L; p.S = max_seq_len;
     p.rows = (int)(pp.L * p.group);
+    p.dv = (int)pp.Ev;
     p.n_splits = pp.plan.n_splits;
     p.keys_per_split = pp.plan.keys_per_split;
     p.neg = sc < 0;
