@@ -183,6 +183,35 @@ def bench_paged(steps, warmup, device="cuda", page=64):
             "gbs": nbytes / (kern_ms * 1e-3) / 1e9, "frac_hbm": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+CHUNKED = dict(B=8, Hq=32, Hkv=8, E=128, L=512, S=4096, page=64, seed=11)
+
+
+def bench_chunked(steps, warmup, device="cuda"):
+    """Chunked prefill against a paged cache: 8 sequences of 4096 cached keys
+    (bf16, 64-key pages in a shuffled pool) whose last 512 positions are the new
+    rows, Hq=32 over Hkv=8, E=128, causal aligned bottom-right."""
+    import torch
+    from transformer_attention_04_amd import inputs
+    from transformer_attention_04_amd import sdpa as S
+    c = CHUNKED
+    nb = c["S"] // c["page"]
+    n_pages = c["B"] * nb
+    q, kc, vc = (t.to(device) for t in inputs.randn_qkv(
+        (c["B"], c["Hq"], c["L"], c["E"]), (n_pages, c["Hkv"], c["page"], c["E"]),
+        (n_pages, c["Hkv"], c["page"], c["E"]), "bf16", seed=c["seed"]))
+    g = torch.Generator().manual_seed(c["seed"] + 1)
+    bt = torch.randperm(n_pages, generator=g).reshape(c["B"], nb).to(torch.int32).to(device)
+    lens = torch.full((c["B"],), c["S"], dtype=torch.int32, device=device)
+    fn = lambda: S.sdpa_fwd_paged(q, kc, vc, bt, lens, max_seq_len=c["S"], is_causal=True, enable_gqa=True)
+    wall, per = time_launches(fn, steps, warmup)
+    L, Sk = c["L"], c["S"]
+    pairs = L * (Sk - L) + L * (L + 1) // 2
+    flops = 4 * c["E"] * pairs * c["B"] * c["Hq"]
+    kern_ms = sum(per) / len(per)
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kern_ms, "flops": flops,
+            "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12}
+
+
 def bench_varlen(steps, warmup, device="cuda"):
     from transformer_attention_04_amd import inputs
     from transformer_attention_04_amd import sdpa as S
@@ -227,7 +256,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workloads", default="all",
-                    help="all | main | decode | paged | neox | varlen | fp32 | bwd | copy (comma separated)")
+                    help="all | main | decode | paged | chunked | neox | varlen | fp32 | bwd | copy (comma separated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -268,6 +297,16 @@ def main(argv=None):
                                               "kernels": "decode_split_kernel (paged) + decode_merge_kernel"}
         print(f"# bf16_gqa_decode paged: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr,
               flush=True)
+    if run_all or "chunked" in sel:
+        r = bench_chunked(max(5, a.steps // 4), min(a.warmup, 5))
+        secondary["bf16 chunked prefill paged"] = {
+            "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+            "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "kernel_us": round(r["kernel_ms"] * 1e3, 1), "flop_per_call": r["flops"],
+            "shape": "B=8 Hq=32 Hkv=8 E=128, 512 new rows on 4096 cached keys, 64-key pages, causal",
+            "kernels": "prefill_mfma_kernel (paged)"}
+        print(f"# chunked prefill paged: {r['kernel_ms'] * 1e3:.1f} us, {r['kernel_tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
     if run_all or "neox" in sel:
         for tag, sc in (("1/sqrt96", None), ("1/96", 1 / 96), ("1.0", 1.0)):
             r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), scale=sc)

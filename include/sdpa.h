@@ -158,13 +158,17 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
                             void* stream);
 
 /*
- * sdpa_fwd_paged -- attention of a few new query rows per sequence against a
- * paged key/value cache (the serving layout of vLLM-style engines the pages
- * mention): the cached keys of a sequence live in fixed-size pages of a shared
- * pool, listed in order by the sequence's row of a block table.
+ * sdpa_fwd_paged -- attention of new query rows against a paged key/value
+ * cache (the serving layout of vLLM-style engines the pages mention): the
+ * cached keys of a sequence live in fixed-size pages of a shared pool, listed
+ * in order by the sequence's row of a block table.  Decode steps (L * Hq / Hkv
+ * <= 16 rows per cache head) run the split-KV kernel and its merge; longer
+ * chunks of new rows (chunked prefill) run the single-pass kernel, which reads
+ * the pages itself and needs no workspace.
  *
  *   dtype       SDPA_BF16 or SDPA_F16.
- *   q           (B, Hq, L, E): the new rows; L * Hq / Hkv <= 16.
+ *   q           (B, Hq, L, E): the new rows of each sequence (the same L for
+ *               every sequence).
  *   k_cache     (n_pages, Hkv, page_size, E), v_cache (n_pages, Hkv, page_size, Ev):
  *               the page pool; page_size a power of two >= 16; E == Ev in
  *               {64, 96, 128}.
@@ -180,8 +184,10 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
  *               j <= n - L + i (bottom-right alignment); with L = 1 it keeps
  *               every cached key.
  *   scale, enable_gqa, out (B, Hq, L, Ev), lse (B, Hq, L, 1) float32,
- *   workspace (size from sdpa_fwd_paged_workspace_size), num_splits (0 auto,
- *   k >= 1 splits) and stream: as for sdpa_fwd.
+ *   workspace (size from sdpa_fwd_paged_workspace_size; 0 bytes, and NULL
+ *   allowed, for chunked prefill), num_splits (0 auto, k >= 1 splits; only
+ *   with L * Hq / Hkv <= 16, else SDPA_ERR_UNSUPPORTED) and stream: as for
+ *   sdpa_fwd.
  *
  * A table entry outside [0, n_pages) for a kept key is never dereferenced:
  * the rows that would read it come out NaN (output and lse) instead of

@@ -202,3 +202,28 @@ def test_binding_refuses_cpu_tensors():
         pytest.skip("libsdpa.so is not built")
     with pytest.raises(ValueError, match="GPU"):
         S.sdpa_fwd(q, q, q)
+
+
+def test_paged_plan_rules(lib):
+    """sdpa_fwd_paged_workspace_size (host only): decode steps get a split-KV
+    workspace, longer chunks of new rows (chunked prefill) need none and take no
+    split count; page size, head dims and dtype are checked."""
+    def ws(L=1, Hq=8, Hkv=2, E=128, Ev=128, ps=64, dtype=S.SDPA_BF16, splits=0, max_len=4096):
+        q, kc, vc = t4((4, Hq, L, E)), t4((100, Hkv, ps, E)), t4((100, Hkv, ps, Ev))
+        n = ctypes.c_size_t(12345)
+        st = lib.sdpa_fwd_paged_workspace_size(dtype, ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc),
+                                               max_len, 1, splits, ctypes.byref(n))
+        return st, n.value
+    st, n = ws(L=4)                        # 16 rows per cache head: split-KV decode
+    assert st == S.SDPA_OK and n > 4 * 8 * 4 * 128 * 4
+    st, n = ws(L=5)                        # 20 rows: chunked prefill, no workspace
+    assert st == S.SDPA_OK and n == 0
+    st, n = ws(L=512, Hq=32, Hkv=8)
+    assert st == S.SDPA_OK and n == 0
+    assert ws(L=512, splits=2)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(L=4, splits=2)[0] == S.SDPA_OK
+    assert ws(ps=48)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(ps=8)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(E=64, Ev=128)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(dtype=S.SDPA_F32)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(splits=-1)[0] == S.SDPA_ERR_INVALID_ARGUMENT

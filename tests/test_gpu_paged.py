@@ -1,10 +1,12 @@
-"""Parity of the paged-cache decode (sdpa_fwd_paged, through the C interface)
-with the float64 oracle (oracle.sdpa_paged) on the same bf16/fp16 values.
+"""Parity of attention against a paged key/value cache (sdpa_fwd_paged, through
+the C interface) with the float64 oracle (oracle.sdpa_paged) on the same
+bf16/fp16 values: decode steps (split-KV kernel) and chunks of many new rows
+(chunked prefill, single-pass kernel).
 
 Bars as for the forward: max |GPU - oracle| <= 2e-2 on the output and 1e-3 on
 lse for bf16 / fp16.  Inputs: a shuffled page pool, ragged cached lengths
-(0, 1, page and split boundaries), GQA, bottom-right causal for several new
-rows, and table entries outside the pool.
+(0, 1, page, tile and split boundaries, fewer cached keys than new rows), GQA,
+bottom-right causal, and table entries outside the pool.
 """
 import numpy as np
 import pytest
@@ -104,3 +106,57 @@ def test_paged_full_decode_shape_sampled():
     for b in (0, 9, 31, 63):
         ref = O.sdpa_paged(q[b:b + 1], kc, vc, bt[b:b + 1], ln[b:b + 1], enable_gqa=True)
         check((out[b:b + 1], lse[b:b + 1]), ref, "bf16", f"sequence {b}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [64, 96, 128])
+@pytest.mark.parametrize("ps", [16, 64, 256])
+def test_paged_chunked_prefill(dtype, E, ps):
+    """200 new rows per sequence (two query tiles, the second ragged) against
+    ragged cached lengths, some shorter than the chunk (causal rows before the
+    cache's first key keep nothing)."""
+    lens = [0, 100, 200, 201, 333, 700, 1000]
+    q, kc, vc, bt, ln = make_cache(len(lens), 8, 2, 200, E, ps, lens, dtype, seed=E + ps + 1)
+    for causal in (False, True):
+        ref = O.sdpa_paged(q, kc, vc, bt, ln, is_causal=causal, enable_gqa=True)
+        check(run(q, kc, vc, bt, ln, dtype, is_causal=causal, enable_gqa=True), ref, dtype,
+              f"E={E} ps={ps} causal={causal}")
+
+
+def test_paged_chunked_prefill_no_gqa_and_scale():
+    lens = [37, 64, 65, 300]
+    q, kc, vc, bt, ln = make_cache(len(lens), 2, 2, 40, 128, 32, lens, "bf16", seed=77)
+    for scale in (-0.3, 1.0):
+        ref = O.sdpa_paged(q, kc, vc, bt, ln, is_causal=True, scale=scale)
+        check(run(q, kc, vc, bt, ln, "bf16", is_causal=True, scale=scale), ref, "bf16", f"scale={scale}")
+
+
+def test_paged_chunked_prefill_bad_table_entry():
+    """A page outside the pool at keys 240..255 of sequence 1: causal rows that
+    keep those keys are NaN, earlier rows and sequence 0 are unaffected."""
+    lens = [300, 300]
+    q, kc, vc, bt, ln = make_cache(2, 4, 2, 100, 64, 16, lens, "fp16", seed=91)
+    bad = bt.clone()
+    bad[1, 15] = kc.shape[0] + 3
+    out, lse = run(q, kc, vc, bad, ln, "fp16", is_causal=True, enable_gqa=True)
+    # row i keeps keys <= 200 + i: rows 40.. keep the bad block
+    assert np.isnan(out[1, :, 40:]).all() and np.isnan(lse[1, :, 40:]).all()
+    ref = O.sdpa_paged(q, kc, vc, bt, ln, is_causal=True, enable_gqa=True)
+    check((out[:1], lse[:1]), (ref[0][:1], ref[1][:1]), "fp16", "good sequence")
+    check((out[1:, :, :40], lse[1:, :, :40]), (ref[0][1:, :, :40], ref[1][1:, :, :40]), "fp16",
+          "rows before the bad block")
+
+
+def test_paged_chunked_prefill_full_shape_sampled():
+    """B=8 sequences of 4096 cached keys whose last 512 are the new chunk,
+    Hq=32, Hkv=8, E=128, 64-key pages in a shuffled pool, causal; query heads
+    of the first and last cache head of three sequences checked."""
+    B, Hq, Hkv, E, ps, S, L = 8, 32, 8, 128, 64, 4096, 512
+    q, kc, vc, bt, ln = make_cache(B, Hq, Hkv, L, E, ps, [S] * B, "bf16", seed=5, extra_pages=0)
+    out, lse = run(q, kc, vc, bt, ln, "bf16", is_causal=True, enable_gqa=True)
+    for b in (0, 3, 7):
+        for g in (0, Hkv - 1):
+            hs = slice(4 * g, 4 * g + 4)
+            ref = O.sdpa_paged(q[b:b + 1, hs], kc[:, g:g + 1], vc[:, g:g + 1], bt[b:b + 1], ln[b:b + 1],
+                               is_causal=True, enable_gqa=True)
+            check((out[b:b + 1, hs], lse[b:b + 1, hs]), ref, "bf16", f"sequence {b} cache head {g}")

@@ -45,6 +45,18 @@ struct AttnParams {
     float scale_abs;        // |scale|
     float scale_log2;       // |scale| * log2(e)
     float scale;            // signed scale (fp32 kernel)
+    // Paged key/value cache (block_table non-null; unmasked batched queries):
+    // k_sb / v_sb = page stride, k_sh / v_sh = head stride, k_sr / v_sr = row
+    // stride; key j of sequence b is row j mod 2^page_shift of page
+    // block_table[b * bt_stride + (j >> page_shift)].  Sequence b holds
+    // min(seq_lens[b], S, max_blocks << page_shift) keys, and its L query rows
+    // are its last L positions (causal aligns bottom-right).
+    const int* block_table;
+    const int* seq_lens;
+    int64_t bt_stride;
+    int page_shift;
+    int n_pages;
+    int max_blocks;
 };
 
 // One launch of the split-KV decode kernel and of its merge pass.

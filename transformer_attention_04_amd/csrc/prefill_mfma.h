@@ -58,7 +58,7 @@
 
 namespace sdpa {
 
-template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(AttnParams p) {
     constexpr int BM = kPrefillBlockM;
@@ -105,6 +105,15 @@ void prefill_mfma_kernel(AttnParams p) {
         vo = c * p.v_sr + (int64_t)kvh * p.v_sh;
         oo = a * p.o_sr + (int64_t)h * p.o_sh;
         lo = (int64_t)h * p.lse_sh + a;
+    } else if (PAGED) {
+        // keys of sequence b come page by page from the pool (offsets per tile)
+        Lb = p.L;
+        Sb = min(max(p.seq_lens[b], 0), min(p.S, p.max_blocks << p.page_shift));
+        qo = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+        ko = (int64_t)kvh * p.k_sh;
+        vo = (int64_t)kvh * p.v_sh;
+        oo = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+        lo = (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
     } else {
         Lb = p.L;
         Sb = p.S;
@@ -117,8 +126,11 @@ void prefill_mfma_kernel(AttnParams p) {
     }
     const int q0 = qt * BM;
     if (q0 >= Lb) return;
-    const int kend = CAUSAL ? min(Sb, min(q0 + BM, Lb)) : Sb;
-    const int ntiles = (kend + BN - 1) / BN;
+    // causal: row i keeps key j <= i + coff (top-left, except bottom-right on a
+    // paged cache, where the rows are the sequence's last Lb positions)
+    const int coff = PAGED ? Sb - Lb : 0;
+    const int kend = CAUSAL ? min(Sb, min(q0 + BM, Lb) + coff) : Sb;
+    const int ntiles = ((PAGED ? max(kend, 0) : kend) + BN - 1) / BN;
     const int qrows = min(BM, Lb - q0);   // valid rows of this block
     const int wrow0 = wave * 32;          // first local row of this wavefront
     const int lrow = wrow0 + lq;          // local row this lane owns
@@ -142,10 +154,49 @@ void prefill_mfma_kernel(AttnParams p) {
     const uint16_t* vbase = (const uint16_t*)p.v + vo;
     const int k_rs = (int)(p.k_sr * 2);
     const int v_rs = (int)(p.v_sr * 2);
-    uint4 kbuf[KCH_T];
+    uint4 kbuf[PAGED ? 4 : KCH_T];
     uint4 vbuf[4];
+    // paged: bit g set when keys 16g .. 16g+15 of the last loaded tile lie on a
+    // page outside the pool: they are not read, their K rows are stored as NaN
+    // (so every row that keeps one of them is NaN) and their V rows as 0
+    int bad_ld = 0;
 
     auto load_tile = [&](int key0) {
+        if constexpr (PAGED) {
+            // A tile is four 16-key groups, each inside one page (pages hold >= 16
+            // keys), read through one buffer resource per group sized to its valid
+            // rows: K load i takes group i (row 16i + tid/16, chunk tid%16), and
+            // wavefront w takes group w of V (four-key run lane%4, chunk lane/4).
+            int bad = 0;
+            __amdgpu_buffer_rsrc_t kr[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int k16 = key0 + 16 * g;
+                const int pg = k16 < Sb ? p.block_table[(int64_t)b * p.bt_stride + (k16 >> p.page_shift)] : 0;
+                const bool okp = (unsigned)pg < (unsigned)p.n_pages;
+                if (!okp && k16 < Sb) bad |= 1 << g;
+                const int nv = okp ? min(16, Sb - k16) : 0;
+                const int64_t row = (int64_t)(okp ? pg : 0) * p.k_sb + (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.k_sr;
+                kr[g] = make_rsrc(kbase + row, nv > 0 ? (nv - 1) * k_rs + D * 2 : 0);
+            }
+            bad_ld = bad;
+            const int ch = tid & 15;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                kbuf[i] = buf_load16(kr[i], ch < D / 8 ? (tid >> 4) * k_rs + ch * 16 : 0x7ffffff0);
+            const int wv = __builtin_amdgcn_readfirstlane(wave);
+            const int k16 = key0 + 16 * wv;
+            const int pg = k16 < Sb ? p.block_table[(int64_t)b * p.bt_stride + (k16 >> p.page_shift)] : 0;
+            const bool okp = (unsigned)pg < (unsigned)p.n_pages;
+            const int nv = okp ? min(16, Sb - k16) : 0;
+            const int64_t vrow = (int64_t)(okp ? pg : 0) * p.v_sb + (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.v_sr;
+            const auto vr = make_rsrc(vbase + vrow, nv > 0 ? (nv - 1) * v_rs + DV * 2 : 0);
+            const int kq = lane & 3, dc = lane >> 2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vbuf[r] = buf_load16(vr, dc < DV / 8 ? (kq * 4 + r) * v_rs + dc * 16 : 0x7ffffff0);
+            return;
+        }
         const int rows = min(BN, Sb - key0);
         const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
         const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + DV * 2);
@@ -165,6 +216,35 @@ void prefill_mfma_kernel(AttnParams p) {
     auto store_tile = [&](int stage) {
         uint16_t* Ks = smem + stage * STAGE;
         uint16_t* Vt = Ks + KTILE;
+        if constexpr (PAGED) {
+            // the load mapping of the paged branch of load_tile, same LDS layout
+            if ((tid & 15) < D / 8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * i + (tid >> 4);
+                    const int row = (r & ~31) | swap_bits23(r & 31);
+                    // all-ones halves are NaN in bf16 and fp16
+                    const uint4 kv = ((bad_ld >> i) & 1) ? make_uint4(~0u, ~0u, ~0u, ~0u) : kbuf[i];
+                    *(uint4*)(Ks + row * KS + (tid & 15) * 8) = kv;
+                }
+            }
+            const int kg = 4 * wave + (lane & 3), dc = lane >> 2;
+            if (dc < DV / 8) {
+                const uint32_t* w0 = (const uint32_t*)&vbuf[0];
+                const uint32_t* w1 = (const uint32_t*)&vbuf[1];
+                const uint32_t* w2 = (const uint32_t*)&vbuf[2];
+                const uint32_t* w3 = (const uint32_t*)&vbuf[3];
+                uint16_t* base = Vt + kg * 4;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(w1[j >> 1], w0[j >> 1], sel);
+                    const uint32_t hi = __builtin_amdgcn_perm(w3[j >> 1], w2[j >> 1], sel);
+                    *(uint2*)(base + (dc * 8 + j) * VS) = make_uint2(lo, hi);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < KCH_T; ++i) {
             const int c = tid + 256 * i;
@@ -212,7 +292,7 @@ void prefill_mfma_kernel(AttnParams p) {
         if (t + 1 < ntiles) load_tile(key0 + BN);
         const uint16_t* Ks = smem + (t & 1) * STAGE;
         const uint16_t* Vt = Ks + KTILE;
-        const bool active = wave_has_rows && (!CAUSAL || key0 <= q0 + wrow0 + 31);
+        const bool active = wave_has_rows && (!CAUSAL || key0 <= q0 + wrow0 + 31 + coff);
         if (active) {
             f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
@@ -251,7 +331,7 @@ void prefill_mfma_kernel(AttnParams p) {
                             s[kb][c * 8 + j] = fmaf(s[kb][c * 8 + j], p.scale_abs, bias[j]);
                     }
             }
-            const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
+            const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0 + coff);
             // Register r of block kb holds local key kb*32 + (r/8)*16 + r%8 (+ 8hh + key0).
             // A key is kept when that local index is below `lim` (and the bool mask says so).
             uint32_t mbits = 0xffffffffu;
@@ -284,7 +364,7 @@ void prefill_mfma_kernel(AttnParams p) {
                     }
             }
             int lim = Sb - (key0 + hh * 8);
-            if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
+            if (CAUSAL) lim = min(lim, my_row + 1 + coff - (key0 + hh * 8));
 
             auto softmax_pv = [&](auto masked_tag) {
                 constexpr bool MASKED = decltype(masked_tag)::value;
@@ -385,11 +465,11 @@ void prefill_mfma_kernel(AttnParams p) {
     }
 }
 
-template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false>
 hipError_t launch_prefill_one(const AttnParams& p, hipStream_t stream) {
     const long long grid = (long long)p.n_qtiles * p.Hq * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, DV, CAUSAL, MASK, VARLEN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, DV, CAUSAL, MASK, VARLEN, PAGED>), dim3((unsigned)grid),
                        dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -416,6 +496,12 @@ template <typename Tr, int D>
 hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool varlen,
                             hipStream_t s) {
     if (p.dv != D) return launch_prefill_dv<Tr, D>(p, causal, mask, varlen, s);
+    if (p.block_table) {
+        // queries against a paged cache (more new rows than the split-KV decode takes)
+        if (mask != MASK_NONE || varlen) return hipErrorInvalidValue;
+        return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, false, true>(p, s)
+                      : launch_prefill_one<Tr, D, D, false, MASK_NONE, false, true>(p, s);
+    }
     if (varlen) {
         // packed segments keep the 128-row kernel: 256-row tiles waste more
         // rows on short segments

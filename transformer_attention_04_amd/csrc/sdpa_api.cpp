@@ -227,16 +227,23 @@ sdpa_status paged_plan(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tenso
                     (long long)pp.page_size);
     pp.page_shift = shift;
     const int64_t group = pp.Hkv > 0 ? pp.Hq / pp.Hkv : 1;
-    if (pp.L * group > sdpa::kDecodeMaxRows)
-        return fail(SDPA_ERR_UNSUPPORTED, "the paged-cache kernel takes L * Hq / Hkv <= %d new rows per cache head",
-                    sdpa::kDecodeMaxRows);
     if (pp.E != pp.Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev");
     if (!supported_head_dim(pp.E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim must be 64, 96 or 128");
+    if (num_splits < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits must be 0 or positive");
+    if (pp.L * group > sdpa::kDecodeMaxRows) {
+        // chunked prefill: the single-pass kernel reads the pages itself, no workspace
+        if (num_splits > 0)
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "split-KV needs L * Hq / Hkv <= %d new rows per cache head (got %lld)",
+                        sdpa::kDecodeMaxRows, (long long)(pp.L * group));
+        pp.plan = Plan();
+        *out = pp;
+        return SDPA_OK;
+    }
     // Splits as for the dense split-KV path (about 2048 workgroups), each a
     // multiple of 128 keys spanning at most 64 pages (a split's pages sit in
     // the 64 lanes of a wavefront).  At least one split, so that rows with no cached
     // key still get output 0 and lse -inf from the merge.
-    if (num_splits < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits must be 0 or positive");
     const int64_t quantum = sdpa::kDecodeKeyQuantum;
     const int64_t S = max_seq_len;
     int64_t splits = num_splits;
@@ -515,9 +522,34 @@ sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_t
     if (lse_sr != 1) return fail(SDPA_ERR_UNSUPPORTED, "lse: the query dimension must have stride 1");
     double sc;
     if ((st = resolve_scale(scale, pp.E, &sc)) != SDPA_OK) return st;
-    if (pp.plan.workspace > workspace_bytes || !workspace)
+    if (pp.plan.workspace > workspace_bytes || (pp.plan.workspace > 0 && !workspace))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes needed, %zu given",
                     pp.plan.workspace, workspace_bytes);
+    if (!pp.plan.decode) {
+        sdpa::AttnParams a{};
+        a.q = q->data; a.k = k_cache->data; a.v = v_cache->data; a.o = out->data; a.lse = (float*)lse->data;
+        a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_sr = q->stride[2];
+        a.k_sb = k_cache->stride[0]; a.k_sh = k_cache->stride[1]; a.k_sr = k_cache->stride[2];
+        a.v_sb = v_cache->stride[0]; a.v_sh = v_cache->stride[1]; a.v_sr = v_cache->stride[2];
+        a.o_sb = out->stride[0]; a.o_sh = out->stride[1]; a.o_sr = out->stride[2];
+        a.lse_sb = lse->size[0] > 1 ? lse->stride[0] : 0;
+        a.lse_sh = lse->size[1] > 1 ? lse->stride[1] : 0;
+        a.B = (int)pp.B; a.Hq = (int)pp.Hq; a.Hkv = (int)pp.Hkv; a.group = (int)(pp.Hq / pp.Hkv);
+        a.L = (int)pp.L; a.S = max_seq_len;
+        a.dv = (int)pp.Ev;
+        a.n_qtiles = (int)((pp.L + sdpa::kPrefillBlockM - 1) / sdpa::kPrefillBlockM);
+        fill_scale(a, sc);
+        a.block_table = block_table;
+        a.seq_lens = seq_lens;
+        a.bt_stride = bt_stride;
+        a.page_shift = pp.page_shift;
+        a.n_pages = (int)pp.n_pages;
+        a.max_blocks = max_blocks;
+        hipError_t e = launch_single_pass(dtype, a, (int)pp.E, is_causal != 0, sdpa::MASK_NONE, false,
+                                          (hipStream_t)stream);
+        if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "paged prefill launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     sdpa::DecodeParams p{};
     p.q = q->data; p.k = k_cache->data; p.v = v_cache->data; p.o = out->data; p.lse = (float*)lse->data;
     float* ws = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);

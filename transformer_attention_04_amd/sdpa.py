@@ -224,7 +224,9 @@ def sdpa_fwd(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, 
 
 def sdpa_fwd_paged(query, k_cache, v_cache, block_table, seq_lens, max_seq_len=None, is_causal=False,
                    scale=None, enable_gqa=False, num_splits=0, workspace=None):
-    """Attention of new rows against a paged key/value cache on the GPU.
+    """Attention of new rows against a paged key/value cache on the GPU (decode
+    steps through the split-KV kernel, longer chunks of new rows through the
+    single-pass kernel).
 
     query (B, Hq, L, E); k_cache / v_cache (n_pages, Hkv, page_size, E);
     block_table (B, max_blocks) int32 and seq_lens (B,) int32 on the device;
