@@ -33,6 +33,8 @@
  *    E != Ev (value rows of another width than query/key rows, which the
  *    operation allows) is handled for bf16/fp16 inputs without attn_mask by
  *    sdpa_fwd; every other entry point and combination needs E == Ev.
+ *    sdpa_fwd also takes E == Ev any multiple of 8 from 8 to 128 for
+ *    bf16/fp16 inputs without attn_mask (single-pass kernel only).
  *    E = 0 (an empty score sum) is valid for the operation but not handled by
  *    the kernels: it returns SDPA_ERR_UNSUPPORTED.
  */

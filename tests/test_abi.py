@@ -107,10 +107,27 @@ def test_gqa_rules(lib):
 
 
 def test_unsupported_head_dims(lib):
-    st, _ = call(lib, *qkv(E=80))
+    # other head dims (multiples of 8 up to 128) run unmasked on bf16/fp16 only, with E == Ev
+    st, _ = call(lib, *qkv(E=80), dtype=S.SDPA_F32)
     assert st == S.SDPA_ERR_UNSUPPORTED
+    st, _ = call(lib, *qkv(E=80), mask=t4((1, 1, 16, 32)))
+    assert st == S.SDPA_ERR_UNSUPPORTED
+    for e in (4, 84, 136, 256):
+        st, _ = call(lib, *qkv(E=e))
+        assert st == S.SDPA_ERR_UNSUPPORTED, e
     st, _ = call(lib, *qkv(E=64, Ev=80))
     assert st == S.SDPA_ERR_UNSUPPORTED
+    st, _ = call(lib, *qkv(E=80, Ev=64))
+    assert st == S.SDPA_ERR_UNSUPPORTED
+    # the split-KV decode takes head dims 64, 96, 128 only
+    q, k, v = qkv(L=1, E=80)
+    n = ctypes.c_size_t(0)
+    st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                     None, 0, 0, 2, ctypes.byref(n))
+    assert st == S.SDPA_ERR_UNSUPPORTED
+    st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                     None, 0, 0, 0, ctypes.byref(n))
+    assert st == S.SDPA_OK and n.value == 0
     # E != Ev runs on the 16-bit kernels without a mask only
     st, msg = call(lib, *qkv(E=64, Ev=128), dtype=S.SDPA_F32)
     assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg

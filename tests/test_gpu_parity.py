@@ -403,3 +403,40 @@ def test_value_dim_differs(dtype, E, Ev):
     for splits in (0, 3):
         r = run_both(qd, kd, vd, dtype, enable_gqa=True, num_splits=splits)
         assert_parity(*r, dtype, f"decode E={E} Ev={Ev} splits={splits}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [8, 16, 32, 40, 80, 120])
+def test_other_head_dims(dtype, E):
+    """Head dims other than 64/96/128 (multiples of 8 up to 128), zero-padded
+    to the next multiple of 32 inside the kernel: ragged tiles, causal and not,
+    GQA, unit and default scales, and a decode-shaped call (single pass)."""
+    q, k, v = inputs.randn_qkv((2, 4, 200, E), (2, 2, 333, E), (2, 2, 333, E), dtype, seed=E + 500)
+    for causal in (False, True):
+        r = run_both(q, k, v, dtype, is_causal=causal, enable_gqa=True)
+        assert r[0].shape == (2, 4, 200, E)
+        assert_parity(*r, dtype, f"E={E} causal={causal}")
+    r = run_both(q[:, :2, :70], k[:, :2], v[:, :2], dtype, scale=1.0)
+    assert_parity(*r, dtype, f"E={E} scale=1")
+    qd, kd, vd = inputs.randn_qkv((3, 8, 1, E), (3, 2, 1000, E), (3, 2, 1000, E), dtype, seed=E + 501)
+    r = run_both(qd, kd, vd, dtype, enable_gqa=True)
+    assert_parity(*r, dtype, f"decode shape E={E}")
+
+
+@pytest.mark.parametrize("E", [8, 24, 40, 80, 120, 64, 96, 128])
+def test_writes_stay_inside_out(E):
+    """Every kernel path writes only its output rows: out is a view into a
+    larger buffer filled with a sentinel, with ragged query tiles; the padding
+    before, between and after the heads' rows must be untouched."""
+    B, Hq, Hkv, L, Sk = 2, 4, 2, 200, 333
+    q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), "bf16", seed=E + 900)
+    for causal in (False, True):
+        buf = torch.full((B, Hq, L + 3, E + 8), 7.0, dtype=torch.bfloat16, device=DEV)
+        out = buf[:, :, 1:L + 1, :E]
+        o, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal, enable_gqa=True, out=out)
+        torch.cuda.synchronize()
+        mask = torch.ones_like(buf, dtype=torch.bool)
+        mask[:, :, 1:L + 1, :E] = False
+        assert bool((buf[mask] == 7.0).all()), f"E={E} causal={causal}: writes outside out"
+        ro, rl = O.sdpa(q, k, v, is_causal=causal, enable_gqa=True)
+        assert_parity(out, lse, ro, rl, "bf16", f"E={E} causal={causal} strided out")

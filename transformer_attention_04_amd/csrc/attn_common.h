@@ -57,6 +57,7 @@ struct AttnParams {
     int page_shift;
     int n_pages;
     int max_blocks;
+    int e;                  // query/key head dim E (the padded instances read E of D columns)
 };
 
 // One launch of the split-KV decode kernel and of its merge pass.

@@ -58,7 +58,8 @@
 
 namespace sdpa {
 
-template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false,
+          bool PADE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(AttnParams p) {
     constexpr int BM = kPrefillBlockM;
@@ -138,11 +139,21 @@ void prefill_mfma_kernel(AttnParams p) {
     const bool wave_has_rows = wrow0 < qrows;
 
     // Q^T operand, resident for the whole loop (negated when the scale is negative).
+    // Row widths in bytes that bound the buffer resources.  The padded instances
+    // must use E: with the padded width a row's range would reach into the next
+    // rows (rows are only 2E bytes apart), and stores of rows past the tile's
+    // valid rows would land in them instead of being dropped.
+    const int qk_bytes = PADE ? p.e * 2 : D * 2;
+    const int v_bytes = PADE ? p.e * 2 : DV * 2;
     const int q_rs = (int)(p.q_sr * 2);
-    const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + D * 2);
+    const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + qk_bytes);
     uint4 qreg[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
+    for (int kk = 0; kk < NKK; ++kk) {
+        // padded head dim: columns from E on are not read (they load as 0)
+        const int col = kk * 16 + hh * 8;
+        qreg[kk] = buf_load16(qrs, (!PADE || col < p.e) ? lrow * q_rs + col * 2 : 0x7ffffff0);
+    }
     wait_vmem_all();
     // negated after all loads have landed (a select per load would wait for each in turn)
     if (p.neg) {
@@ -198,18 +209,19 @@ void prefill_mfma_kernel(AttnParams p) {
             return;
         }
         const int rows = min(BN, Sb - key0);
-        const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
-        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + DV * 2);
+        const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + qk_bytes);
+        const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + v_bytes);
 #pragma unroll
         for (int i = 0; i < KCH_T; ++i) {
             const int c = tid + 256 * i;
             const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-            kbuf[i] = buf_load16(kr, r * k_rs + col * 2);
+            kbuf[i] = buf_load16(kr, (!PADE || col < p.e) ? r * k_rs + col * 2 : 0x7ffffff0);
         }
         if (VIT == 256 || tid < VIT) {
             const int kg = tid % (BN / 4), dc = tid / (BN / 4);
+            const bool vin = !PADE || dc * 8 < p.e;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, (kg * 4 + r) * v_rs + dc * 16);
+            for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, vin ? (kg * 4 + r) * v_rs + dc * 16 : 0x7ffffff0);
         }
     };
 
@@ -447,7 +459,7 @@ void prefill_mfma_kernel(AttnParams p) {
     const float l_tot = pair32_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const int o_rs = (int)(p.o_sr * 2);
-    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + DV * 2);
+    const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + v_bytes);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -456,7 +468,7 @@ void prefill_mfma_kernel(AttnParams p) {
             uint2 st;
             st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
             st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-            buf_store8(st, ors, lrow * o_rs + d * 2);
+            if (!PADE || d < p.e) buf_store8(st, ors, lrow * o_rs + d * 2);
         }
     if (hh == 0) {
         const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
@@ -465,11 +477,12 @@ void prefill_mfma_kernel(AttnParams p) {
     }
 }
 
-template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false>
+template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false,
+          bool PADE = false>
 hipError_t launch_prefill_one(const AttnParams& p, hipStream_t stream) {
     const long long grid = (long long)p.n_qtiles * p.Hq * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, DV, CAUSAL, MASK, VARLEN, PAGED>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_mfma_kernel<Tr, D, DV, CAUSAL, MASK, VARLEN, PAGED, PADE>), dim3((unsigned)grid),
                        dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -532,6 +545,14 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
     return hipErrorInvalidValue;
 }
 
+// Other head dims E (a multiple of 8 up to 128, E == Ev; unmasked batched calls):
+// the four-wave kernel for the next multiple of 32, reading and writing E columns.
+template <typename Tr, int DP>
+hipError_t launch_prefill_pad(const AttnParams& p, bool causal, hipStream_t s) {
+    return causal ? launch_prefill_one<Tr, DP, DP, true, MASK_NONE, false, false, true>(p, s)
+                  : launch_prefill_one<Tr, DP, DP, false, MASK_NONE, false, false, true>(p, s);
+}
+
 template <typename Tr>
 hipError_t launch_prefill_t(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                             hipStream_t s) {
@@ -539,6 +560,15 @@ hipError_t launch_prefill_t(const AttnParams& p, int D, bool causal, int mask, b
         case 64: return launch_prefill_d<Tr, 64>(p, causal, mask, varlen, s);
         case 96: return launch_prefill_d<Tr, 96>(p, causal, mask, varlen, s);
         case 128: return launch_prefill_d<Tr, 128>(p, causal, mask, varlen, s);
+    }
+    if (D < 8 || D > 128 || D % 8 != 0 || p.e != D || p.dv != D || mask != MASK_NONE || varlen ||
+        p.block_table)
+        return hipErrorInvalidValue;
+    switch ((D + 31) / 32) {
+        case 1: return launch_prefill_pad<Tr, 32>(p, causal, s);
+        case 2: return launch_prefill_pad<Tr, 64>(p, causal, s);
+        case 3: return launch_prefill_pad<Tr, 96>(p, causal, s);
+        case 4: return launch_prefill_pad<Tr, 128>(p, causal, s);
     }
     return hipErrorInvalidValue;
 }

@@ -62,6 +62,8 @@ sdpa_status check_vector_layout(const sdpa_tensor4& t, int ebytes, const char* n
 }
 
 bool supported_head_dim(int64_t e) { return e == 64 || e == 96 || e == 128; }
+// Other head dims the single-pass 16-bit kernel takes unmasked, zero-padded in registers.
+bool padded_head_dim(int64_t e) { return e >= 8 && e <= 128 && e % 8 == 0; }
 
 struct Plan {
     bool decode = false;
@@ -75,10 +77,11 @@ struct Plan {
 // workgroups (several per compute unit) while keeping each split long enough
 // that the final merge stays small next to the key/value stream.
 sdpa_status make_plan(sdpa_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
-                      int64_t Ev, bool has_mask, bool causal, int num_splits, Plan* plan) {
+                      int64_t E, int64_t Ev, bool has_mask, bool causal, int num_splits, Plan* plan) {
     const int64_t group = Hkv > 0 ? Hq / Hkv : 1;
     const bool eligible = !has_mask && !causal && (dtype == SDPA_BF16 || dtype == SDPA_F16) &&
-                          L * group <= sdpa::kDecodeMaxRows && L > 0;
+                          L * group <= sdpa::kDecodeMaxRows && L > 0 && supported_head_dim(E) &&
+                          supported_head_dim(Ev);
     Plan pl;
     if (num_splits == -1) {
         pl.decode = false;
@@ -87,8 +90,8 @@ sdpa_status make_plan(sdpa_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int6
     } else if (num_splits >= 1) {
         if (!eligible)
             return fail(SDPA_ERR_UNSUPPORTED,
-                        "the split-KV decode kernel needs no mask, no causal flag, bf16/fp16 and "
-                        "L*Hq/Hkv <= %d (got L=%lld, group=%lld)",
+                        "the split-KV decode kernel needs no mask, no causal flag, bf16/fp16, head dims "
+                        "in {64, 96, 128} and L*Hq/Hkv <= %d (got L=%lld, group=%lld)",
                         sdpa::kDecodeMaxRows, (long long)L, (long long)group);
         pl.decode = true;
     } else {
@@ -287,7 +290,7 @@ sdpa_status sdpa_fwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, con
     sdpa_status st = check_shapes(dtype, q, k, v, attn_mask, enable_gqa, &s);
     if (st != SDPA_OK) return st;
     Plan pl;
-    st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.Ev, attn_mask != nullptr, is_causal != 0,
+    st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.E, s.Ev, attn_mask != nullptr, is_causal != 0,
                    num_splits, &pl);
     if (st != SDPA_OK) return st;
     *bytes = pl.workspace;
@@ -317,8 +320,11 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
     if (s.B * s.Hq * s.L == 0) return ok();  // nothing to compute
-    if (!supported_head_dim(s.E) || !supported_head_dim(s.Ev))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be one of 64, 96, 128",
+    if (!(supported_head_dim(s.E) && supported_head_dim(s.Ev)) &&
+        !(padded_head_dim(s.E) && s.E == s.Ev && dtype != SDPA_F32 && !attn_mask))
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "head dims E=%lld, Ev=%lld: each must be one of 64, 96, 128, or E == Ev a multiple "
+                    "of 8 up to 128 for bf16/fp16 without a mask",
                     (long long)s.E, (long long)s.Ev);
     if (s.E != s.Ev && (dtype == SDPA_F32 || attn_mask))
         return fail(SDPA_ERR_UNSUPPORTED,
@@ -340,7 +346,7 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     double sc;
     if ((st = resolve_scale(scale, s.E, &sc)) != SDPA_OK) return st;
     Plan pl;
-    if ((st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.Ev, attn_mask != nullptr, is_causal != 0,
+    if ((st = make_plan(dtype, s.B, s.Hq, s.Hkv, s.L, s.S, s.E, s.Ev, attn_mask != nullptr, is_causal != 0,
                         num_splits, &pl)) != SDPA_OK)
         return st;
     if (pl.workspace > workspace_bytes || (pl.workspace > 0 && !workspace))
@@ -401,6 +407,7 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
     p.L = (int)s.L; p.S = (int)s.S;
     p.dv = (int)s.Ev;
+    p.e = (int)s.E;
     const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
     p.n_qtiles = (int)((s.L + bm - 1) / bm);
     fill_scale(p, sc);
@@ -467,6 +474,7 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     p.B = n_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
     p.L = max_seqlen_q; p.S = max_seqlen_k;
     p.dv = Ev;
+    p.e = E;
     const int bm = dtype == SDPA_F32 ? sdpa::kF32BlockM : sdpa::kPrefillBlockM;
     p.n_qtiles = (max_seqlen_q + bm - 1) / bm;
     fill_scale(p, sc);
@@ -537,6 +545,7 @@ sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_t
         a.B = (int)pp.B; a.Hq = (int)pp.Hq; a.Hkv = (int)pp.Hkv; a.group = (int)(pp.Hq / pp.Hkv);
         a.L = (int)pp.L; a.S = max_seq_len;
         a.dv = (int)pp.Ev;
+        a.e = (int)pp.E;
         a.n_qtiles = (int)((pp.L + sdpa::kPrefillBlockM - 1) / sdpa::kPrefillBlockM);
         fill_scale(a, sc);
         a.block_table = block_table;
