@@ -20,7 +20,7 @@ host RAM, float64).  Inputs are upcast exactly from whatever dtype they hold;
 nothing is rounded back to a narrow format.  numpy's matmul serves as the one
 library step (the dot products).
 
-Readings where the pages leave a step open (each is also listed in the design doc):
+Readings where the pages leave a step open:
   * scale=None means 1/sqrt(E) with E the query's last dimension, computed in
     double; with E = 0 the scores are empty sums equal to 0 and the logits are
     the bias alone, whatever the scale.
