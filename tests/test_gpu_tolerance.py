@@ -1,0 +1,120 @@
+"""Every kernel path against the per-element tolerance (oracle/tolerance.py).
+
+Stricter than the fixed bars of the other parity tests where outputs are small:
+each GPU output element (and lse) must lie within the budget a float32
+FlashAttention-style computation may spend on that element, with the weights
+rounded to the input format before the value product (exactref.ai
+"scaled_dot_product_attention", "Tolerance options" and the budget list of its
+"Full specification").  Special rows must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_oracle as O
+from oracle import tolerance as T
+from transformer_attention_04_amd import inputs
+from transformer_attention_04_amd import sdpa as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check_covered(out, lse, q, k, v, dtype, what, **kw):
+    to, tl = T.tolerance(q, k, v, dtype=dtype, **kw)
+    xo, xl = O.sdpa(q, k, v, **kw)
+    out, lse = _np(out), _np(lse)
+    co, cl = T.covers(out, xo, to), T.covers(lse, xl, tl)
+    fin = to > 0
+    ratio = float((np.abs(out - xo)[fin] / to[fin]).max(initial=0.0))
+    print(f"{what}: worst output error / tolerance {ratio:.3f}")
+    assert co.all(), f"{what}: {int((~co).sum())} output elements outside the tolerance (worst ratio {ratio:.2f})"
+    assert cl.all(), f"{what}: {int((~cl).sum())} lse elements outside the tolerance"
+
+
+@pytest.mark.parametrize("dtype,E,causal", [("bf16", 128, True), ("bf16", 96, False), ("fp16", 64, True),
+                                            ("fp16", 128, False)])
+def test_eight_wave_prefill(dtype, E, causal):
+    q, k, v = inputs.randn_qkv((1, 2, 300, E), (1, 2, 300, E), (1, 2, 300, E), dtype, seed=E + 7)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal)
+    torch.cuda.synchronize()
+    check_covered(out, lse, q, k, v, dtype, f"{dtype} E={E} causal={causal}", is_causal=causal)
+
+
+def test_masks_varlen_and_widened_dims():
+    q, k, v = inputs.randn_qkv((1, 2, 200, 96), (1, 2, 257, 96), (1, 2, 257, 96), "bf16", seed=3)
+    g = torch.Generator().manual_seed(4)
+    fm = torch.randn(1, 2, 200, 257, generator=g)
+    fm[torch.rand(1, 2, 200, 257, generator=g) < 0.2] = float("-inf")
+    fm[..., 0] = 0.0
+    for m, what in ((fm, "float mask (unaligned rows: four-wave kernel)"),
+                    (fm[..., :256].contiguous(), "float mask (aligned rows: eight-wave kernel)"),
+                    (fm > 0, "bool mask")):
+        kk, vv = (k, v) if m.shape[-1] == 257 else (k[:, :, :256].contiguous(), v[:, :, :256].contiguous())
+        out, lse = S.sdpa_fwd(q.to(DEV), kk.to(DEV), vv.to(DEV), attn_mask=m.to(DEV), is_causal=True)
+        torch.cuda.synchronize()
+        mm = m.double().numpy() if m.dtype != torch.bool else m.numpy()
+        check_covered(out, lse, q, kk, vv, "bf16", what, attn_mask=mm, is_causal=True)
+    q, k, v = inputs.randn_qkv((1, 4, 150, 64), (1, 2, 333, 64), (1, 2, 333, 128), "fp16", seed=5)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), enable_gqa=True, is_causal=True)
+    torch.cuda.synchronize()
+    check_covered(out, lse, q, k, v, "fp16", "Ev != E, GQA", enable_gqa=True, is_causal=True)
+    q, k, v = inputs.randn_qkv((1, 2, 150, 40), (1, 2, 333, 40), (1, 2, 333, 40), "bf16", seed=6)
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    check_covered(out, lse, q, k, v, "bf16", "head dim 40")
+    lengths = [1, 37, 128, 129, 300]
+    qv, kv, vv, cu = inputs.varlen_inputs(lengths, 4, 2, 64, "fp16", seed=8)
+    out, lse = S.sdpa_fwd_varlen(qv.to(DEV), kv.to(DEV), vv.to(DEV), cu.to(DEV), max_seqlen_q=300,
+                                 max_seqlen_k=300, is_causal=True, enable_gqa=True)
+    torch.cuda.synchronize()
+    cu_ = cu.tolist()
+    for i in range(len(lengths)):
+        a, b = cu_[i], cu_[i + 1]
+        qs, ks, vs = (t[0, a:b].permute(1, 0, 2).contiguous() for t in (qv, kv, vv))
+        check_covered(out[0, a:b].permute(1, 0, 2), lse[0, :, a:b], qs, ks, vs, "fp16",
+                      f"varlen segment {i}", is_causal=True, enable_gqa=True)
+
+
+def test_decode_and_paged():
+    q, k, v = inputs.randn_qkv((2, 8, 1, 128), (2, 2, 1000, 128), (2, 2, 1000, 128), "bf16", seed=9)
+    for splits in (0, 5):
+        out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), enable_gqa=True, num_splits=splits)
+        torch.cuda.synchronize()
+        check_covered(out, lse, q, k, v, "bf16", f"split-KV decode, splits={splits}", enable_gqa=True)
+    ps, n = 64, 700
+    nb = (n + ps - 1) // ps
+    for L in (1, 100):
+        qp, kc, vc = inputs.randn_qkv((1, 8, L, 128), (nb + 3, 2, ps, 128), (nb + 3, 2, ps, 128), "bf16", seed=10 + L)
+        bt = torch.randperm(nb + 3, generator=torch.Generator().manual_seed(L))[:nb].reshape(1, nb).to(torch.int32)
+        lens = torch.tensor([n], dtype=torch.int32)
+        out, lse = S.sdpa_fwd_paged(qp.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), lens.to(DEV), max_seq_len=n,
+                                    is_causal=True, enable_gqa=True)
+        torch.cuda.synchronize()
+        kd = torch.cat([kc[p] for p in bt[0].tolist()], dim=1)[:, :n][None]
+        vd = torch.cat([vc[p] for p in bt[0].tolist()], dim=1)[:, :n][None]
+        bias = np.where(np.arange(n)[None, :] <= n - L + np.arange(L)[:, None], 0.0, -np.inf)
+        check_covered(out, lse, qp, kd, vd, "bf16", f"paged, {L} new rows", attn_mask=bias, enable_gqa=True)
+
+
+def test_fp32_path():
+    q, k, v = inputs.workload_inputs("fp32_single_head")
+    for kw in ({}, {"is_causal": True}, {"scale": 1.0}):
+        out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **kw)
+        torch.cuda.synchronize()
+        check_covered(out, lse, q, k, v, "fp32", f"fp32 {kw}", **kw)
+
+
+def test_headline_shape_sampled():
+    """bf16 causal B=4 H=16 L=S=2048 E=128 in the benchmark's launch configuration;
+    two (batch, head) slices against their per-element tolerance."""
+    q, k, v = inputs.workload_inputs("bf16_causal_e128")
+    out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 15)):
+        check_covered(out[b, h], lse[b, h], q[b, h], k[b, h], v[b, h], "bf16", f"headline b={b} h={h}",
+                      is_causal=True)
