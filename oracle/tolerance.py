@@ -151,14 +151,15 @@ def tolerance(query, key, value, attn_mask=None, is_causal=False, scale=None, en
             pv = P @ absv[n_]
             sv = kept.astype(np.float64) @ absv[n_]
             nrs = np.ceil(nk / 32.0) + 1.0
+            lse_c = np.where(normal, LS[n_, r0:r1], 0.0)          # finite stand-in on special rows
             lt = ((P * eta).sum(axis=-1) + _gamma(nk) + nrs * (e_exp + 2 * U32)
-                  + (2 * ulps + 4) * U32 * (np.abs(LS[n_, r0:r1]) + msh + np.log(nk + 1.0)))
+                  + (2 * ulps + 4) * U32 * (np.abs(lse_c) + msh + np.log(nk + 1.0)))
             b = (pe + u_w * pv + a_w * sv + _gamma(nk)[:, None] * (pv + np.abs(Oc))
                  + ((2 * nrs + 4) * U32)[:, None] * np.abs(Oc)
                  + (lt + e_exp + 4 * U32)[:, None] * pdev)
             b = b * (1.0 + 2.0 ** -10)
             b = b + u_out * (np.abs(Oc) + b) + OUT_ABS[dtype]
-            lt = lt * (1.0 + 2.0 ** -10) + U32 * np.abs(LS[n_, r0:r1])
+            lt = lt * (1.0 + 2.0 ** -10) + U32 * np.abs(lse_c)
             out_tol[n_, r0:r1] = np.where(normal[:, None], b, 0.0)
             lse_tol[n_, r0:r1] = np.where(normal, lt, 0.0)
     return out_tol.reshape(lead + (L, Ev)), lse_tol.reshape(lead + (L,))

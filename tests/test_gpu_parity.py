@@ -440,3 +440,53 @@ def test_writes_stay_inside_out(E):
         assert bool((buf[mask] == 7.0).all()), f"E={E} causal={causal}: writes outside out"
         ro, rl = O.sdpa(q, k, v, is_causal=causal, enable_gqa=True)
         assert_parity(out, lse, ro, rl, "bf16", f"E={E} causal={causal} strided out")
+
+
+def _bool_mask(shape, seed, keep=0.7):
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(shape, generator=g) < keep
+
+
+@pytest.mark.parametrize("dtype,E,causal,L,Sk,B,Hq,Hkv,mshape", [
+    ("bf16", 128, True, 300, 300 - 300 % 16, 2, 4, 2, "full"),
+    ("bf16", 96, False, 200, 256, 1, 4, 4, "head"),
+    ("fp16", 64, True, 520, 512, 1, 2, 1, "row"),
+    ("fp16", 128, False, 129, 144, 2, 2, 2, "batch"),
+    ("bf16", 64, False, 64, 4096, 1, 2, 2, "full"),
+])
+def test_bool_mask_eight_wave(dtype, E, causal, L, Sk, B, Hq, Hkv, mshape):
+    """Bool masks whose rows are whole 16-byte chunks (key count a multiple of
+    16) run on the eight-wave kernel: random keep patterns with fully masked
+    rows, broadcast shapes, GQA, causal, ragged query tiles."""
+    q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), dtype, seed=E + L)
+    shape = {"full": (B, Hq, L, Sk), "head": (1, Hq, L, Sk), "row": (1, 1, L, Sk), "batch": (B, 1, 1, Sk)}[mshape]
+    m = _bool_mask(shape, L + Sk)
+    if mshape != "batch":
+        m[..., 3, :] = False                 # a row with no kept key
+    r = run_both(q, k, v, dtype, attn_mask=m, is_causal=causal, enable_gqa=Hq != Hkv)
+    assert_parity(*r, dtype, f"bool {mshape} causal={causal}")
+    for scale in (-0.2, 1.0):
+        r = run_both(q[:, :, :100], k, v, dtype, attn_mask=m[..., :100, :] if m.shape[-2] > 1 else m,
+                     is_causal=causal, scale=scale, enable_gqa=Hq != Hkv)
+        assert_parity(*r, dtype, f"bool {mshape} scale={scale}")
+
+
+def test_bool_mask_same_result_on_both_kernels():
+    """The same bool mask once with 16-byte rows (eight-wave kernel) and once
+    as a view with a row stride of S + 8 (four-wave kernel)."""
+    q, k, v = inputs.randn_qkv((1, 4, 300, 128), (1, 4, 320, 128), (1, 4, 320, 128), "bf16", seed=12)
+    m = _bool_mask((1, 4, 300, 320), 13)
+    wide = torch.zeros((1, 4, 300, 328), dtype=torch.bool)
+    wide[..., :320] = m
+    outs = []
+    for mm in (m.to(DEV), wide.to(DEV)[..., :320]):
+        o, l = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), attn_mask=mm, is_causal=True)
+        torch.cuda.synchronize()
+        outs.append((o, l))
+    ro, rl = O.sdpa(q, k, v, attn_mask=m, is_causal=True)
+    for o, l in outs:
+        assert_parity(o, l, ro, rl, "bf16", "bool mask, both kernels")
+    l0, l1 = outs[0][1].cpu(), outs[1][1].cpu()
+    fin = torch.isfinite(l0)
+    assert torch.equal(fin, torch.isfinite(l1)) and torch.equal(l0[~fin], l1[~fin])
+    assert float((l0[fin] - l1[fin]).abs().max()) < 1e-4
