@@ -222,11 +222,16 @@ sdpa_status sdpa_fwd_paged_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* 
  *
  *   dtype      SDPA_BF16 or SDPA_F16 (SDPA_F32 returns SDPA_ERR_UNSUPPORTED).
  *   q, k, v    as for sdpa_fwd; E == Ev in {64, 96, 128}.
- *   out, lse   the results of sdpa_fwd for the same q, k, v, is_causal,
- *              scale and enable_gqa (no mask): out (B, Hq, L, Ev) dtype,
- *              lse (B, Hq, L, 1) float32.
+ *   attn_mask, mask_dtype
+ *              as for sdpa_fwd (NULL, or a float32 bias / bool keep mask
+ *              broadcastable to (B, Hq, L, S), key stride 1).  The mask gets
+ *              no gradient.
+ *   out, lse   the results of sdpa_fwd for the same q, k, v, attn_mask,
+ *              is_causal, scale and enable_gqa: out (B, Hq, L, Ev) dtype,
+ *              lse (B, Hq, L, 1) float32.  A row with no kept key (lse -inf)
+ *              contributes nothing.
  *   dout       (B, Hq, L, Ev), dtype: gradient of the loss with respect to out.
- *   is_causal, scale, enable_gqa   as for sdpa_fwd.  There is no mask argument.
+ *   is_causal, scale, enable_gqa   as for sdpa_fwd.
  *   dq         (B, Hq, L, E), dk (B, Hkv, S, E), dv (B, Hkv, S, Ev), dtype;
  *              written completely (rows no query reaches get 0), rounded to
  *              nearest-even.  They must not alias any input.
@@ -241,6 +246,7 @@ sdpa_status sdpa_fwd_paged_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* 
  */
 sdpa_status sdpa_bwd(sdpa_dtype dtype,
                      const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* attn_mask, sdpa_dtype mask_dtype,
                      const sdpa_tensor4* out, const sdpa_tensor4* lse, const sdpa_tensor4* dout,
                      int is_causal, const double* scale, int enable_gqa,
                      const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(S.EXPORTED) == set(declared_functions())
-    assert lib.sdpa_abi_version() == 3
+    assert lib.sdpa_abi_version() == 4
 
 
 def t4(shape, strides=None, data=FAKE):

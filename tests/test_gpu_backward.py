@@ -31,11 +31,15 @@ def bwd_bar(ref):
 
 def run_bwd(q, k, v, g, dtype, **kw):
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
-    out, lse = S.sdpa_fwd(qd, kd, vd, is_causal=kw.get("is_causal", False), scale=kw.get("scale"),
+    m = kw.get("attn_mask")
+    md = None if m is None else m.to(DEV)
+    out, lse = S.sdpa_fwd(qd, kd, vd, attn_mask=md, is_causal=kw.get("is_causal", False), scale=kw.get("scale"),
                           enable_gqa=kw.get("enable_gqa", False))
-    dq, dk, dv = S.sdpa_bwd(qd, kd, vd, out, lse, gd, is_causal=kw.get("is_causal", False),
+    dq, dk, dv = S.sdpa_bwd(qd, kd, vd, out, lse, gd, attn_mask=md, is_causal=kw.get("is_causal", False),
                             scale=kw.get("scale"), enable_gqa=kw.get("enable_gqa", False))
     torch.cuda.synchronize()
+    if m is not None:
+        kw = dict(kw, attn_mask=m.numpy() if m.dtype == torch.bool else m.double().numpy())
     return (dq, dk, dv), O.sdpa_backward(q, k, v, g, **kw)
 
 
@@ -111,3 +115,40 @@ def test_backward_headline_shape_sampled():
     for b, h in [(0, 0), (1, 7), (2, 15), (3, 3), (3, 15)]:
         ref = O.sdpa_backward(q[b, h], k[b, h], v[b, h], g[b, h], is_causal=True)
         assert_bwd((dq[b, h], dk[b, h], dv[b, h]), ref, f"headline b={b} h={h}")
+
+
+def _masks(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    fm = torch.randn(shape, generator=g)
+    fm[torch.rand(shape, generator=g) < 0.15] = float("-inf")
+    bm = torch.rand(shape, generator=g) < 0.8
+    return fm, bm
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [64, 96, 128])
+def test_backward_masks(dtype, E):
+    """Float (bias with -inf) and bool masks, full and broadcast shapes, with and
+    without causal; rows with no kept key contribute nothing; key counts that
+    are and are not whole vectors of the mask's loads."""
+    for (L, Sk, mshape, causal) in ((200, 256, "full", False), (150, 333, "row", True), (130, 130, "head", True)):
+        q, k, v = inputs.randn_qkv((2, 2, L, E), (2, 2, Sk, E), (2, 2, Sk, E), dtype, seed=E + L)
+        g = inputs.randn_qkv((2, 2, L, E), (1, 1, 1, E), (1, 1, 1, E), dtype, seed=E + L + 1)[0]
+        shape = {"full": (2, 2, L, Sk), "row": (1, 1, L, Sk), "head": (1, 2, L, Sk)}[mshape]
+        fm, bm = _masks(shape, E + Sk)
+        fm[..., 5, :] = float("-inf")          # a row with no kept key
+        bm[..., 7, :] = False
+        for m, what in ((fm, "float"), (bm, "bool")):
+            gpu, ref = run_bwd(q, k, v, g, dtype, attn_mask=m, is_causal=causal)
+            assert_bwd(gpu, ref, f"{dtype} E={E} {what} {mshape} causal={causal}")
+            assert float(gpu[0][..., 5 if what == "float" else 7, :].abs().max()) == 0.0
+
+
+def test_backward_mask_gqa_and_scale():
+    q, k, v = inputs.randn_qkv((1, 4, 190, 128), (1, 2, 190, 128), (1, 2, 190, 128), "bf16", seed=41)
+    g = inputs.randn_qkv((1, 4, 190, 128), (1, 1, 1, 128), (1, 1, 1, 128), "bf16", seed=42)[0]
+    fm, bm = _masks((1, 4, 190, 190), 43)
+    for m in (fm, bm):
+        for scale in (None, -0.3):
+            gpu, ref = run_bwd(q, k, v, g, "bf16", attn_mask=m, is_causal=True, enable_gqa=True, scale=scale)
+            assert_bwd(gpu, ref, f"gqa {m.dtype} scale={scale}")

@@ -123,6 +123,11 @@ struct BwdParams {
     int n_ktiles;   // 128-key tiles
     int elem;       // ELEM_BF16 or ELEM_F16
     float scale;    // signed
+    // Optional mask, as in the forward: float32 bias or uint8 keep flags,
+    // element (b, h, i, j) at b*m_sb + h*m_sh + i*m_sr + j (0 strides broadcast)
+    const void* mask;
+    int64_t m_sb, m_sh, m_sr;
+    int mask_vec;   // rows allow vector loads (16-byte float / 8-byte bool runs)
 };
 
 hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
@@ -132,7 +137,7 @@ hipError_t launch_prefill_f16(const AttnParams& p, int D, bool causal, int mask,
 hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int elem, int D, hipStream_t stream);
-hipError_t launch_backward(const BwdParams& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, hipStream_t stream);
 
 // Tile sizes the host needs for grids and workspace.
 constexpr int kPrefillBlockM = 128;  // query rows per MFMA workgroup

@@ -109,7 +109,43 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------- dQ
 
-template <typename Tr, int D, bool CAUSAL>
+// Mask values of 8 consecutive keys starting at byte offset off of a
+// range-checked mask resource: float32 bias (MASK_FLOAT) into b[0..7], or keep
+// flags (MASK_BOOL, any nonzero byte keeps) into bits 0..7 of the result.
+template <int MASK>
+__device__ __forceinline__ uint32_t bwd_mask8(__amdgpu_buffer_rsrc_t r, int off, bool vec, float* b) {
+    if constexpr (MASK == MASK_FLOAT) {
+        if (vec) {
+            const uint4 b0 = buf_load16(r, off), b1 = buf_load16(r, off + 16);
+            b[0] = __uint_as_float(b0.x); b[1] = __uint_as_float(b0.y);
+            b[2] = __uint_as_float(b0.z); b[3] = __uint_as_float(b0.w);
+            b[4] = __uint_as_float(b1.x); b[5] = __uint_as_float(b1.y);
+            b[6] = __uint_as_float(b1.z); b[7] = __uint_as_float(b1.w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[j] = __uint_as_float(buf_load4(r, off + 4 * j));
+        }
+        return 0xffu;
+    } else {
+        uint2 u;
+        if (vec) {
+            u = buf_load8(r, off);
+        } else {
+            u.x = u.y = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u.x |= buf_load1(r, off + j) << (8 * j);
+                u.y |= buf_load1(r, off + 4 + j) << (8 * j);
+            }
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bits |= ((((j < 4 ? u.x : u.y) >> (8 * (j & 3))) & 0xffu) != 0 ? 1u : 0u) << j;
+        return bits;
+    }
+}
+
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
     constexpr int BM = 128, BN = 64;
@@ -152,7 +188,9 @@ void bwd_dq_kernel(BwdParams p) {
     }
     const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
     const bool row_ok = my_row < p.L;
-    const float lse2 = row_ok ? p.lse[b * p.lse_sb + h * p.lse_sh + my_row] * kLog2e : 0.f;
+    float lse2 = row_ok ? p.lse[b * p.lse_sb + h * p.lse_sh + my_row] * kLog2e : 0.f;
+    // a masked row with no kept key (lse -inf) has P = 0: exp2(-inf - 0)
+    if (MASK != MASK_NONE && lse2 == kNegInf) lse2 = 0.f;
     const float drow = row_ok ? p.dsum[rowid + my_row] : 0.f;
     const float c2 = p.scale * kLog2e;  // signed
     // All of the above has landed before the loop: otherwise the first uses in
@@ -217,12 +255,33 @@ void bwd_dq_kernel(BwdParams p) {
             int lim = p.S - (key0 + hh * 8);
             if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
             uint4 pb[4];
+            constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;  // bytes per mask element
+            // this wave's rows of the mask from key key0 on (unused without a mask)
+            const auto mr = make_rsrc(
+                MASK == MASK_NONE ? p.mask
+                                  : (const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                                                           (int64_t)(q0 + wrow0) * p.m_sr + key0) * MES,
+                MASK == MASK_NONE ? 0 : ((qrows - 1 - wrow0) * (int)p.m_sr + (p.S - key0)) * MES);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 float ds[16];
+                float mb[16];       // float mask: bias of register r
+                uint32_t mk = ~0u;  // bool mask: keep bit of register r
+                if constexpr (MASK != MASK_NONE) {
+                    mk = 0;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        mk |= bwd_mask8<MASK>(mr, (lq * (int)p.m_sr + kb * 32 + c * 16 + hh * 8) * MES, p.mask_vec != 0,
+                                              mb + 8 * c) << (8 * c);
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pv = fast_exp2(fmaf(s[kb][r], c2, -lse2));
+                    float pv;
+                    if constexpr (MASK == MASK_FLOAT)
+                        pv = fast_exp2(fmaf(fmaf(s[kb][r], p.scale, mb[r]), kLog2e, -lse2));
+                    else
+                        pv = fast_exp2(fmaf(s[kb][r], c2, -lse2));
+                    if constexpr (MASK == MASK_BOOL) pv = ((mk >> r) & 1u) ? pv : 0.f;
                     if (edge) pv = (kb * 32 + (r >> 3) * 16 + (r & 7) < lim) ? pv : 0.f;
                     ds[r] = pv * (dp[kb][r] - drow);
                 }
@@ -270,7 +329,7 @@ void bwd_dq_kernel(BwdParams p) {
 // wavefronts 0-3 own dK (S, dP, dS, dK^T += Q^T dS), wavefronts 4-7 own dV
 // (S, P, dV^T += dO^T P).  Each role fits two wavefronts per SIMD; S is
 // computed by both roles.
-template <typename Tr, int D, bool CAUSAL>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BK = 128, BN = 64;     // keys per workgroup, queries per step
@@ -369,7 +428,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             }
         }
         if (tid < BN) {
-            Ls[tid] = lbuf * kLog2e;
+            // a masked row with no kept key (lse -inf) has P = 0: exp2(-inf - 0)
+            Ls[tid] = (MASK != MASK_NONE && lbuf == kNegInf) ? 0.f : lbuf * kLog2e;
             Ls[BN + tid] = dbuf;
         }
     };
@@ -391,6 +451,26 @@ void bwd_dkdv_kernel(BwdParams p) {
         if (active) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
+                // mask values of this lane's key for the 16 queries of register r
+                // (query 32qb + 16(r/8) + 8hh + r%8 of the block), loaded before the products
+                float mb[16];
+                uint32_t mk = ~0u;
+                if constexpr (MASK != MASK_NONE) {
+                    constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
+                    const int qf = qrow0 + qb * 32, nq = p.L - qf;
+                    const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                                                                     (int64_t)qf * p.m_sr + wkey0) * MES,
+                                              nq > 0 ? ((nq - 1) * (int)p.m_sr + (p.S - wkey0)) * MES : 0);
+                    mk = 0;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = ((16 * (r >> 3) + 8 * hh + (r & 7)) * (int)p.m_sr + lq) * MES;
+                        if constexpr (MASK == MASK_FLOAT)
+                            mb[r] = __uint_as_float(buf_load4(mr, off));
+                        else
+                            mk |= (buf_load1(mr, off) != 0 ? 1u : 0u) << r;
+                    }
+                }
                 f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
@@ -423,7 +503,12 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int r = 8 * half + j;
-                        float e = fast_exp2(fmaf(s[r], c2, -lv[j]));
+                        float e;
+                        if constexpr (MASK == MASK_FLOAT)
+                            e = fast_exp2(fmaf(fmaf(s[r], p.scale, mb[r]), kLog2e, -lv[j]));
+                        else
+                            e = fast_exp2(fmaf(s[r], c2, -lv[j]));
+                        if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
                         if (edge) {
                             const int qi = qrow0 + qbase + 16 * half + j;
                             const bool keep = qi < p.L && (!CAUSAL || qi >= my_key);
@@ -475,43 +560,55 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
 }
 
-template <typename Tr, int D>
-hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
-    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
-    if (nrows > 0)
-        hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, p);
-    if (nrows > 0) {
+template <typename Tr, int D, bool CAUSAL, int MASK>
+void launch_bwd_grads(const BwdParams& p, hipStream_t s) {
+    if ((int64_t)p.B * p.Hq * p.L > 0) {
         const unsigned g = (unsigned)p.n_qtiles * p.Hq * p.B;
-        if (causal)
-            hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, true>), dim3(g), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, false>), dim3(g), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, CAUSAL, MASK>), dim3(g), dim3(256), 0, s, p);
     }
     if ((int64_t)p.S * p.Hkv * p.B > 0) {
         const unsigned g = (unsigned)p.n_ktiles * p.Hkv * p.B;
-        if (causal)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, true>), dim3(g), dim3(512), 0, s, p);
-        else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, false>), dim3(g), dim3(512), 0, s, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK>), dim3(g), dim3(512), 0, s, p);
+    }
+}
+
+template <typename Tr, int D, int MASK>
+void launch_bwd_m(const BwdParams& p, bool causal, hipStream_t s) {
+    if (causal)
+        launch_bwd_grads<Tr, D, true, MASK>(p, s);
+    else
+        launch_bwd_grads<Tr, D, false, MASK>(p, s);
+}
+
+template <typename Tr, int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, int mask, hipStream_t s) {
+    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
+    if (nrows > 0)
+        hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, p);
+    switch (mask) {
+        case MASK_NONE: launch_bwd_m<Tr, D, MASK_NONE>(p, causal, s); break;
+        case MASK_FLOAT: launch_bwd_m<Tr, D, MASK_FLOAT>(p, causal, s); break;
+        case MASK_BOOL: launch_bwd_m<Tr, D, MASK_BOOL>(p, causal, s); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <typename Tr>
-hipError_t launch_bwd_t(const BwdParams& p, int D, bool causal, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdParams& p, int D, bool causal, int mask, hipStream_t s) {
     switch (D) {
-        case 64: return launch_bwd_d<Tr, 64>(p, causal, s);
-        case 96: return launch_bwd_d<Tr, 96>(p, causal, s);
-        case 128: return launch_bwd_d<Tr, 128>(p, causal, s);
+        case 64: return launch_bwd_d<Tr, 64>(p, causal, mask, s);
+        case 96: return launch_bwd_d<Tr, 96>(p, causal, mask, s);
+        case 128: return launch_bwd_d<Tr, 128>(p, causal, mask, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_backward(const BwdParams& p, int D, bool causal, hipStream_t stream) {
-    return p.elem == ELEM_BF16 ? launch_bwd_t<BF16>(p, D, causal, stream)
-                               : launch_bwd_t<F16>(p, D, causal, stream);
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, hipStream_t stream) {
+    return p.elem == ELEM_BF16 ? launch_bwd_t<BF16>(p, D, causal, mask, stream)
+                               : launch_bwd_t<F16>(p, D, causal, mask, stream);
 }
 
 }  // namespace sdpa

@@ -278,7 +278,7 @@ sdpa_status paged_plan(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tenso
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 3; }
+int sdpa_abi_version(void) { return 4; }
 
 const char* sdpa_last_error(void) { return g_err; }
 
@@ -607,13 +607,16 @@ sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, con
 }
 
 sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
-                     const sdpa_tensor4* v, const sdpa_tensor4* out, const sdpa_tensor4* lse,
+                     const sdpa_tensor4* v, const sdpa_tensor4* attn_mask, sdpa_dtype mask_dtype,
+                     const sdpa_tensor4* out, const sdpa_tensor4* lse,
                      const sdpa_tensor4* dout, int is_causal, const double* scale, int enable_gqa,
                      const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
                      void* workspace, size_t workspace_bytes, void* stream) {
     Shapes s;
-    sdpa_status st = check_shapes(dtype, q, k, v, nullptr, enable_gqa, &s);
+    sdpa_status st = check_shapes(dtype, q, k, v, attn_mask, enable_gqa, &s);
     if (st != SDPA_OK) return st;
+    if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
     if (dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "the backward kernels take bf16 or fp16");
     if (!out || !lse || !dout || !dq || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv descriptors must not be NULL");
@@ -646,6 +649,11 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     if (s.L > 0 && !lse->data) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse data must not be NULL");
     const int64_t lse_sr = lse->size[2] > 1 ? lse->stride[2] : 1;
     if (lse_sr != 1) return fail(SDPA_ERR_UNSUPPORTED, "lse: the query dimension must have stride 1");
+    if (attn_mask) {
+        if (!attn_mask->data && s.S > 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask data is NULL");
+        if (s.S > 1 && attn_mask->stride[3] != 1)
+            return fail(SDPA_ERR_UNSUPPORTED, "attn_mask: the key dimension must have stride 1");
+    }
     double sc;
     if ((st = resolve_scale(scale, s.E, &sc)) != SDPA_OK) return st;
     const size_t need = bwd_workspace_bytes(s);
@@ -674,7 +682,19 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     p.n_ktiles = (int)((s.S + 127) / 128);
     p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16;
     p.scale = (float)sc;
-    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, (hipStream_t)stream);
+    int mask_kind = sdpa::MASK_NONE;
+    if (attn_mask) {
+        mask_kind = mask_dtype == SDPA_F32 ? sdpa::MASK_FLOAT : sdpa::MASK_BOOL;
+        p.mask = attn_mask->data;
+        p.m_sb = attn_mask->size[0] > 1 ? attn_mask->stride[0] : 0;
+        p.m_sh = attn_mask->size[1] > 1 ? attn_mask->stride[1] : 0;
+        p.m_sr = attn_mask->size[2] > 1 ? attn_mask->stride[2] : 0;
+        // vector loads: aligned runs, and whole vectors at the end of each row
+        const int64_t mvec = mask_dtype == SDPA_F32 ? 4 : 8, mal = mask_dtype == SDPA_F32 ? 16 : 8;
+        p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 && p.m_sh % mvec == 0 &&
+                     p.m_sr % mvec == 0 && s.S % mvec == 0;
+    }
+    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, mask_kind, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -76,8 +76,8 @@ def load_library():
     lib.sdpa_fwd_paged_workspace_size.argtypes = [ctypes.c_int, P, P, P, i32, ctypes.c_int, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_fwd_paged_workspace_size.restype = ctypes.c_int
-    lib.sdpa_bwd.argtypes = [ctypes.c_int, P, P, P, P, P, P, ctypes.c_int, ctypes.POINTER(dbl),
-                             ctypes.c_int, P, P, P, vp, ctypes.c_size_t, vp]
+    lib.sdpa_bwd.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, P, P, P, ctypes.c_int,
+                             ctypes.POINTER(dbl), ctypes.c_int, P, P, P, vp, ctypes.c_size_t, vp]
     lib.sdpa_bwd.restype = ctypes.c_int
     lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int, P, P, P, ctypes.c_int,
                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -276,17 +276,18 @@ def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
     return n.value
 
 
-def sdpa_bwd(query, key, value, out, lse, grad, is_causal=False, scale=None, enable_gqa=False,
-             workspace=None):
+def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False, scale=None,
+             enable_gqa=False, workspace=None):
     """Gradients of exact attention on the GPU: returns (grad_query, grad_key, grad_value).
 
-    ``out`` and ``lse`` are sdpa_fwd's results for the same arguments and
-    ``grad`` the gradient with respect to ``out`` (exactref.ai
-    "scaled_dot_product_attention.backward"; no mask).  The outputs have the
-    shapes and dtype of query, key and value.
+    ``out`` and ``lse`` are sdpa_fwd's results for the same arguments (the
+    optional float or bool ``attn_mask`` included) and ``grad`` the gradient
+    with respect to ``out`` (exactref.ai "scaled_dot_product_attention.backward";
+    the mask gets no gradient).  The outputs have the shapes and dtype of
+    query, key and value.
     """
     lib = load_library()
-    _require_gpu(query, key, value, out, lse, grad)
+    _require_gpu(query, key, value, out, lse, grad, attn_mask)
     if query.dtype not in (torch.float16, torch.bfloat16) or any(
             t.dtype != query.dtype for t in (key, value, out, grad)):
         raise ValueError("the backward takes float16 or bfloat16 query, key, value, out and grad")
@@ -297,6 +298,8 @@ def sdpa_bwd(query, key, value, out, lse, grad, is_causal=False, scale=None, ena
     Hkv, S, Ev = k4.shape[1], v4.shape[2], v4.shape[3]
     o4, g4 = _as4d(out), _as4d(grad)
     l4 = lse.reshape(B, Hq, L, 1)
+    m4, mdt = _mask_4d(attn_mask, q4, S)
+    dm = _desc(m4) if m4 is not None else None
     dev = query.device
     dq4 = torch.empty((B, Hq, L, E), dtype=query.dtype, device=dev)
     dk4 = torch.empty((B, Hkv, S, E), dtype=query.dtype, device=dev)
@@ -305,7 +308,8 @@ def sdpa_bwd(query, key, value, out, lse, grad, is_causal=False, scale=None, ena
         nbytes = sdpa_bwd_workspace_size(q4, k4, v4, enable_gqa)
         if workspace is None or workspace.numel() < nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        _check(lib.sdpa_bwd(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4), _desc(o4), _desc(l4),
+        _check(lib.sdpa_bwd(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4),
+                            ctypes.byref(dm) if dm is not None else None, mdt, _desc(o4), _desc(l4),
                             _desc(g4), int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)),
                             _desc(dq4), _desc(dk4), _desc(dv4), workspace.data_ptr(), nbytes,
                             _stream(dev)))
