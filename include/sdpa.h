@@ -253,6 +253,49 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_bwd_varlen -- gradients of packed variable-length attention (the
+ * block-diagonal mask of sdpa_fwd_varlen), as sdpa_bwd computes them for each
+ * segment on its own.
+ *
+ *   q, k, v, out, dout  packed (total, heads, head dim) tensors of dtype
+ *               (SDPA_BF16 or SDPA_F16) with token and head strides in
+ *               elements (multiples of 8, unit last stride, 16-byte aligned):
+ *               q, out, dout over total_q tokens and Hq heads, k, v over
+ *               total_k tokens and Hkv heads; out and lse from sdpa_fwd_varlen
+ *               with the same arguments; lse (Hq, total_q) float32 with head
+ *               stride lse_stride_head.
+ *   cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv,
+ *   E, Ev, total_q, total_k, is_causal, scale, enable_gqa
+ *               as for sdpa_fwd_varlen (DEVICE offsets; the maxima must bound
+ *               every segment's length: longer segments are cut to them);
+ *               E == Ev in {64, 96, 128}.
+ *   dq (total_q, Hq, E), dk (total_k, Hkv, E), dv (total_k, Hkv, Ev)
+ *               written for every token of a segment (tokens outside all
+ *               segments are not written); dk, dv summed over the query heads
+ *               of each key/value head.  They must not alias any input.
+ *   workspace   at least Hq * total_q * 4 + 256 bytes
+ *               (sdpa_bwd_varlen_workspace_size), owned by the caller.
+ */
+sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                            const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                            const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                            const void* out, int64_t o_stride_tok, int64_t o_stride_head,
+                            const float* lse, int64_t lse_stride_head,
+                            const void* dout, int64_t do_stride_tok, int64_t do_stride_head,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t n_seqs,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                            int32_t E, int32_t Ev, int64_t total_q, int64_t total_k, int is_causal,
+                            const double* scale, int enable_gqa,
+                            void* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
+                            void* dk, int64_t dk_stride_tok, int64_t dk_stride_head,
+                            void* dv, int64_t dv_stride_tok, int64_t dv_stride_head,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sdpa_bwd_varlen needs (Hq * total_q float32 values plus
+ * alignment).  Host only. */
+sdpa_status sdpa_bwd_varlen_workspace_size(int32_t Hq, int64_t total_q, size_t* bytes);
+
+/*
  * sdpa_bwd_workspace_size -- bytes of workspace sdpa_bwd needs for these
  * shapes (B * Hq * L float32 values, plus alignment).  Host only.
  */

@@ -244,3 +244,31 @@ def test_paged_plan_rules(lib):
     assert ws(E=64, Ev=128)[0] == S.SDPA_ERR_UNSUPPORTED
     assert ws(dtype=S.SDPA_F32)[0] == S.SDPA_ERR_UNSUPPORTED
     assert ws(splits=-1)[0] == S.SDPA_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_backward_argument_errors(lib):
+    def call(**kw):
+        a = dict(dtype=S.SDPA_BF16, ptr=FAKE, st=1024, sh=128, lse=FAKE, lsh=365, cq=FAKE, ck=FAKE, n=4,
+                 mq=200, mk=200, Hq=8, Hkv=8, E=128, Ev=128, tq=365, tk=365, causal=1, gqa=0, ws=FAKE,
+                 wsb=1 << 20)
+        a.update(kw)
+        p, st, sh = a["ptr"], a["st"], a["sh"]
+        return lib.sdpa_bwd_varlen(a["dtype"], p, st, sh, p, st, sh, p, st, sh, p, st, sh, a["lse"], a["lsh"],
+                                   p, st, sh, a["cq"], a["ck"], a["n"], a["mq"], a["mk"], a["Hq"], a["Hkv"],
+                                   a["E"], a["Ev"], a["tq"], a["tk"], a["causal"], None, a["gqa"],
+                                   p, st, sh, p, st, sh, p, st, sh, a["ws"], a["wsb"], None)
+    assert call(dtype=S.SDPA_F32) == S.SDPA_ERR_UNSUPPORTED
+    assert call(dtype=S.SDPA_BOOL) == S.SDPA_ERR_INVALID_ARGUMENT
+    assert call(Hkv=2) == S.SDPA_ERR_INVALID_ARGUMENT        # grouped heads need enable_gqa
+    assert call(Hkv=3, gqa=1) == S.SDPA_ERR_INVALID_ARGUMENT
+    assert call(cq=None) == S.SDPA_ERR_INVALID_ARGUMENT
+    assert call(E=128, Ev=64) == S.SDPA_ERR_UNSUPPORTED
+    assert call(E=80, Ev=80) == S.SDPA_ERR_UNSUPPORTED
+    assert call(ptr=FAKE + 8) == S.SDPA_ERR_UNSUPPORTED       # misaligned base
+    assert call(st=1020) == S.SDPA_ERR_UNSUPPORTED            # stride not a multiple of 8
+    assert call(wsb=8 * 365 * 4) == S.SDPA_ERR_INVALID_ARGUMENT   # workspace too small
+    assert call(n=-1) == S.SDPA_ERR_INVALID_ARGUMENT
+    assert call(n=0) == S.SDPA_OK                              # nothing to do
+    n = ctypes.c_size_t(0)
+    assert lib.sdpa_bwd_varlen_workspace_size(8, 365, ctypes.byref(n)) == S.SDPA_OK
+    assert n.value == 8 * 365 * 4 + 256

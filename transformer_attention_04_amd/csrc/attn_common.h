@@ -128,6 +128,13 @@ struct BwdParams {
     const void* mask;
     int64_t m_sb, m_sh, m_sr;
     int mask_vec;   // rows allow vector loads (16-byte float / 8-byte bool runs)
+    // Packed variable-length batches (cu_q non-null): B segments, row r of
+    // segment b is token cu_q[b] + r (keys: cu_k[b] + j) with the _sr strides
+    // per token; L, S bound the segment lengths; lse (h, token) at
+    // h * lse_sh + token; the D workspace laid out (h, token).
+    const int* cu_q;
+    const int* cu_k;
+    int64_t total_q, total_k;
 };
 
 hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
@@ -137,7 +144,7 @@ hipError_t launch_prefill_f16(const AttnParams& p, int D, bool causal, int mask,
 hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int elem, int D, hipStream_t stream);
-hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, bool varlen, hipStream_t stream);
 
 // Tile sizes the host needs for grids and workspace.
 constexpr int kPrefillBlockM = 128;  // query rows per MFMA workgroup

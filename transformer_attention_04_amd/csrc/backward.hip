@@ -73,20 +73,29 @@ __device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int c, int col0, 
 
 // ------------------------------------------------------------- D = dO . O
 
-template <int D>
+template <int D, bool VARLEN = false>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
-    // 16 lanes per row, 16 rows per workgroup; row index over (b, h, i)
+    // 16 lanes per row, 16 rows per workgroup; row index over (b, h, i), or
+    // (h, token) for packed batches
     const int tid = threadIdx.x;
     const int64_t row = (int64_t)blockIdx.x * 16 + tid / 16;
     const int c = tid & 15;
-    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
+    const int64_t nrows = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.L;
     float acc = 0.f;
     if (row < nrows && c < D / 8) {
-        const int i = (int)(row % p.L);
-        const int64_t bh = row / p.L;
-        const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-        const uint4 o = *(const uint4*)((const uint16_t*)p.o + b * p.o_sb + h * p.o_sh + i * p.o_sr + c * 8);
-        const uint4 g = *(const uint4*)((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + i * p.do_sr + c * 8);
+        uint4 o, g;
+        if constexpr (VARLEN) {
+            const int64_t t = row % p.total_q;
+            const int h = (int)(row / p.total_q);
+            o = *(const uint4*)((const uint16_t*)p.o + t * p.o_sr + h * p.o_sh + c * 8);
+            g = *(const uint4*)((const uint16_t*)p.dout + t * p.do_sr + h * p.do_sh + c * 8);
+        } else {
+            const int i = (int)(row % p.L);
+            const int64_t bh = row / p.L;
+            const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+            o = *(const uint4*)((const uint16_t*)p.o + b * p.o_sb + h * p.o_sh + i * p.o_sr + c * 8);
+            g = *(const uint4*)((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + i * p.do_sr + c * 8);
+        }
         const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -145,9 +154,23 @@ __device__ __forceinline__ uint32_t bwd_mask8(__amdgpu_buffer_rsrc_t r, int off,
     }
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
+// Segment b of a packed batch: first row a and key c, lengths Lb and Sb
+// (offsets clamped to the packed totals, lengths to the launch's L and S).
+__device__ __forceinline__ void bwd_segment(const BwdParams& p, int b, int64_t& a, int& Lb, int64_t& c, int& Sb) {
+    const int64_t a0 = min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
+    const int64_t e0 = min(max((int64_t)p.cu_q[b + 1], a0), p.total_q);
+    const int64_t c0 = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
+    const int64_t d0 = min(max((int64_t)p.cu_k[b + 1], c0), p.total_k);
+    a = a0;
+    c = c0;
+    Lb = (int)min(e0 - a0, (int64_t)p.L);
+    Sb = (int)min(d0 - c0, (int64_t)p.S);
+}
+
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool VARLEN = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
+    static_assert(!(VARLEN && MASK != MASK_NONE), "packed batches take no mask");
     constexpr int BM = 128, BN = 64;
     constexpr int RS = D + 8;            // LDS row stride, 16-bit words
     constexpr int TILE = BN * RS;        // one K or V block
@@ -164,20 +187,26 @@ void bwd_dq_kernel(BwdParams p) {
     const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest (causal) first
     const int bh = (int)(blockIdx.x % nbh);
     const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.group;
+    int Lb = p.L, Sb = p.S;
+    int64_t qa = 0, kc = 0;  // packed batches: first token of segment b's rows and keys
+    if constexpr (VARLEN) bwd_segment(p, b, qa, Lb, kc, Sb);
+    const int64_t q_b = VARLEN ? qa * p.q_sr : b * p.q_sb, do_b = VARLEN ? qa * p.do_sr : b * p.do_sb;
+    const int64_t k_b = VARLEN ? kc * p.k_sr : b * p.k_sb, v_b = VARLEN ? kc * p.v_sr : b * p.v_sb;
+    const int64_t dq_b = VARLEN ? qa * p.dq_sr : b * p.dq_sb;
     const int q0 = qt * BM;
-    if (q0 >= p.L) return;
-    const int qrows = min(BM, p.L - q0);
+    if (q0 >= Lb) return;
+    const int qrows = min(BM, Lb - q0);
     const int wrow0 = wave * 32;
     const int my_row = q0 + wrow0 + lq;
     const bool wave_has_rows = wrow0 < qrows;
-    const int kend = CAUSAL ? min(p.S, q0 + BM) : p.S;
+    const int kend = CAUSAL ? min(Sb, q0 + BM) : Sb;
     const int ntiles = (kend + BN - 1) / BN;
 
     // Q^T and dO^T operands (lane: query lq, elements 16kk + 8hh .. +7)
     const int q_rs = (int)(p.q_sr * 2), do_rs = (int)(p.do_sr * 2);
-    const auto qrs = make_rsrc((const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)q0 * p.q_sr,
+    const auto qrs = make_rsrc((const uint16_t*)p.q + q_b + h * p.q_sh + (int64_t)q0 * p.q_sr,
                                (qrows - 1) * q_rs + D * 2);
-    const auto gdrs = make_rsrc((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)q0 * p.do_sr,
+    const auto gdrs = make_rsrc((const uint16_t*)p.dout + do_b + h * p.do_sh + (int64_t)q0 * p.do_sr,
                                 (qrows - 1) * do_rs + D * 2);
     const int lrow = wrow0 + lq;
     uint4 qreg[NKK], dreg[NKK];
@@ -186,9 +215,10 @@ void bwd_dq_kernel(BwdParams p) {
         qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
         dreg[kk] = buf_load16(gdrs, lrow * do_rs + (kk * 16 + hh * 8) * 2);
     }
-    const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
-    const bool row_ok = my_row < p.L;
-    float lse2 = row_ok ? p.lse[b * p.lse_sb + h * p.lse_sh + my_row] * kLog2e : 0.f;
+    const int64_t rowid = VARLEN ? (int64_t)h * p.total_q + qa : ((int64_t)b * p.Hq + h) * p.L;
+    const int64_t lse_b = VARLEN ? h * p.lse_sh + qa : b * p.lse_sb + h * p.lse_sh;
+    const bool row_ok = my_row < Lb;
+    float lse2 = row_ok ? p.lse[lse_b + my_row] * kLog2e : 0.f;
     // a masked row with no kept key (lse -inf) has P = 0: exp2(-inf - 0)
     if (MASK != MASK_NONE && lse2 == kNegInf) lse2 = 0.f;
     const float drow = row_ok ? p.dsum[rowid + my_row] : 0.f;
@@ -202,12 +232,12 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
-    const uint16_t* kbase = (const uint16_t*)p.k + b * p.k_sb + kvh * p.k_sh;
-    const uint16_t* vbase = (const uint16_t*)p.v + b * p.v_sb + kvh * p.v_sh;
+    const uint16_t* kbase = (const uint16_t*)p.k + k_b + kvh * p.k_sh;
+    const uint16_t* vbase = (const uint16_t*)p.v + v_b + kvh * p.v_sh;
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
     uint4 kbuf[NCH_T], vbuf[NCH_T];
     auto load_tile = [&](int key0) {
-        const int rows = min(BN, p.S - key0);
+        const int rows = min(BN, Sb - key0);
         const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, (rows - 1) * k_rs + D * 2);
         const auto vr = make_rsrc(vbase + (int64_t)key0 * p.v_sr, (rows - 1) * v_rs + D * 2);
 #pragma unroll
@@ -251,8 +281,8 @@ void bwd_dq_kernel(BwdParams p) {
                     dp[kb] = Tr::mfma32(as_vec8<Tr>(va), as_vec8<Tr>(dreg[kk]), dp[kb]);
                 }
             // register r of block kb: key key0 + 32kb + 16(r/8) + 8hh + r%8, query my_row
-            const bool edge = (key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
-            int lim = p.S - (key0 + hh * 8);
+            const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
+            int lim = Sb - (key0 + hh * 8);
             if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
             uint4 pb[4];
             constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;  // bytes per mask element
@@ -261,7 +291,7 @@ void bwd_dq_kernel(BwdParams p) {
                 MASK == MASK_NONE ? p.mask
                                   : (const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
                                                            (int64_t)(q0 + wrow0) * p.m_sr + key0) * MES,
-                MASK == MASK_NONE ? 0 : ((qrows - 1 - wrow0) * (int)p.m_sr + (p.S - key0)) * MES);
+                MASK == MASK_NONE ? 0 : ((qrows - 1 - wrow0) * (int)p.m_sr + (Sb - key0)) * MES);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 float ds[16];
@@ -309,7 +339,7 @@ void bwd_dq_kernel(BwdParams p) {
 
     // dQ = scale * dQ^T, rounded to nearest-even; lane: query lrow, e = 32db + 8g + 4hh + 0..3
     const int dq_rs = (int)(p.dq_sr * 2);
-    const auto ors = make_rsrc((uint16_t*)p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)q0 * p.dq_sr,
+    const auto ors = make_rsrc((uint16_t*)p.dq + dq_b + h * p.dq_sh + (int64_t)q0 * p.dq_sr,
                                (qrows - 1) * dq_rs + D * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -329,9 +359,10 @@ void bwd_dq_kernel(BwdParams p) {
 // wavefronts 0-3 own dK (S, dP, dS, dK^T += Q^T dS), wavefronts 4-7 own dV
 // (S, P, dV^T += dO^T P).  Each role fits two wavefronts per SIMD; S is
 // computed by both roles.
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool VARLEN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
+    static_assert(!(VARLEN && MASK != MASK_NONE), "packed batches take no mask");
     constexpr int BK = 128, BN = 64;     // keys per workgroup, queries per step
     constexpr int NT = 512;
     constexpr int RS = D + 8;
@@ -350,18 +381,23 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int kt = (int)(blockIdx.x / nbh);   // lowest key tiles (most causal work) first
     const int bkv = (int)(blockIdx.x % nbh);
     const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
+    int Lb = p.L, Sb = p.S;
+    int64_t qa = 0, kc = 0;  // packed batches: first token of segment b's rows and keys
+    if constexpr (VARLEN) bwd_segment(p, b, qa, Lb, kc, Sb);
+    const int64_t q_b = VARLEN ? qa * p.q_sr : b * p.q_sb, do_b = VARLEN ? qa * p.do_sr : b * p.do_sb;
+    const int64_t k_b = VARLEN ? kc * p.k_sr : b * p.k_sb, v_b = VARLEN ? kc * p.v_sr : b * p.v_sb;
     const int k0 = kt * BK;
-    if (k0 >= p.S) return;
-    const int krows = min(BK, p.S - k0);
+    if (k0 >= Sb) return;
+    const int krows = min(BK, Sb - k0);
     const int wkey0 = k0 + kw * 32;            // first key of this wavefront
     const int my_key = wkey0 + lq;
     const bool wave_has_keys = kw * 32 < krows;
 
     // K^T (and for dK, V^T) operands (lane: key lq, elements 16kk + 8hh .. +7)
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
-    const auto krs = make_rsrc((const uint16_t*)p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)k0 * p.k_sr,
+    const auto krs = make_rsrc((const uint16_t*)p.k + k_b + kvh * p.k_sh + (int64_t)k0 * p.k_sr,
                                (krows - 1) * k_rs + D * 2);
-    const auto vrs = make_rsrc((const uint16_t*)p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)k0 * p.v_sr,
+    const auto vrs = make_rsrc((const uint16_t*)p.v + v_b + kvh * p.v_sh + (int64_t)k0 * p.v_sr,
                                (krows - 1) * v_rs + D * 2);
     const int lkey = kw * 32 + lq;
     uint4 kreg[NKK], vreg[NKK];
@@ -379,7 +415,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     // query blocks this workgroup visits: causal keeps query i >= key j
     const int qb0 = CAUSAL ? k0 / BN : 0;
-    const int nqb = (p.L + BN - 1) / BN;
+    const int nqb = (Lb + BN - 1) / BN;
     const int nsteps = p.group * max(0, nqb - qb0);  // (query head, query block) pairs
 
     const int q_rs = (int)(p.q_sr * 2), do_rs = (int)(p.do_sr * 2);
@@ -392,10 +428,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto load_tile = [&](int st) {
         int h, qrow0;
         step_coords(st, h, qrow0);
-        const int rows = min(BN, p.L - qrow0);
-        const auto qr = make_rsrc((const uint16_t*)p.q + b * p.q_sb + h * p.q_sh + (int64_t)qrow0 * p.q_sr,
+        const int rows = min(BN, Lb - qrow0);
+        const auto qr = make_rsrc((const uint16_t*)p.q + q_b + h * p.q_sh + (int64_t)qrow0 * p.q_sr,
                                   (rows - 1) * q_rs + D * 2);
-        const auto gr = make_rsrc((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + (int64_t)qrow0 * p.do_sr,
+        const auto gr = make_rsrc((const uint16_t*)p.dout + do_b + h * p.do_sh + (int64_t)qrow0 * p.do_sr,
                                   (rows - 1) * do_rs + D * 2);
 #pragma unroll
         for (int i = 0; i < NCH_T; ++i) {
@@ -408,8 +444,9 @@ void bwd_dkdv_kernel(BwdParams p) {
         if (tid < BN) {
             // raw values (range-checked loads read 0 past the last row); scaled
             // when stored, so that nothing here waits for the loads
-            const int64_t rowid = ((int64_t)b * p.Hq + h) * p.L;
-            const auto lr = make_rsrc(p.lse + b * p.lse_sb + h * p.lse_sh + qrow0, rows * 4);
+            const int64_t rowid = VARLEN ? (int64_t)h * p.total_q + qa : ((int64_t)b * p.Hq + h) * p.L;
+            const int64_t lse_b = VARLEN ? h * p.lse_sh + qa : b * p.lse_sb + h * p.lse_sh;
+            const auto lr = make_rsrc(p.lse + lse_b + qrow0, rows * 4);
             const auto dr = make_rsrc(p.dsum + rowid + qrow0, rows * 4);
             lbuf = __uint_as_float(buf_load4(lr, tid * 4));
             dbuf = __uint_as_float(buf_load4(dr, tid * 4));
@@ -457,10 +494,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                 uint32_t mk = ~0u;
                 if constexpr (MASK != MASK_NONE) {
                     constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
-                    const int qf = qrow0 + qb * 32, nq = p.L - qf;
+                    const int qf = qrow0 + qb * 32, nq = Lb - qf;
                     const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
                                                                      (int64_t)qf * p.m_sr + wkey0) * MES,
-                                              nq > 0 ? ((nq - 1) * (int)p.m_sr + (p.S - wkey0)) * MES : 0);
+                                              nq > 0 ? ((nq - 1) * (int)p.m_sr + (Sb - wkey0)) * MES : 0);
                     mk = 0;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -486,7 +523,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                 }
                 // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
                 const int qbase = qb * 32 + 8 * hh;
-                const bool edge = (qrow0 + BN > p.L) || (CAUSAL && qrow0 < wkey0 + 31);
+                const bool edge = (qrow0 + BN > Lb) || (CAUSAL && qrow0 < wkey0 + 31);
                 float w[16];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -511,7 +548,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                         if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
                         if (edge) {
                             const int qi = qrow0 + qbase + 16 * half + j;
-                            const bool keep = qi < p.L && (!CAUSAL || qi >= my_key);
+                            const bool keep = qi < Lb && (!CAUSAL || qi >= my_key);
                             e = keep ? e : 0.f;
                         }
                         w[r] = role == 0 ? e * (dp[r] - dv8[j]) : e;  // dS or P
@@ -546,7 +583,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     void* obase = role == 0 ? p.dk : p.dv;
     const int64_t o_sb = role == 0 ? p.dk_sb : p.dv_sb, o_sh = role == 0 ? p.dk_sh : p.dv_sh;
     const int64_t o_sr = role == 0 ? p.dk_sr : p.dv_sr;
-    const auto ors = make_rsrc((uint16_t*)obase + b * o_sb + kvh * o_sh + (int64_t)k0 * o_sr,
+    const auto ors = make_rsrc((uint16_t*)obase + (VARLEN ? kc * o_sr : b * o_sb) + kvh * o_sh + (int64_t)k0 * o_sr,
                                (krows - 1) * o_rs + D * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -560,31 +597,41 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK>
+template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
 void launch_bwd_grads(const BwdParams& p, hipStream_t s) {
     if ((int64_t)p.B * p.Hq * p.L > 0) {
         const unsigned g = (unsigned)p.n_qtiles * p.Hq * p.B;
-        hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, CAUSAL, MASK>), dim3(g), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(g), dim3(256), 0, s, p);
     }
     if ((int64_t)p.S * p.Hkv * p.B > 0) {
         const unsigned g = (unsigned)p.n_ktiles * p.Hkv * p.B;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK>), dim3(g), dim3(512), 0, s, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(g), dim3(512), 0, s, p);
     }
 }
 
-template <typename Tr, int D, int MASK>
+template <typename Tr, int D, int MASK, bool VARLEN = false>
 void launch_bwd_m(const BwdParams& p, bool causal, hipStream_t s) {
     if (causal)
-        launch_bwd_grads<Tr, D, true, MASK>(p, s);
+        launch_bwd_grads<Tr, D, true, MASK, VARLEN>(p, s);
     else
-        launch_bwd_grads<Tr, D, false, MASK>(p, s);
+        launch_bwd_grads<Tr, D, false, MASK, VARLEN>(p, s);
 }
 
 template <typename Tr, int D>
-hipError_t launch_bwd_d(const BwdParams& p, bool causal, int mask, hipStream_t s) {
-    const int64_t nrows = (int64_t)p.B * p.Hq * p.L;
-    if (nrows > 0)
-        hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, p);
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
+    const int64_t nrows = varlen ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.L;
+    if (nrows > 0) {
+        const dim3 grid((unsigned)((nrows + 15) / 16));
+        if (varlen)
+            hipLaunchKernelGGL((bwd_dot_kernel<D, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((bwd_dot_kernel<D>), grid, dim3(256), 0, s, p);
+    }
+    if (varlen) {
+        if (mask != MASK_NONE) return hipErrorInvalidValue;
+        launch_bwd_m<Tr, D, MASK_NONE, true>(p, causal, s);
+        return hipGetLastError();
+    }
     switch (mask) {
         case MASK_NONE: launch_bwd_m<Tr, D, MASK_NONE>(p, causal, s); break;
         case MASK_FLOAT: launch_bwd_m<Tr, D, MASK_FLOAT>(p, causal, s); break;
@@ -595,20 +642,20 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, int mask, hipStream_t s
 }
 
 template <typename Tr>
-hipError_t launch_bwd_t(const BwdParams& p, int D, bool causal, int mask, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdParams& p, int D, bool causal, int mask, bool varlen, hipStream_t s) {
     switch (D) {
-        case 64: return launch_bwd_d<Tr, 64>(p, causal, mask, s);
-        case 96: return launch_bwd_d<Tr, 96>(p, causal, mask, s);
-        case 128: return launch_bwd_d<Tr, 128>(p, causal, mask, s);
+        case 64: return launch_bwd_d<Tr, 64>(p, causal, mask, varlen, s);
+        case 96: return launch_bwd_d<Tr, 96>(p, causal, mask, varlen, s);
+        case 128: return launch_bwd_d<Tr, 128>(p, causal, mask, varlen, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, hipStream_t stream) {
-    return p.elem == ELEM_BF16 ? launch_bwd_t<BF16>(p, D, causal, mask, stream)
-                               : launch_bwd_t<F16>(p, D, causal, mask, stream);
+hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, bool varlen, hipStream_t stream) {
+    return p.elem == ELEM_BF16 ? launch_bwd_t<BF16>(p, D, causal, mask, varlen, stream)
+                               : launch_bwd_t<F16>(p, D, causal, mask, varlen, stream);
 }
 
 }  // namespace sdpa

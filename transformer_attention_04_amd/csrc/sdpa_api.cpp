@@ -694,7 +694,94 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
         p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 && p.m_sh % mvec == 0 &&
                      p.m_sr % mvec == 0 && s.S % mvec == 0;
     }
-    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, mask_kind, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, mask_kind, false, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sdpa_status sdpa_bwd_varlen_workspace_size(int32_t Hq, int64_t total_q, size_t* bytes) {
+    if (!bytes) return fail(SDPA_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+    if (Hq < 0 || total_q < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    *bytes = (size_t)Hq * (size_t)total_q * sizeof(float) + 256;
+    return ok();
+}
+
+sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                            const void* k, int64_t k_stride_tok, int64_t k_stride_head, const void* v,
+                            int64_t v_stride_tok, int64_t v_stride_head, const void* out, int64_t o_stride_tok,
+                            int64_t o_stride_head, const float* lse, int64_t lse_stride_head, const void* dout,
+                            int64_t do_stride_tok, int64_t do_stride_head, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t n_seqs, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t E, int32_t Ev,
+                            int64_t total_q, int64_t total_k, int is_causal, const double* scale,
+                            int enable_gqa, void* dq, int64_t dq_stride_tok, int64_t dq_stride_head,
+                            void* dk, int64_t dk_stride_tok, int64_t dk_stride_head, void* dv,
+                            int64_t dv_stride_tok, int64_t dv_stride_head, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16)
+        return fail(dtype == SDPA_F32 ? SDPA_ERR_UNSUPPORTED : SDPA_ERR_INVALID_ARGUMENT,
+                    "the backward kernels take bf16 or fp16");
+    if (n_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq < 0 || Hkv < 0 || E < 0 || Ev < 0 ||
+        total_q < 0 || total_k < 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    if (Hq != Hkv) {
+        if (!enable_gqa)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query has %d heads and key/value %d: pass enable_gqa",
+                        Hq, Hkv);
+        if (Hkv == 0 || Hq % Hkv != 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query heads (%d) must be a multiple of key/value heads (%d)",
+                        Hq, Hkv);
+    }
+    if (n_seqs == 0 || Hq == 0 || (total_q == 0 && total_k == 0)) return ok();
+    if (!cu_seqlens_q || !cu_seqlens_k)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must not be NULL");
+    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %d and %d)", E, Ev);
+    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d is not one of 64, 96, 128", E);
+    const void* ptrs[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (int i = 0; i < 8; ++i) {
+        const bool need = (i == 1 || i == 2 || i == 6 || i == 7) ? total_k > 0 : total_q > 0;
+        if (need && !ptrs[i]) return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
+    }
+    if (total_q > 0 && !lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must not be NULL");
+    const int64_t vec = 16 / elem_bytes(dtype);
+    const int64_t strides[16] = {q_stride_tok, q_stride_head, k_stride_tok, k_stride_head, v_stride_tok,
+                                 v_stride_head, o_stride_tok, o_stride_head, do_stride_tok, do_stride_head,
+                                 dq_stride_tok, dq_stride_head, dk_stride_tok, dk_stride_head, dv_stride_tok,
+                                 dv_stride_head};
+    for (int i = 0; i < 16; ++i)
+        if (strides[i] % vec != 0)
+            return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
+    double sc;
+    sdpa_status st;
+    if ((st = resolve_scale(scale, E, &sc)) != SDPA_OK) return st;
+    const size_t need = (size_t)Hq * (size_t)total_q * sizeof(float) + 256;
+    if (workspace_bytes < need || !workspace)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes needed, %zu given", need,
+                    workspace_bytes);
+    sdpa::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout; p.lse = lse;
+    p.dsum = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.q_sr = q_stride_tok; p.q_sh = q_stride_head;
+    p.k_sr = k_stride_tok; p.k_sh = k_stride_head;
+    p.v_sr = v_stride_tok; p.v_sh = v_stride_head;
+    p.o_sr = o_stride_tok; p.o_sh = o_stride_head;
+    p.do_sr = do_stride_tok; p.do_sh = do_stride_head;
+    p.dq_sr = dq_stride_tok; p.dq_sh = dq_stride_head;
+    p.dk_sr = dk_stride_tok; p.dk_sh = dk_stride_head;
+    p.dv_sr = dv_stride_tok; p.dv_sh = dv_stride_head;
+    p.lse_sh = lse_stride_head;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+    p.total_q = total_q; p.total_k = total_k;
+    p.B = n_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+    p.L = max_seqlen_q; p.S = max_seqlen_k;
+    p.n_qtiles = (max_seqlen_q + 127) / 128;
+    p.n_ktiles = (max_seqlen_k + 127) / 128;
+    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16;
+    p.scale = (float)sc;
+    hipError_t e = sdpa::launch_backward(p, E, is_causal != 0, sdpa::MASK_NONE, true, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }

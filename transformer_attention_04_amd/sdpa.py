@@ -21,7 +21,8 @@ SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 _DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
 
 EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_fwd_paged",
-            "sdpa_fwd_paged_workspace_size", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_last_error",
+            "sdpa_fwd_paged_workspace_size", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_bwd_varlen",
+            "sdpa_bwd_varlen_workspace_size", "sdpa_last_error",
             "sdpa_abi_version")
 
 
@@ -82,6 +83,13 @@ def load_library():
     lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int, P, P, P, ctypes.c_int,
                                             ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_int
+    lib.sdpa_bwd_varlen.argtypes = ([ctypes.c_int] + [vp, i64, i64] * 4 + [vp, i64] + [vp, i64, i64]
+                                    + [vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, i64, ctypes.c_int,
+                                       ctypes.POINTER(dbl), ctypes.c_int] + [vp, i64, i64] * 3
+                                    + [vp, ctypes.c_size_t, vp])
+    lib.sdpa_bwd_varlen.restype = ctypes.c_int
+    lib.sdpa_bwd_varlen_workspace_size.argtypes = [i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sdpa_bwd_varlen_workspace_size.restype = ctypes.c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_abi_version.argtypes = []
@@ -314,6 +322,62 @@ def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False,
                             _desc(dq4), _desc(dk4), _desc(dv4), workspace.data_ptr(), nbytes,
                             _stream(dev)))
     return dq4.reshape(query.shape), dk4.reshape(key.shape), dv4.reshape(value.shape)
+
+
+def sdpa_bwd_varlen(q, k, v, out, lse, grad, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
+                    max_seqlen_k=None, is_causal=False, scale=None, enable_gqa=False, workspace=None):
+    """Gradients of packed variable-length attention (sdpa_fwd_varlen's block-
+    diagonal mask): returns (grad_q, grad_k, grad_v) shaped like q, k, v.
+
+    Layouts as for sdpa_fwd_varlen: q, k, v, out and grad (total, heads, head
+    dim) or (1, total, heads, head dim); lse (Hq, total_q) or (1, Hq, total_q)
+    as sdpa_fwd_varlen returns it.
+    """
+    lib = load_library()
+    _require_gpu(q, k, v, out, lse, grad, cu_seqlens_q, cu_seqlens_k)
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in (k, v, out, grad)):
+        raise ValueError("the backward takes float16 or bfloat16 q, k, v, out and grad")
+    batched = q.dim() == 4
+    q3, k3, v3, o3, g3 = (t[0] if t.dim() == 4 else t for t in (q, k, v, out, grad))
+    l2 = lse[0] if lse.dim() == 3 else lse
+    if cu_seqlens_k is None:
+        cu_seqlens_k = cu_seqlens_q
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 device tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    n_seqs = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None or max_seqlen_k is None:
+        cq, ck = cu_seqlens_q.cpu().long(), cu_seqlens_k.cpu().long()
+        max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if n_seqs > 0 else 0
+        max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if n_seqs > 0 else 0
+    total_q, Hq, E = q3.shape
+    total_k, Hkv, _ = k3.shape
+    Ev = v3.shape[2]
+    for t in (q3, k3, v3, o3, g3, l2):
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("the last dimension must have stride 1")
+    dev = q.device
+    dq3 = torch.empty((total_q, Hq, E), dtype=q.dtype, device=dev)
+    dk3 = torch.empty((total_k, Hkv, E), dtype=q.dtype, device=dev)
+    dv3 = torch.empty((total_k, Hkv, Ev), dtype=q.dtype, device=dev)
+    with torch.cuda.device(dev):
+        n = ctypes.c_size_t(0)
+        _check(lib.sdpa_bwd_varlen_workspace_size(Hq, total_q, ctypes.byref(n)))
+        if workspace is None or workspace.numel() < n.value:
+            workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+        _check(lib.sdpa_bwd_varlen(
+            _DTYPE[q.dtype], q3.data_ptr(), q3.stride(0), q3.stride(1), k3.data_ptr(), k3.stride(0), k3.stride(1),
+            v3.data_ptr(), v3.stride(0), v3.stride(1), o3.data_ptr(), o3.stride(0), o3.stride(1),
+            l2.data_ptr(), l2.stride(0), g3.data_ptr(), g3.stride(0), g3.stride(1),
+            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_q), int(max_seqlen_k),
+            Hq, Hkv, E, Ev, total_q, total_k, int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)),
+            dq3.data_ptr(), dq3.stride(0), dq3.stride(1), dk3.data_ptr(), dk3.stride(0), dk3.stride(1),
+            dv3.data_ptr(), dv3.stride(0), dv3.stride(1), workspace.data_ptr(), n.value, _stream(dev)))
+    if batched:
+        return dq3.unsqueeze(0), dk3.unsqueeze(0), dv3.unsqueeze(0)
+    return dq3, dk3, dv3
 
 
 def sdpa_fwd_bmhk(query, key, value, is_causal=False, scale=None, num_splits=0):
