@@ -454,9 +454,10 @@ def _bool_mask(shape, seed, keep=0.7):
     ("fp16", 128, False, 129, 144, 2, 2, 2, "batch"),
     ("bf16", 64, False, 64, 4096, 1, 2, 2, "full"),
 ])
-def test_bool_mask_aligned_rows(dtype, E, causal, L, Sk, B, Hq, Hkv, mshape):
-    """Bool masks with aligned rows (8-byte mask loads): random keep patterns
-    with fully masked rows, broadcast shapes, GQA, causal, ragged query tiles."""
+def test_bool_mask_eight_wave(dtype, E, causal, L, Sk, B, Hq, Hkv, mshape):
+    """Bool masks whose rows are whole 16-byte chunks (key count a multiple of
+    16) run on the eight-wave kernel: random keep patterns with fully masked
+    rows, broadcast shapes, GQA, causal, ragged query tiles."""
     q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), dtype, seed=E + L)
     shape = {"full": (B, Hq, L, Sk), "head": (1, Hq, L, Sk), "row": (1, 1, L, Sk), "batch": (B, 1, 1, Sk)}[mshape]
     m = _bool_mask(shape, L + Sk)
@@ -470,12 +471,12 @@ def test_bool_mask_aligned_rows(dtype, E, causal, L, Sk, B, Hq, Hkv, mshape):
         assert_parity(*r, dtype, f"bool {mshape} scale={scale}")
 
 
-def test_bool_mask_vector_and_byte_loads_agree():
-    """The same bool mask once with aligned rows (8-byte loads) and once as a
-    view with a row stride of S + 4 (byte loads)."""
+def test_bool_mask_same_result_on_both_kernels():
+    """The same bool mask once with 16-byte rows (eight-wave kernel) and once
+    as a view with a row stride of S + 8 (four-wave kernel)."""
     q, k, v = inputs.randn_qkv((1, 4, 300, 128), (1, 4, 320, 128), (1, 4, 320, 128), "bf16", seed=12)
     m = _bool_mask((1, 4, 300, 320), 13)
-    wide = torch.zeros((1, 4, 300, 324), dtype=torch.bool)
+    wide = torch.zeros((1, 4, 300, 328), dtype=torch.bool)
     wide[..., :320] = m
     outs = []
     for mm in (m.to(DEV), wide.to(DEV)[..., :320]):
@@ -484,7 +485,7 @@ def test_bool_mask_vector_and_byte_loads_agree():
         outs.append((o, l))
     ro, rl = O.sdpa(q, k, v, attn_mask=m, is_causal=True)
     for o, l in outs:
-        assert_parity(o, l, ro, rl, "bf16", "bool mask, vector and byte loads")
+        assert_parity(o, l, ro, rl, "bf16", "bool mask, both kernels")
     l0, l1 = outs[0][1].cpu(), outs[1][1].cpu()
     fin = torch.isfinite(l0)
     assert torch.equal(fin, torch.isfinite(l1)) and torch.equal(l0[~fin], l1[~fin])

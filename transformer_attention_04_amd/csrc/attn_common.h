@@ -39,7 +39,7 @@ struct AttnParams {
     int Hq, Hkv, group;     // group = Hq / Hkv
     int L, S;               // batched: lengths; varlen: max segment lengths
     int n_qtiles;
-    int mask_vec;           // mask rows are aligned for vector loads
+    int mask_vec;           // bit 0: vector mask loads allowed; bit 1: bool rows in whole 16-byte chunks
     int neg;                // the scale is negative: q is negated on load
     int dv;                 // value head dim Ev (== E except on the four-wave batched path)
     float scale_abs;        // |scale|

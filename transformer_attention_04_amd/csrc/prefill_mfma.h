@@ -539,6 +539,12 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
             return causal ? launch_prefill_one<Tr, D, D, true, MASK_FLOAT, false>(p, s)
                           : launch_prefill_one<Tr, D, D, false, MASK_FLOAT, false>(p, s);
         case MASK_BOOL:
+            // the eight-wave kernel moves the mask in 16-byte chunks of whole
+            // rows (bit 1 of mask_vec) and needs a positive scale (masked
+            // scores are -inf before the scale is applied)
+            if ((p.mask_vec & 2) && p.scale_log2 > 0.f)
+                return causal ? launch_prefill_pp<Tr, D, true, MASK_BOOL>(p, s)
+                              : launch_prefill_pp<Tr, D, false, MASK_BOOL>(p, s);
             return causal ? launch_prefill_one<Tr, D, D, true, MASK_BOOL, false>(p, s)
                           : launch_prefill_one<Tr, D, D, false, MASK_BOOL, false>(p, s);
     }

@@ -75,6 +75,12 @@
 // 16-byte reads of 16 rows fall in distinct banks.  The 64 KB this takes
 // come from the Q^T staging area: Q^T is loaded into registers at each tile
 // start instead.  Causal and edge masking are applied after the bias.
+//
+// Bool mask (MASK_BOOL; rows in whole 16-byte chunks, positive scale): the
+// same cursor moves the wave's 32 rows x 64 keys of mask bytes (2 KB) in two
+// direct-to-LDS loads per block; each lane reads 8 bytes per 16-key chunk
+// (conflict-free: a load's lane order puts row r's chunk c at (16c + r%16) *
+// 16) and sets the scores of masked keys to -inf before the row maximum.
 #pragma once
 
 #include "attn_common.h"
@@ -184,21 +190,26 @@ template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr bool FMASK = MASK == MASK_FLOAT;
+    constexpr bool BMASK = MASK == MASK_BOOL;
+    constexpr bool ANYMASK = FMASK || BMASK;
     constexpr int BM = kPPBlockM;
     constexpr int BN = 64;
     constexpr int NC = D / 8;          // 16-byte chunks per row
     constexpr int KTILE = BN * D;      // one K or V block, 16-bit words
     constexpr int NSTAGE = 3;          // ring of K/V stages
     constexpr int STAGE = 2 * KTILE;   // K block then V block
-    constexpr int QAREA = FMASK ? 0 : BM * D;   // Q^T of the next tile, 16-bit words
-    constexpr int BAREA = FMASK ? 8 * 32 * BN * 2 : 0;  // bias of one block per wave (fp32), 16-bit words
+    constexpr int QAREA = ANYMASK ? 0 : BM * D;   // Q^T of the next tile, 16-bit words
+    // mask of one block per wave (fp32 bias or bool bytes), 16-bit words
+    constexpr int MBYTES = FMASK ? 4 : 1;                 // bytes per mask element
+    constexpr int WAREA = 32 * BN * MBYTES;               // bytes per wave
+    constexpr int BAREA = ANYMASK ? 8 * WAREA / 2 : 0;
     constexpr int NKK = D / 16;        // k-steps of the score product
     constexpr int NDB = D / 32;        // 32-row blocks of O^T
     constexpr int NDMA = NC / 4;       // direct-to-LDS loads per wave per block
     constexpr int NQDMA = NC / 2;      // direct-to-LDS loads per wave per Q tile
-    constexpr int NBDMA = 8;           // direct-to-LDS loads per wave per bias block
+    constexpr int NBDMA = BMASK ? 2 : 8;   // direct-to-LDS loads per wave per mask block
+    constexpr int NBRD = BMASK ? 4 : 8;    // mask reads per lane per block
     static_assert(D == 64 || D == 96 || D == 128, "head dim must be 64, 96 or 128");
-    static_assert(MASK == MASK_NONE || MASK == MASK_FLOAT, "no boolean masks here");
     static_assert(2 * NKK == 4 * NDB, "one K operand read per P.V product");
     static_assert((NSTAGE * STAGE + QAREA + BAREA) * 2 <= 160 * 1024, "LDS budget");
 
@@ -329,8 +340,11 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     // Load i, lane m: row 4i + m/16 of the wave's 32, chunk (m%16) ^ (row%16)
     // of the row's 16 chunks of 4 keys; relative to row 16(i/4), the lane's
     // byte offset depends on i only through i%4.
-    const uint32_t b_lds = smem_addr + (uint32_t)((NSTAGE * STAGE + QAREA) * 2 + wave * 8192);
-    const int m_rs = (int)(p.m_sr * 4);
+    // Bool mask: the same cursor moves 32 rows x 64 bytes per block in two
+    // loads; load i, lane m: row 16i + m%16, 16-byte chunk m/16 (keys
+    // 16(m/16) .. +15), so the chunk a lane reads sits at (chunk*16 + row%16)*16.
+    const uint32_t b_lds = smem_addr + (uint32_t)((NSTAGE * STAGE + QAREA) * 2 + wave * WAREA);
+    const int m_rs = (int)(p.m_sr * MBYTES);
     int b_off[4];
     if constexpr (FMASK) {
 #pragma unroll
@@ -338,9 +352,12 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             const int row = 4 * i + (lane >> 4);
             b_off[i] = row * m_rs + (((lane & 15) ^ (row & 15)) * 16);
         }
+    } else if constexpr (BMASK) {
+        b_off[0] = b_off[1] = b_off[2] = b_off[3] = (lane & 15) * m_rs + (lane >> 4) * 16;
     }
     int bP = (int)blockIdx.x, bs = 0, bt = 0, blast = -1;
-    const float* bptr = (const float*)p.mask;  // bias of the cursor's item, first row of this wave
+    using MElem = std::conditional_t<FMASK, float, uint8_t>;
+    const MElem* bptr = (const MElem*)p.mask;  // mask of the cursor's item, first row of this wave
     int brows = 0;                              // rows of this wave in that item
     auto bias_enter = [&] {
         while (bP < w.n_pairs) {
@@ -354,7 +371,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                              : ntl - 1;
             if (blast >= 0) {
                 brows = min(32, qrows - wave * 32);
-                bptr = (const float*)p.mask + (int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                bptr = (const MElem*)p.mask + (int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
                        (int64_t)(qt * BM + wave * 32) * p.m_sr;
                 return;
             }
@@ -367,12 +384,13 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     // key of the wave's last row, so every byte read is range checked.
     auto bias_next = [&] {
         if (bP >= w.n_pairs) return false;
-        const float* base = bptr + bt * BN;
-        const int kbytes = (p.S - bt * BN) * 4;
+        const MElem* base = bptr + bt * BN;
+        const int kbytes = (p.S - bt * BN) * MBYTES;
         const u32x4_t rs0 = pp_rsrc(base, (brows - 1) * m_rs + kbytes);
         const u32x4_t rs1 = pp_rsrc((const char*)base + (int64_t)16 * m_rs, (brows - 17) * m_rs + kbytes);
 #pragma unroll
-        for (int i = 0; i < NBDMA; ++i) pp_dma16(i < 4 ? rs0 : rs1, b_off[i & 3], b_lds + i * 1024);
+        for (int i = 0; i < NBDMA; ++i)
+            pp_dma16(i < NBDMA / 2 ? rs0 : rs1, b_off[i & 3], b_lds + i * 1024);
         if (++bt > blast) {
             next_item(bP, bs);
             bt = 0;
@@ -388,23 +406,46 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     int b_rd = 0;
     if constexpr (FMASK) {
         const int z = (2 * hh) ^ (lq & 15);
-        b_rd = ((NSTAGE * STAGE + QAREA) * 2 + wave * 8192 + lq * 256) ^ (z * 16);
+        b_rd = ((NSTAGE * STAGE + QAREA) * 2 + wave * WAREA + lq * 256) ^ (z * 16);
+    } else if constexpr (BMASK) {
+        // read i = (kb, c): keys 16(2kb + c) + 8hh + 0..7 of row lq
+        b_rd = (NSTAGE * STAGE + QAREA) * 2 + wave * WAREA + (lq >> 4) * 1024 + (lq & 15) * 16 + hh * 8;
     }
     auto bias_read = [&](int i) {
-        const int J = 8 * (i >> 2) + 4 * ((i >> 1) & 1) + (i & 1);
-        return *(const float4*)((const char*)smem + (b_rd ^ (J * 16)));
-    };
-    // Adds bias read i (4 keys) to the scores: logit = |scale| * s + bias.
-    auto bias_add = [&](f32x16_t* s, int i, float4 bv) {
-        const int kb = i >> 2, r0 = ((i >> 1) & 1) * 8 + (i & 1) * 4;
-        float l[4] = {fmaf(s[kb][r0 + 0], p.scale_abs, bv.x), fmaf(s[kb][r0 + 1], p.scale_abs, bv.y),
-                      fmaf(s[kb][r0 + 2], p.scale_abs, bv.z), fmaf(s[kb][r0 + 3], p.scale_abs, bv.w)};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pp_pin(l[r]);
-            s[kb][r0 + r] = l[r];
+        if constexpr (BMASK) {
+            return *(const uint2*)((const char*)smem + b_rd + i * 256);
+        } else {
+            const int J = 8 * (i >> 2) + 4 * ((i >> 1) & 1) + (i & 1);
+            return *(const float4*)((const char*)smem + (b_rd ^ (J * 16)));
         }
     };
+    // Adds bias read i (4 keys) to the scores: logit = |scale| * s + bias.
+    // Bool mask: read i (8 bytes) decides scores s[kb][8c + 0..7], kb = i/2, c = i%2.
+    auto mask_apply = [&](f32x16_t* s, int i, uint2 bv) {
+        const int kb = i >> 1, r0 = (i & 1) * 8;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t byte = ((r < 4 ? bv.x : bv.y) >> (8 * (r & 3))) & 0xffu;
+            float l = byte != 0 ? s[kb][r0 + r] : kNegInf;
+            pp_pin(l);
+            s[kb][r0 + r] = l;
+        }
+    };
+    auto bias_add = [&](f32x16_t* s, int i, auto bv) {
+        if constexpr (BMASK) {
+            mask_apply(s, i, bv);
+        } else {
+            const int kb = i >> 2, r0 = ((i >> 1) & 1) * 8 + (i & 1) * 4;
+            float l[4] = {fmaf(s[kb][r0 + 0], p.scale_abs, bv.x), fmaf(s[kb][r0 + 1], p.scale_abs, bv.y),
+                          fmaf(s[kb][r0 + 2], p.scale_abs, bv.z), fmaf(s[kb][r0 + 3], p.scale_abs, bv.w)};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pp_pin(l[r]);
+                s[kb][r0 + r] = l[r];
+            }
+        }
+    };
+    using MaskRead = std::conditional_t<BMASK, uint2, float4>;
     bool kv_after_bias = false;  // direct-to-LDS K/V loads were issued after the latest bias load
 
     // K operand: LDS row kb*32 + lq, chunk kk*2 + hh -> position
@@ -580,11 +621,11 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         }
         fence();
         // section 2: O^T += V^T P^T of block t, row sum between the products;
-        // float mask: the bias of block t + 1 added to its scores between the
-        // last NBDMA products (the wait for its load at the first of them)
+        // masks: the bias (or bool mask) of block t + 1 applied to its scores
+        // between the last NBRD products (the wait for its load at the first)
         {
             float p8[8];
-            float4 bq;
+            MaskRead bq;
             static_for<NOP>([&](auto jt) {
                 constexpr int j = decltype(jt)::value;
                 issue(std::integral_constant<int, NOP + j + LA>{});
@@ -603,8 +644,8 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                         pp_pin(l_run);
                     }
                 });
-                if constexpr (FMASK) {
-                    constexpr int J0 = NOP - NBDMA;
+                if constexpr (ANYMASK) {
+                    constexpr int J0 = NOP - NBRD;
                     if constexpr (j == J0) {
                         // read addresses computed here, not kept in registers across the loop
                         asm volatile("" : "+v"(b_rd));
@@ -615,21 +656,21 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                             __builtin_amdgcn_s_waitcnt(0x0F70);
                         bq = bias_read(0);
                     } else if constexpr (j > J0) {
-                        const float4 cv = bq;
+                        const MaskRead cv = bq;
                         bq = bias_read(j - J0);
                         bias_add(s_next, j - J0 - 1, cv);
                     }
                 }
                 fence();
             });
-            if constexpr (FMASK) bias_add(s_next, NBDMA - 1, bq);
+            if constexpr (ANYMASK) bias_add(s_next, NBRD - 1, bq);
         }
     };
 
     // Prologue: Q^T of the first item (float mask: the bias of the wave's
     // first block instead), K blocks 0-2 and V blocks 0-1.
     int P = (int)blockIdx.x, s = 0;
-    if constexpr (FMASK) {
+    if constexpr (ANYMASK) {
         bias_enter();
         bias_next();
     } else {
@@ -661,7 +702,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // for all of the wave's loads), or (float mask) straight from memory:
         // lane (lq, hh) holds elements 16kk + 8hh .. +7 of its row.  Negated
         // when the scale is negative.
-        if constexpr (FMASK) {
+        if constexpr (ANYMASK) {
             const int q_rows = max(0, min(32, qrows - wrow0));
             const auto qrs = make_rsrc((const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh +
                                            (int64_t)(q0 + wrow0) * p.q_sr,
@@ -681,20 +722,20 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
         sh_run = kNegInf;
         l_run = 0.f;
-        if (!FMASK && has_next) {
+        if (!ANYMASK && has_next) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): Q area reads done
             load_q(nP, ns);
         }
         scores(cur, sA);  // unconditional, so that no score register stays live across items
-        if (FMASK && last_tile >= 0) {
+        if (ANYMASK && last_tile >= 0) {
             // the bias of block 0 (loaded after this wave's last bias read), then
             // the next block's load into the area just read
             __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
-            float4 bv = bias_read(0);
+            MaskRead bv = bias_read(0);
 #pragma unroll
-            for (int i = 0; i < NBDMA; ++i) {
-                const float4 cv = bv;
-                if (i + 1 < NBDMA) bv = bias_read(i + 1);
+            for (int i = 0; i < NBRD; ++i) {
+                const MaskRead cv = bv;
+                if (i + 1 < NBRD) bv = bias_read(i + 1);
                 bias_add(sA, i, cv);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): bias reads done
@@ -715,7 +756,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // K/V load, so that section 2 of the next iteration waits for it with
         // the K/V load still in flight.
         auto step_end = [&](int t, bool bias_read_here) {
-            const bool bl = FMASK && bias_read_here;
+            const bool bl = ANYMASK && bias_read_here;
             if (t == 0) {
                 pp_barrier<0>();
                 const bool bi = bl && bias_next();

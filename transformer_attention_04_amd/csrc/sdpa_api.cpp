@@ -403,6 +403,10 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
         // vector loads also need whole vectors at the end of each row
         p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 &&
                      p.m_sh % mvec == 0 && p.m_sr % mvec == 0 && s.S % mvec == 0;
+        // bit 1 (bool masks): rows in whole 16-byte chunks, for the eight-wave kernel
+        if (mask_dtype == SDPA_BOOL && (uintptr_t)attn_mask->data % 16 == 0 && p.m_sb % 16 == 0 &&
+            p.m_sh % 16 == 0 && p.m_sr % 16 == 0 && s.S % 16 == 0)
+            p.mask_vec |= 2;
     }
     p.B = (int)s.B; p.Hq = (int)s.Hq; p.Hkv = (int)s.Hkv; p.group = (int)(s.Hq / s.Hkv);
     p.L = (int)s.L; p.S = (int)s.S;
