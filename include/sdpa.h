@@ -1,5 +1,7 @@
 /*
- * libsdpa: exact scaled dot-product attention, forward pass, for AMD MI355X (gfx950).
+ * libsdpa: exact scaled dot-product attention for AMD MI355X (gfx950): the
+ * forward pass (batched, packed variable-length, and against a paged
+ * key/value cache) and its gradients (batched and packed).
  *
  * The operation (exactref.ai, "scaled_dot_product_attention", sections
  * "Arguments" and "Full specification"): for query (..., L, E), key (..., S, E)
@@ -13,6 +15,10 @@
  * top-left corner), and grouped-query heads where query head h reads key/value
  * head h / (Hq / Hkv).  A row with no kept key has output 0 and lse -inf.  The
  * output has the inputs' dtype, rounded to nearest-even; lse is float32.
+ *
+ * Entry points: sdpa_fwd (+ _workspace_size), sdpa_fwd_varlen, sdpa_fwd_paged
+ * (+ _workspace_size), sdpa_bwd (+ _workspace_size), sdpa_bwd_varlen
+ * (+ _workspace_size), sdpa_last_error, sdpa_abi_version.
  *
  * Conventions for every entry point
  *  - All data pointers are DEVICE pointers (HIP global memory) owned by the

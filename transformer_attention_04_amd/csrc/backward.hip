@@ -30,6 +30,14 @@
 // pair and head dimension instead of the 5 of one shared pass; in exchange
 // every wavefront fits in 256 registers (two per SIMD).
 //
+// Optional masks, as in the forward: a float32 bias enters the logit as
+// scale * s + bias, a bool mask sets P = 0 on the keys it drops; the dQ kernel
+// reads its row's mask in 8-key runs, the dK/dV kernel down its key's column.
+// A row whose forward kept no key (lse -inf) is read with lse 0, so all its
+// weights are exp(-inf) = 0 and it contributes nothing.  Packed
+// variable-length batches (block-diagonal mask) take each segment's first
+// token and lengths from cu_seqlens and address rows by token.
+//
 // LDS tiles are row-major with 8 elements of padding per row (16-byte row
 // reads conflict-free).  Rows are stored at position swap23(r) within each
 // 32-row group (bits 2 and 3 of the row index swapped): then register r of

@@ -24,6 +24,10 @@
 //    weights of its keys from LDS and accumulates rows x 8 outputs.
 //  * at the end the 4 lane groups and the 4 wavefronts are combined through
 //    LDS into one normalised partial per query row.
+//  * value rows may be narrower or wider than query/key rows (Ev != E: the
+//    V chunks, partial outputs and merge use Ev); a paged cache variant reads
+//    K/V through a block table (pages of >= 16 keys, one buffer resource per
+//    16-key half, the split's page indices held in the lanes of a wavefront).
 #include "attn_common.h"
 #include "device_utils.h"
 

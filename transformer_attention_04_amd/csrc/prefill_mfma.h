@@ -1,7 +1,12 @@
 // Single-pass attention forward for bf16 / fp16 inputs on gfx950 matrix cores:
-// the kernel for float and boolean masks and for packed variable-length
-// batches, and the dispatch of all bf16 / fp16 forward calls (unmasked batched
-// calls go to the eight-wave kernel of prefill_pp.h).
+// the four-wave kernel, and the dispatch of all bf16 / fp16 forward calls.
+// Unmasked batched calls, float masks with aligned rows and bool masks whose
+// rows are whole 16-byte chunks go to the eight-wave kernel of prefill_pp.h;
+// this kernel takes the other masks, packed variable-length batches, value
+// rows of another width (Ev != E), head dims padded to a multiple of 32
+// (columns past E never read or written), and queries against a paged
+// key/value cache (chunked prefill: pages read through the block table in
+// 16-key groups, causal aligned bottom-right).
 //
 // Method: the blocked form of exact attention described on the khchao.com NN
 // Lab page ("FlashAttention Tiling & Online Softmax Algorithm"): queries in
