@@ -178,3 +178,33 @@ def test_backward_varlen(dtype, E, causal):
         ref = O.sdpa_backward(*seg, is_causal=causal, enable_gqa=True)
         gpu = [t[0, a:b].permute(1, 0, 2)[None] for t in (dq, dk, dv)]
         assert_bwd(gpu, ref, f"{dtype} E={E} causal={causal} segment {i} (length {b - a})")
+
+
+def _draw_bwd(rng):
+    hkv = rng.choice([1, 2])
+    return dict(dtype=rng.choice(["bf16", "fp16"]), B=rng.choice([1, 2]), Hkv=hkv, Hq=hkv * rng.choice([1, 2, 3]),
+                L=rng.choice([1, 33, 128, 150, 257]), S=rng.choice([1, 40, 128, 200, 256, 333]),
+                E=rng.choice([64, 96, 128]), causal=rng.random() < 0.5,
+                mask=rng.choice([None, None, "float", "bool"]), mshape=rng.choice(["full", "row", "head", "batch"]),
+                scale=rng.choice([None, None, 1.0, -0.3]))
+
+
+BWD_CASES = [_draw_bwd(__import__("random").Random(500 + i)) for i in range(32)]
+
+
+@pytest.mark.parametrize("ci", range(len(BWD_CASES)))
+def test_backward_random_configuration(ci):
+    """Seeded random shapes, heads, masks, causal and scales against the oracle's backward."""
+    c = BWD_CASES[ci]
+    q, k, v = inputs.randn_qkv((c["B"], c["Hq"], c["L"], c["E"]), (c["B"], c["Hkv"], c["S"], c["E"]),
+                               (c["B"], c["Hkv"], c["S"], c["E"]), c["dtype"], seed=700 + ci)
+    g = inputs.randn_qkv((c["B"], c["Hq"], c["L"], c["E"]), (1, 1, 1, c["E"]), (1, 1, 1, c["E"]), c["dtype"],
+                         seed=800 + ci)[0]
+    kw = dict(is_causal=c["causal"], scale=c["scale"], enable_gqa=c["Hq"] != c["Hkv"])
+    if c["mask"] is not None:
+        shape = {"full": (c["B"], c["Hq"], c["L"], c["S"]), "row": (1, 1, c["L"], c["S"]),
+                 "head": (1, c["Hq"], c["L"], c["S"]), "batch": (c["B"], 1, 1, c["S"])}[c["mshape"]]
+        fm, bm = _masks(shape, 900 + ci)
+        kw["attn_mask"] = fm if c["mask"] == "float" else bm
+    gpu, ref = run_bwd(q, k, v, g, c["dtype"], **kw)
+    assert_bwd(gpu, ref, f"case {ci}: {c}")
