@@ -63,9 +63,16 @@
 
 namespace sdpa {
 
+// Wavefronts per SIMD: 3 where the registers allow it without spills (causal,
+// unmasked, head dims <= 64: more wavefronts to overlap the softmax's vector
+// work with the matrix products), else 2.
+template <int D, int DV, bool CAUSAL, int MASK>
+constexpr int kPrefillWaves = (D <= 64 && DV <= 64 && CAUSAL && MASK == MASK_NONE) ? 3 : 2;
+
 template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false,
           bool PADE = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(kPrefillWaves<D, DV, CAUSAL, MASK>, kPrefillWaves<D, DV, CAUSAL, MASK>)))
 void prefill_mfma_kernel(AttnParams p) {
     constexpr int BM = kPrefillBlockM;
     constexpr int BN = 64;
