@@ -49,7 +49,8 @@ import numpy as np
 
 __all__ = [
     "resolve_scale", "bias_from_mask", "causal_bias", "logits", "weights",
-    "sdpa", "sdpa_backward", "block_diagonal_bias", "sdpa_varlen", "sdpa_paged", "entropy",
+    "sdpa", "sdpa_backward", "block_diagonal_bias", "sdpa_varlen", "sdpa_paged", "sdpa_paged_varlen",
+    "entropy",
 ]
 
 
@@ -335,6 +336,36 @@ def sdpa_paged(q, k_cache, v_cache, block_table, seq_lens, is_causal=False, scal
             bias = np.where(j <= n - L + i, 0.0, -np.inf)
         o, l_ = sdpa(q[b], kb, vb, attn_mask=bias, scale=scale, enable_gqa=enable_gqa)
         out[b], lse[b] = o, l_
+    return out, lse
+
+
+def sdpa_paged_varlen(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, is_causal=False, scale=None,
+                      enable_gqa=False):
+    """Packed new rows of several sequences against a paged cache, float64.
+
+    q (total_q, Hq, E) holds sequence b's new rows at tokens cu_seqlens_q[b] ..
+    cu_seqlens_q[b + 1] - 1 (each sequence its own number L_b of new rows);
+    the cache, block table and seq_lens are as for sdpa_paged, and each
+    sequence is exactly sdpa_paged of its own rows (bottom-right causal over
+    its n_b cached keys).  Returns out (total_q, Hq, Ev) and lse (Hq, total_q).
+    """
+    qq = _f64(q)
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).ravel()]
+    bt = np.asarray(block_table)
+    lens = np.asarray(seq_lens).ravel()
+    total, Hq, _ = qq.shape
+    Ev = np.asarray(v_cache).shape[-1]
+    out = np.zeros((total, Hq, Ev))
+    lse = np.full((Hq, total), -np.inf)
+    for b in range(len(cu) - 1):
+        a, e = cu[b], cu[b + 1]
+        if e == a:
+            continue
+        qb = np.transpose(qq[a:e], (1, 0, 2))[None]            # (1, Hq, L_b, E)
+        o, l_ = sdpa_paged(qb, k_cache, v_cache, bt[b:b + 1], lens[b:b + 1], is_causal=is_causal,
+                           scale=scale, enable_gqa=enable_gqa)
+        out[a:e] = np.transpose(o[0], (1, 0, 2))
+        lse[:, a:e] = l_[0]
     return out, lse
 
 

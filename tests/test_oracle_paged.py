@@ -117,3 +117,56 @@ def test_no_cached_keys_is_an_empty_row():
     assert np.isfinite(out[1]).all()
     o, l_ = O.sdpa(q[0], np.zeros((1, 0, 4)), np.zeros((1, 0, 4)))
     assert o.shape == (1, 1, 4) and (o == 0).all() and np.isneginf(l_).all()
+
+
+def test_packed_rows_per_sequence():
+    """sdpa_paged_varlen: packed new rows of different counts per sequence.
+    Fixed against dense attention over all packed rows and all sequences'
+    gathered keys at once, with one explicit bias: a key of another sequence
+    is -inf, and (causal) row r of sequence b keeps its own key j iff
+    j <= n_b - L_b + r; and, when every sequence has the same count, against
+    the batched sdpa_paged."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, E, Ev, ps = 4, 2, 8, 6, 16
+    lens = [5, 40, 17, 33]
+    counts = [3, 0, 17, 40]                   # new rows per sequence (more than cached for the last)
+    nblk = [(n + ps - 1) // ps for n in lens]
+    n_pages = sum(nblk) + 3
+    kc = rng.standard_normal((n_pages, Hkv, ps, E))
+    vc = rng.standard_normal((n_pages, Hkv, ps, Ev))
+    perm = rng.permutation(n_pages)
+    bt = np.zeros((len(lens), max(nblk)), dtype=np.int64)
+    pos = 0
+    for b, nb in enumerate(nblk):
+        bt[b, :nb] = perm[pos:pos + nb]
+        pos += nb
+    cu = np.concatenate([[0], np.cumsum(counts)])
+    q = rng.standard_normal((int(cu[-1]), Hq, E))
+    for causal in (False, True):
+        out, lse = O.sdpa_paged_varlen(q, cu, kc, vc, bt, lens, is_causal=causal, enable_gqa=True)
+        # dense reference: every sequence's keys gathered by hand, one packed bias
+        keys = [np.concatenate([kc[bt[b, j]] for j in range(nblk[b])], axis=1)[:, :lens[b]] for b in range(4)]
+        vals = [np.concatenate([vc[bt[b, j]] for j in range(nblk[b])], axis=1)[:, :lens[b]] for b in range(4)]
+        K, V = np.concatenate(keys, axis=1)[None], np.concatenate(vals, axis=1)[None]
+        koff = np.concatenate([[0], np.cumsum(lens)])
+        bias = np.full((int(cu[-1]), int(koff[-1])), -np.inf)
+        for b in range(4):
+            for r in range(counts[b]):
+                for j in range(lens[b]):
+                    if not causal or j <= lens[b] - counts[b] + r:
+                        bias[cu[b] + r, koff[b] + j] = 0.0
+        ro, rl = O.sdpa(np.transpose(q, (1, 0, 2))[None], K, V, attn_mask=bias, enable_gqa=True)
+        fin = np.isfinite(rl[0])
+        assert np.array_equal(np.isneginf(lse), np.isneginf(rl[0]))
+        assert np.abs(lse[fin] - rl[0][fin]).max() < 1e-12
+        assert np.abs(out - np.transpose(ro[0], (1, 0, 2))).max() < 1e-12
+    # equal counts: the batched function on the same rows
+    cnt = 7
+    cu2 = np.arange(5) * cnt
+    q2 = rng.standard_normal((4 * cnt, Hq, E))
+    o2, l2 = O.sdpa_paged_varlen(q2, cu2, kc, vc, bt, lens, is_causal=True, enable_gqa=True)
+    ob, lb = O.sdpa_paged(np.transpose(q2.reshape(4, cnt, Hq, E), (0, 2, 1, 3)), kc, vc, bt, lens,
+                          is_causal=True, enable_gqa=True)
+    assert np.abs(o2 - np.transpose(ob, (0, 2, 1, 3)).reshape(4 * cnt, Hq, Ev)).max() < 1e-13
+    fin = np.isfinite(lb)
+    assert np.abs(np.transpose(l2.reshape(Hq, 4, cnt), (1, 0, 2))[fin] - lb[fin]).max() < 1e-13
