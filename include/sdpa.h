@@ -17,7 +17,7 @@
  * output has the inputs' dtype, rounded to nearest-even; lse is float32.
  *
  * Entry points: sdpa_fwd (+ _workspace_size), sdpa_fwd_varlen, sdpa_fwd_paged
- * (+ _workspace_size), sdpa_bwd (+ _workspace_size), sdpa_bwd_varlen
+ * (+ _workspace_size), sdpa_fwd_paged_varlen, sdpa_bwd (+ _workspace_size), sdpa_bwd_varlen
  * (+ _workspace_size), sdpa_last_error, sdpa_abi_version.
  *
  * Conventions for every entry point
@@ -214,6 +214,39 @@ sdpa_status sdpa_fwd_paged_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* 
                                           const sdpa_tensor4* k_cache, const sdpa_tensor4* v_cache,
                                           int32_t max_seq_len, int enable_gqa, int num_splits,
                                           size_t* bytes);
+
+/*
+ * sdpa_fwd_paged_varlen -- packed new rows of several sequences, each its own
+ * number of rows, against the paged cache of sdpa_fwd_paged (chunked prefill
+ * of requests with different chunk lengths); no workspace.
+ *
+ *   dtype       SDPA_BF16 or SDPA_F16.
+ *   q           packed (total_q, Hq, E), token and head strides in elements
+ *               (multiples of 8, unit last stride, 16-byte aligned base);
+ *               sequence b's rows are tokens cu_seqlens_q[b] ..
+ *               cu_seqlens_q[b + 1] - 1 (DEVICE int32, n_seqs + 1 offsets;
+ *               max_seqlen_q must bound every count).
+ *   k_cache, v_cache, block_table, bt_stride, max_blocks, seq_lens,
+ *   max_seq_len  as for sdpa_fwd_paged (one table row and one length per
+ *               sequence); E == Ev in {64, 96, 128}.
+ *   is_causal   row r of sequence b is position n_b - L_b + r of it (L_b its
+ *               row count, n_b its cached length) and keeps key j iff
+ *               j <= n_b - L_b + r.
+ *   scale, enable_gqa   as for sdpa_fwd.
+ *   out         packed (total_q, Hq, Ev) with token and head strides; lse
+ *               (Hq, total_q) float32 with head stride lse_stride_head.
+ *               Tokens outside every sequence are not written.
+ * Table entries outside the pool: as for sdpa_fwd_paged (the rows that keep
+ * such a key come out NaN).
+ */
+sdpa_status sdpa_fwd_paged_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_tok,
+                                  int64_t q_stride_head, const int32_t* cu_seqlens_q, int32_t n_seqs,
+                                  int32_t max_seqlen_q, int64_t total_q, int32_t Hq,
+                                  const sdpa_tensor4* k_cache, const sdpa_tensor4* v_cache,
+                                  const int32_t* block_table, int64_t bt_stride, int32_t max_blocks,
+                                  const int32_t* seq_lens, int32_t max_seq_len, int is_causal,
+                                  const double* scale, int enable_gqa, void* out, int64_t o_stride_tok,
+                                  int64_t o_stride_head, float* lse, int64_t lse_stride_head, void* stream);
 
 /*
  * sdpa_bwd -- gradients of batched attention (exactref.ai

@@ -354,7 +354,7 @@ def sdpa_paged_varlen(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, 
     bt = np.asarray(block_table)
     lens = np.asarray(seq_lens).ravel()
     total, Hq, _ = qq.shape
-    Ev = np.asarray(v_cache).shape[-1]
+    Ev = v_cache.shape[-1]
     out = np.zeros((total, Hq, Ev))
     lse = np.full((Hq, total), -np.inf)
     for b in range(len(cu) - 1):

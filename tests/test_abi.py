@@ -272,3 +272,26 @@ def test_varlen_backward_argument_errors(lib):
     n = ctypes.c_size_t(0)
     assert lib.sdpa_bwd_varlen_workspace_size(8, 365, ctypes.byref(n)) == S.SDPA_OK
     assert n.value == 8 * 365 * 4 + 256
+
+
+def test_paged_varlen_argument_errors(lib):
+    def call(**kw):
+        a = dict(dtype=S.SDPA_BF16, q=FAKE, qt=1024, qh=128, cu=FAKE, n=3, mq=100, tq=250, Hq=8,
+                 kc=t4((64, 2, 64, 128)), vc=t4((64, 2, 64, 128)), bt=FAKE, bts=16, mb=16, sl=FAKE, ms=1000,
+                 causal=1, gqa=1, o=FAKE, ot=1024, oh=128, lse=FAKE, lh=250)
+        a.update(kw)
+        return lib.sdpa_fwd_paged_varlen(a["dtype"], a["q"], a["qt"], a["qh"], a["cu"], a["n"], a["mq"], a["tq"],
+                                         a["Hq"], ctypes.byref(a["kc"]), ctypes.byref(a["vc"]), a["bt"], a["bts"],
+                                         a["mb"], a["sl"], a["ms"], a["causal"], None, a["gqa"], a["o"], a["ot"],
+                                         a["oh"], a["lse"], a["lh"], None)
+    assert call(dtype=S.SDPA_F32) == S.SDPA_ERR_UNSUPPORTED
+    assert call(gqa=0) == S.SDPA_ERR_INVALID_ARGUMENT          # 8 query heads over 2 cache heads
+    assert call(Hq=5) == S.SDPA_ERR_INVALID_ARGUMENT           # not a multiple of the cache heads
+    assert call(kc=t4((64, 2, 48, 128)), vc=t4((64, 2, 48, 128))) == S.SDPA_ERR_UNSUPPORTED  # page size
+    assert call(vc=t4((64, 2, 64, 64))) == S.SDPA_ERR_UNSUPPORTED                           # E != Ev
+    assert call(vc=t4((63, 2, 64, 128))) == S.SDPA_ERR_INVALID_ARGUMENT                     # pools differ
+    assert call(bts=8) == S.SDPA_ERR_INVALID_ARGUMENT           # max_blocks > table stride
+    assert call(cu=None) == S.SDPA_ERR_INVALID_ARGUMENT
+    assert call(q=FAKE + 8) == S.SDPA_ERR_UNSUPPORTED           # misaligned base
+    assert call(qt=1020) == S.SDPA_ERR_UNSUPPORTED              # stride not a multiple of 8
+    assert call(n=0) == S.SDPA_OK                               # nothing to do

@@ -160,3 +160,25 @@ def test_paged_chunked_prefill_full_shape_sampled():
             ref = O.sdpa_paged(q[b:b + 1, hs], kc[:, g:g + 1], vc[:, g:g + 1], bt[b:b + 1], ln[b:b + 1],
                                is_causal=True, enable_gqa=True)
             check((out[b:b + 1, hs], lse[b:b + 1, hs]), ref, "bf16", f"sequence {b} cache head {g}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E", [64, 128])
+@pytest.mark.parametrize("ps", [16, 64])
+def test_paged_packed_rows(dtype, E, ps):
+    """Packed new rows, a different count per sequence (0, 1, a partial tile,
+    several tiles, more rows than cached keys), against a shuffled page pool,
+    grouped heads, causal and not: parity with oracle.sdpa_paged_varlen."""
+    lens = [5, 300, 64, 1000, 130]
+    counts = [1, 0, 64, 300, 200]
+    q4, kc, vc, bt, ln = make_cache(len(lens), 8, 2, 1, E, ps, lens, dtype, seed=E + ps + 3)
+    cu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int32)
+    q = inputs.randn_qkv((int(cu[-1]), 8, E), (1, 1, E), (1, 1, E), dtype, seed=E + ps + 4)[0]
+    for causal in (False, True):
+        out, lse = S.sdpa_fwd_paged_varlen(q.to(DEV), cu.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), ln.to(DEV),
+                                           is_causal=causal, enable_gqa=True)
+        torch.cuda.synchronize()
+        ro, rl = O.sdpa_paged_varlen(q, cu, kc, vc, bt, ln, is_causal=causal, enable_gqa=True)
+        # lse (Hq, total) -> (total, Hq), the leading dims of out
+        check((out.cpu().double().numpy(), lse.cpu().double().numpy().T), (ro, rl.T), dtype,
+              f"E={E} ps={ps} causal={causal}")

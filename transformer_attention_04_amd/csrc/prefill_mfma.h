@@ -106,7 +106,18 @@ void prefill_mfma_kernel(AttnParams p) {
 
     int Lb, Sb;
     int64_t qo, ko, vo, oo, lo, mo = 0;
-    if (VARLEN) {
+    if (VARLEN && PAGED) {
+        // packed new rows of sequence b (tokens cu_q[b] ..) against its paged keys
+        const int64_t a = min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
+        const int64_t e = min(max((int64_t)p.cu_q[b + 1], a), p.total_q);
+        Lb = (int)min(e - a, (int64_t)p.L);
+        Sb = min(max(p.seq_lens[b], 0), min(p.S, p.max_blocks << p.page_shift));
+        qo = a * p.q_sr + (int64_t)h * p.q_sh;
+        ko = (int64_t)kvh * p.k_sh;
+        vo = (int64_t)kvh * p.v_sh;
+        oo = a * p.o_sr + (int64_t)h * p.o_sh;
+        lo = (int64_t)h * p.lse_sh + a;
+    } else if (VARLEN) {
         const int64_t a = min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
         const int64_t e = min(max((int64_t)p.cu_q[b + 1], a), p.total_q);
         const int64_t c = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
@@ -522,8 +533,12 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
                             hipStream_t s) {
     if (p.dv != D) return launch_prefill_dv<Tr, D>(p, causal, mask, varlen, s);
     if (p.block_table) {
-        // queries against a paged cache (more new rows than the split-KV decode takes)
-        if (mask != MASK_NONE || varlen) return hipErrorInvalidValue;
+        // queries against a paged cache (more new rows than the split-KV decode
+        // takes, or packed rows of several sequences)
+        if (mask != MASK_NONE) return hipErrorInvalidValue;
+        if (varlen)
+            return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, true, true>(p, s)
+                          : launch_prefill_one<Tr, D, D, false, MASK_NONE, true, true>(p, s);
         return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, false, true>(p, s)
                       : launch_prefill_one<Tr, D, D, false, MASK_NONE, false, true>(p, s);
     }

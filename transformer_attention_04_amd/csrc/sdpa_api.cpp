@@ -596,6 +596,83 @@ sdpa_status sdpa_fwd_paged(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_t
     return ok();
 }
 
+sdpa_status sdpa_fwd_paged_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                  const int32_t* cu_seqlens_q, int32_t n_seqs, int32_t max_seqlen_q,
+                                  int64_t total_q, int32_t Hq, const sdpa_tensor4* k_cache,
+                                  const sdpa_tensor4* v_cache, const int32_t* block_table, int64_t bt_stride,
+                                  int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                  int is_causal, const double* scale, int enable_gqa, void* out,
+                                  int64_t o_stride_tok, int64_t o_stride_head, float* lse,
+                                  int64_t lse_stride_head, void* stream) {
+    if (dtype != SDPA_BF16 && dtype != SDPA_F16)
+        return fail(dtype == SDPA_F32 ? SDPA_ERR_UNSUPPORTED : SDPA_ERR_INVALID_ARGUMENT,
+                    "the paged-cache kernels take bf16 or fp16");
+    if (!k_cache || !v_cache) return fail(SDPA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must not be NULL");
+    for (int d = 0; d < 4; ++d)
+        if (k_cache->size[d] < 0 || v_cache->size[d] < 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    if (n_seqs < 0 || max_seqlen_q < 0 || total_q < 0 || Hq < 0 || max_seq_len < 0 || max_blocks < 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
+    const int64_t n_pages = k_cache->size[0], Hkv = k_cache->size[1], ps = k_cache->size[2];
+    const int64_t E = k_cache->size[3], Ev = v_cache->size[3];
+    if (v_cache->size[0] != n_pages || v_cache->size[1] != Hkv || v_cache->size[2] != ps)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must share pages, heads and page size");
+    if (Hq != Hkv) {
+        if (!enable_gqa)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query has %d heads and the cache %lld: pass enable_gqa", Hq,
+                        (long long)Hkv);
+        if (Hkv == 0 || Hq % Hkv != 0)
+            return fail(SDPA_ERR_INVALID_ARGUMENT, "query heads must be a multiple of cache heads");
+    }
+    int shift = 0;
+    while (shift < 30 && ((int64_t)1 << shift) < ps) ++shift;
+    if (ps < 16 || ((int64_t)1 << shift) != ps)
+        return fail(SDPA_ERR_UNSUPPORTED, "page_size must be a power of two >= 16 (got %lld)", (long long)ps);
+    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev");
+    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim must be 64, 96 or 128");
+    if (bt_stride < max_blocks) return fail(SDPA_ERR_INVALID_ARGUMENT, "need 0 <= max_blocks <= bt_stride");
+    if ((int64_t)max_blocks * ps > INT32_MAX || n_pages > INT32_MAX)
+        return fail(SDPA_ERR_UNSUPPORTED, "cache too large for 32-bit key indices");
+    if (n_seqs == 0 || total_q == 0 || Hq == 0 || max_seqlen_q == 0) return ok();
+    if (!cu_seqlens_q || !block_table || !seq_lens)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q, block_table and seq_lens must not be NULL");
+    if (!q || !out || !lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
+    const int eb = elem_bytes(dtype);
+    const int64_t vec = 16 / eb;
+    if (!aligned16(q) || !aligned16(out))
+        return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
+    const int64_t strides[4] = {q_stride_tok, q_stride_head, o_stride_tok, o_stride_head};
+    for (int i = 0; i < 4; ++i)
+        if (strides[i] % vec != 0)
+            return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
+    sdpa_status st;
+    if (n_pages > 0) {
+        if ((st = check_vector_layout(*k_cache, eb, "k_cache")) != SDPA_OK) return st;
+        if ((st = check_vector_layout(*v_cache, eb, "v_cache")) != SDPA_OK) return st;
+    }
+    double sc;
+    if ((st = resolve_scale(scale, E, &sc)) != SDPA_OK) return st;
+    sdpa::AttnParams a{};
+    a.q = q; a.k = k_cache->data; a.v = v_cache->data; a.o = out; a.lse = lse;
+    a.cu_q = cu_seqlens_q;
+    a.q_sr = q_stride_tok; a.q_sh = q_stride_head;
+    a.k_sb = k_cache->stride[0]; a.k_sh = k_cache->stride[1]; a.k_sr = k_cache->stride[2];
+    a.v_sb = v_cache->stride[0]; a.v_sh = v_cache->stride[1]; a.v_sr = v_cache->stride[2];
+    a.o_sr = o_stride_tok; a.o_sh = o_stride_head;
+    a.lse_sh = lse_stride_head;
+    a.total_q = total_q;
+    a.B = n_seqs; a.Hq = Hq; a.Hkv = (int)Hkv; a.group = (int)(Hq / Hkv);
+    a.L = max_seqlen_q; a.S = max_seq_len;
+    a.dv = (int)Ev; a.e = (int)E;
+    a.n_qtiles = (max_seqlen_q + sdpa::kPrefillBlockM - 1) / sdpa::kPrefillBlockM;
+    fill_scale(a, sc);
+    a.block_table = block_table; a.seq_lens = seq_lens; a.bt_stride = bt_stride;
+    a.page_shift = shift; a.n_pages = (int)n_pages; a.max_blocks = max_blocks;
+    hipError_t e = launch_single_pass(dtype, a, (int)E, is_causal != 0, sdpa::MASK_NONE, true, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "paged prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4* k,
                                     const sdpa_tensor4* v, int enable_gqa, size_t* bytes) {
     if (!bytes) return fail(SDPA_ERR_INVALID_ARGUMENT, "bytes must not be NULL");

@@ -21,7 +21,7 @@ SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 _DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
 
 EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_fwd_paged",
-            "sdpa_fwd_paged_workspace_size", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_bwd_varlen",
+            "sdpa_fwd_paged_workspace_size", "sdpa_fwd_paged_varlen", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_bwd_varlen",
             "sdpa_bwd_varlen_workspace_size", "sdpa_last_error",
             "sdpa_abi_version")
 
@@ -77,6 +77,10 @@ def load_library():
     lib.sdpa_fwd_paged_workspace_size.argtypes = [ctypes.c_int, P, P, P, i32, ctypes.c_int, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_fwd_paged_workspace_size.restype = ctypes.c_int
+    lib.sdpa_fwd_paged_varlen.argtypes = [ctypes.c_int, vp, i64, i64, vp, i32, i32, i64, i32, P, P, vp, i64, i32,
+                                          vp, i32, ctypes.c_int, ctypes.POINTER(dbl), ctypes.c_int, vp, i64, i64,
+                                          vp, i64, vp]
+    lib.sdpa_fwd_paged_varlen.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, P, P, P, ctypes.c_int,
                              ctypes.POINTER(dbl), ctypes.c_int, P, P, P, vp, ctypes.c_size_t, vp]
     lib.sdpa_bwd.restype = ctypes.c_int
@@ -272,6 +276,54 @@ def sdpa_fwd_paged(query, k_cache, v_cache, block_table, seq_lens, max_seq_len=N
                                   int(bool(enable_gqa)), _desc(out), _desc(lse), workspace.data_ptr(),
                                   n.value, int(num_splits), _stream(dev)))
     return out, lse.reshape(B, Hq, L)
+
+
+def sdpa_fwd_paged_varlen(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, max_seqlen_q=None,
+                          max_seq_len=None, is_causal=False, scale=None, enable_gqa=False):
+    """Packed new rows of several sequences (each its own count) against a
+    paged key/value cache on the GPU.
+
+    q (total_q, Hq, E) or (1, total_q, Hq, E); cu_seqlens_q int32 (n_seqs + 1)
+    offsets; k_cache / v_cache (n_pages, Hkv, page_size, E); block_table
+    (n_seqs, max_blocks) and seq_lens (n_seqs,) int32, all on the device.
+    is_causal aligns each sequence's rows bottom-right.  Returns out shaped
+    like q (with Ev) and lse (Hq, total_q) (or (1, Hq, total_q)).
+    """
+    lib = load_library()
+    _require_gpu(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens)
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("the paged-cache kernels take float16 or bfloat16 query and cache")
+    for t in (cu_seqlens_q, block_table, seq_lens):
+        if t.dtype != torch.int32:
+            raise ValueError("cu_seqlens_q, block_table and seq_lens must be int32")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be 2-D (n_seqs, max_blocks)")
+    if block_table.stride(1) != 1:
+        block_table = block_table.contiguous()
+    cu_seqlens_q, seq_lens = cu_seqlens_q.contiguous(), seq_lens.contiguous()
+    n_seqs = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None:
+        cq = cu_seqlens_q.cpu().long()
+        max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if n_seqs > 0 else 0
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    batched = q.dim() == 4
+    q3 = q[0] if batched else q
+    total_q, Hq, E = q3.shape
+    Ev = v_cache.shape[3]
+    dev = q.device
+    out3 = torch.empty((total_q, Hq, Ev), dtype=q.dtype, device=dev)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.sdpa_fwd_paged_varlen(
+            _DTYPE[q.dtype], q3.data_ptr(), q3.stride(0), q3.stride(1), cu_seqlens_q.data_ptr(), n_seqs,
+            int(max_seqlen_q), total_q, Hq, _desc(k_cache), _desc(v_cache), block_table.data_ptr(),
+            block_table.stride(0), block_table.shape[1], seq_lens.data_ptr(), int(max_seq_len),
+            int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), out3.data_ptr(), out3.stride(0),
+            out3.stride(1), lse.data_ptr(), lse.stride(0), _stream(dev)))
+    if batched:
+        return out3.unsqueeze(0), lse.unsqueeze(0)
+    return out3, lse
 
 
 def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
