@@ -379,7 +379,7 @@ def main(argv=None):
             "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
             "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "call_us": round(r["kernel_ms"] * 1e3, 1), "flop_per_call": r["flops"],
-            "kernels": "bwd_dot_kernel + bwd_dq_kernel + bwd_dkdv_kernel"}
+            "kernels": "bwd_dq_kernel + bwd_dkdv_kernel"}
         print(f"# bf16_causal_e128 backward: {r['kernel_ms'] * 1e3:.1f} us/call, "
               f"{r['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 

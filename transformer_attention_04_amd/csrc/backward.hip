@@ -9,9 +9,11 @@
 // definition's sum up to the rounding of O), as the blocked algorithm on the
 // khchao.com NN Lab page keeps only O(N) state per row.
 //
-// Three kernels:
-//   bwd_dot_kernel    D_i = dO_i . O_i in fp32 (HBM-bound, one pass).
-//   bwd_dq_kernel     one workgroup per 128 query rows (4 wavefronts x 32):
+// Two kernels:
+//   bwd_dq_kernel     one workgroup per 128 query rows (4 wavefronts x 32);
+//                     first D_i = dO_i . O_i in fp32 from the dO rows it holds
+//                     and the O rows in the same layout (written to the
+//                     workspace for the second kernel, which runs after it);
 //                     for each 64-key block, S^T = K Q^T and dP^T = V dO^T on
 //                     the matrix cores (the transposed score layout of the
 //                     forward kernels, one query per lane), P^T and dS^T in
@@ -80,49 +82,6 @@ __device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int c, int col0, 
 }
 
 // ------------------------------------------------------------- D = dO . O
-
-template <int D, bool VARLEN = false>
-__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
-    // 16 lanes per row, 16 rows per workgroup; row index over (b, h, i), or
-    // (h, token) for packed batches
-    const int tid = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * 16 + tid / 16;
-    const int c = tid & 15;
-    const int64_t nrows = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.L;
-    float acc = 0.f;
-    if (row < nrows && c < D / 8) {
-        uint4 o, g;
-        if constexpr (VARLEN) {
-            const int64_t t = row % p.total_q;
-            const int h = (int)(row / p.total_q);
-            o = *(const uint4*)((const uint16_t*)p.o + t * p.o_sr + h * p.o_sh + c * 8);
-            g = *(const uint4*)((const uint16_t*)p.dout + t * p.do_sr + h * p.do_sh + c * 8);
-        } else {
-            const int i = (int)(row % p.L);
-            const int64_t bh = row / p.L;
-            const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-            o = *(const uint4*)((const uint16_t*)p.o + b * p.o_sb + h * p.o_sh + i * p.o_sr + c * 8);
-            g = *(const uint4*)((const uint16_t*)p.dout + b * p.do_sb + h * p.do_sh + i * p.do_sr + c * 8);
-        }
-        const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float o0, o1, g0, g1;
-            if (p.elem == ELEM_BF16) {
-                o0 = BF16::to_f32(ow[j] & 0xffff); o1 = BF16::to_f32(ow[j] >> 16);
-                g0 = BF16::to_f32(gw[j] & 0xffff); g1 = BF16::to_f32(gw[j] >> 16);
-            } else {
-                o0 = F16::to_f32(ow[j] & 0xffff); o1 = F16::to_f32(ow[j] >> 16);
-                g0 = F16::to_f32(gw[j] & 0xffff); g1 = F16::to_f32(gw[j] >> 16);
-            }
-            acc = fmaf(o0, g0, acc);
-            acc = fmaf(o1, g1, acc);
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) acc += xor_lane(acc, m);
-    if (row < nrows && c == 0) p.dsum[row] = acc;
-}
 
 // ------------------------------------------------------------------- dQ
 
@@ -223,13 +182,34 @@ void bwd_dq_kernel(BwdParams p) {
         qreg[kk] = buf_load16(qrs, lrow * q_rs + (kk * 16 + hh * 8) * 2);
         dreg[kk] = buf_load16(gdrs, lrow * do_rs + (kk * 16 + hh * 8) * 2);
     }
+    // D_i = dO_i . O_i for this lane's row: O in the layout of dO, fp32 products
+    // over the lane's half of the row, then the other half from lane ^ 32
+    const int o_rs = (int)(p.o_sr * 2);
+    const int64_t o_b = VARLEN ? qa * p.o_sr : b * p.o_sb;
+    const auto ors_in = make_rsrc((const uint16_t*)p.o + o_b + h * p.o_sh + (int64_t)q0 * p.o_sr,
+                                  (qrows - 1) * o_rs + D * 2);
+    float dpart = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const uint4 o = buf_load16(ors_in, lrow * o_rs + (kk * 16 + hh * 8) * 2);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+        const uint32_t gw[4] = {dreg[kk].x, dreg[kk].y, dreg[kk].z, dreg[kk].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dpart = fmaf(Tr::to_f32(ow[j] & 0xffffu), Tr::to_f32(gw[j] & 0xffffu), dpart);
+            dpart = fmaf(Tr::to_f32(ow[j] >> 16), Tr::to_f32(gw[j] >> 16), dpart);
+        }
+    }
     const int64_t rowid = VARLEN ? (int64_t)h * p.total_q + qa : ((int64_t)b * p.Hq + h) * p.L;
     const int64_t lse_b = VARLEN ? h * p.lse_sh + qa : b * p.lse_sb + h * p.lse_sh;
     const bool row_ok = my_row < Lb;
     float lse2 = row_ok ? p.lse[lse_b + my_row] * kLog2e : 0.f;
     // a masked row with no kept key (lse -inf) has P = 0: exp2(-inf - 0)
     if (MASK != MASK_NONE && lse2 == kNegInf) lse2 = 0.f;
-    const float drow = row_ok ? p.dsum[rowid + my_row] : 0.f;
+    const float dfull = pair32_sum(dpart);  // every lane takes part in the exchange
+    const float drow = row_ok ? dfull : 0.f;
+    // the dK/dV kernel, launched after this one, reads D from the workspace
+    if (row_ok && hh == 0) p.dsum[rowid + my_row] = drow;
     const float c2 = p.scale * kLog2e;  // signed
     // All of the above has landed before the loop: otherwise the first uses in
     // the loop would wait (in every iteration) for the loads issued after them,
@@ -627,14 +607,6 @@ void launch_bwd_m(const BwdParams& p, bool causal, hipStream_t s) {
 
 template <typename Tr, int D>
 hipError_t launch_bwd_d(const BwdParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
-    const int64_t nrows = varlen ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.L;
-    if (nrows > 0) {
-        const dim3 grid((unsigned)((nrows + 15) / 16));
-        if (varlen)
-            hipLaunchKernelGGL((bwd_dot_kernel<D, true>), grid, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((bwd_dot_kernel<D>), grid, dim3(256), 0, s, p);
-    }
     if (varlen) {
         if (mask != MASK_NONE) return hipErrorInvalidValue;
         launch_bwd_m<Tr, D, MASK_NONE, true>(p, causal, s);
