@@ -37,8 +37,9 @@
  *    No C++ exception crosses this interface.
  *  - Head dims supported by the kernels: E and Ev each in {64, 96, 128}.
  *    E != Ev (value rows of another width than query/key rows, which the
- *    operation allows) is handled for bf16/fp16 inputs without attn_mask by
- *    sdpa_fwd; every other entry point and combination needs E == Ev.
+ *    operation allows) is handled for bf16/fp16 inputs by sdpa_fwd (with or
+ *    without attn_mask) and sdpa_fwd_varlen; the paged entry points and the
+ *    backward need E == Ev.
  *    sdpa_fwd also takes E == Ev any multiple of 8 from 8 to 128 for
  *    bf16/fp16 inputs without attn_mask (single-pass kernel only).
  *    E = 0 (an empty score sum) is valid for the operation but not handled by

@@ -128,10 +128,12 @@ def test_unsupported_head_dims(lib):
     st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                                      None, 0, 0, 0, ctypes.byref(n))
     assert st == S.SDPA_OK and n.value == 0
-    # E != Ev runs on the 16-bit kernels without a mask only
+    # E != Ev runs on the 16-bit kernels only (masked or not), with head dims 64/96/128
     st, msg = call(lib, *qkv(E=64, Ev=128), dtype=S.SDPA_F32)
     assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
-    st, msg = call(lib, *qkv(E=128, Ev=64), mask=t4((1, 1, 16, 32)))
+    st, msg = call(lib, *qkv(E=128, Ev=64), dtype=S.SDPA_F32, mask=t4((1, 1, 16, 32)))
+    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
+    st, msg = call(lib, *qkv(E=128, Ev=80), mask=t4((1, 1, 16, 32)))
     assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
     st, _ = call(lib, *qkv(E=0))
     assert st == S.SDPA_ERR_UNSUPPORTED
@@ -204,6 +206,8 @@ def test_varlen_argument_errors(lib):
     assert varlen(Hkv=3, gqa=1) == S.SDPA_ERR_INVALID_ARGUMENT
     assert varlen(cq=None) == S.SDPA_ERR_INVALID_ARGUMENT
     assert varlen(E=80, Ev=80) == S.SDPA_ERR_UNSUPPORTED
+    assert varlen(E=64, Ev=80) == S.SDPA_ERR_UNSUPPORTED
+    assert varlen(dtype=S.SDPA_F32, E=64, Ev=128) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(q=FAKE + 4) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(kt=510) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(n=-1) == S.SDPA_ERR_INVALID_ARGUMENT

@@ -406,6 +406,42 @@ def test_value_dim_differs(dtype, E, Ev):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E,Ev", [(64, 128), (128, 64), (96, 64)])
+def test_value_dim_differs_masked_and_packed(dtype, E, Ev):
+    """Ev != E with a float bias (-inf entries, rows with no kept key) and a
+    bool mask in broadcast shapes, causal and not, with GQA; and packed
+    segments (ragged lengths, one empty) with Ev != E, causal and not."""
+    q, k, v = inputs.randn_qkv((2, 4, 150, E), (2, 2, 333, E), (2, 2, 333, Ev), dtype, seed=E + Ev + 11)
+    g = torch.Generator().manual_seed(E * 7 + Ev)
+    fm = torch.randn(2, 1, 150, 333, generator=g)
+    fm[torch.rand(2, 1, 150, 333, generator=g) < 0.3] = float("-inf")
+    fm[:, :, 5] = float("-inf")                       # a row with no kept key
+    bm = torch.rand(1, 4, 150, 333, generator=g) < 0.6
+    for m, what in ((fm, "float"), (bm, "bool")):
+        for causal in (False, True):
+            r = run_both(q, k, v, dtype, attn_mask=m, is_causal=causal, enable_gqa=True)
+            assert r[0].shape == (2, 4, 150, Ev)
+            assert_parity(*r, dtype, f"E={E} Ev={Ev} {what} mask causal={causal}")
+    lengths = [70, 0, 129, 300, 1]
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    tot = int(cu[-1])
+    qv, kv, vv = inputs.randn_qkv((tot, 4, E), (tot, 2, E), (tot, 2, Ev), dtype, seed=E + 2 * Ev)
+    for causal in (False, True):
+        out, lse = S.sdpa_fwd_varlen(qv.to(DEV), kv.to(DEV), vv.to(DEV), cu.to(DEV), is_causal=causal,
+                                     enable_gqa=True)
+        torch.cuda.synchronize()
+        assert out.shape == (tot, 4, Ev)
+        for i, n in enumerate(lengths):
+            a = int(cu[i])
+            if n == 0:
+                continue
+            qs, ks, vs = (t[a:a + n].permute(1, 0, 2).contiguous() for t in (qv, kv, vv))
+            ro, rl = O.sdpa(qs, ks, vs, is_causal=causal, enable_gqa=True)
+            assert_parity(out[a:a + n].permute(1, 0, 2), lse[:, a:a + n], ro, rl, dtype,
+                          f"packed E={E} Ev={Ev} segment {i} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("E", [8, 16, 32, 40, 80, 120])
 def test_other_head_dims(dtype, E):
     """Head dims other than 64/96/128 (multiples of 8 up to 128), zero-padded

@@ -510,19 +510,33 @@ hipError_t launch_prefill_one(const AttnParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Value head dim DV != D: the four-wave kernel, unmasked batched calls only.
+// Value head dim DV != D: the four-wave kernel (its mask and packed-batch code
+// reads scores only, so every mask kind and packed batches take any DV).
+template <typename Tr, int D, int DV, bool CAUSAL>
+hipError_t launch_prefill_dv_one(const AttnParams& p, int mask, bool varlen, hipStream_t s) {
+    if (varlen)
+        return mask == MASK_NONE ? launch_prefill_one<Tr, D, DV, CAUSAL, MASK_NONE, true>(p, s)
+                                 : hipErrorInvalidValue;
+    switch (mask) {
+        case MASK_NONE: return launch_prefill_one<Tr, D, DV, CAUSAL, MASK_NONE, false>(p, s);
+        case MASK_FLOAT: return launch_prefill_one<Tr, D, DV, CAUSAL, MASK_FLOAT, false>(p, s);
+        case MASK_BOOL: return launch_prefill_one<Tr, D, DV, CAUSAL, MASK_BOOL, false>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <typename Tr, int D>
 hipError_t launch_prefill_dv(const AttnParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
-    if (mask != MASK_NONE || varlen) return hipErrorInvalidValue;
+    if (p.block_table) return hipErrorInvalidValue;
     switch (p.dv) {
-        case 64: if constexpr (D != 64) return causal ? launch_prefill_one<Tr, D, 64, true, MASK_NONE, false>(p, s)
-                                                      : launch_prefill_one<Tr, D, 64, false, MASK_NONE, false>(p, s);
+        case 64: if constexpr (D != 64) return causal ? launch_prefill_dv_one<Tr, D, 64, true>(p, mask, varlen, s)
+                                                      : launch_prefill_dv_one<Tr, D, 64, false>(p, mask, varlen, s);
                  break;
-        case 96: if constexpr (D != 96) return causal ? launch_prefill_one<Tr, D, 96, true, MASK_NONE, false>(p, s)
-                                                      : launch_prefill_one<Tr, D, 96, false, MASK_NONE, false>(p, s);
+        case 96: if constexpr (D != 96) return causal ? launch_prefill_dv_one<Tr, D, 96, true>(p, mask, varlen, s)
+                                                      : launch_prefill_dv_one<Tr, D, 96, false>(p, mask, varlen, s);
                  break;
-        case 128: if constexpr (D != 128) return causal ? launch_prefill_one<Tr, D, 128, true, MASK_NONE, false>(p, s)
-                                                        : launch_prefill_one<Tr, D, 128, false, MASK_NONE, false>(p, s);
+        case 128: if constexpr (D != 128) return causal ? launch_prefill_dv_one<Tr, D, 128, true>(p, mask, varlen, s)
+                                                        : launch_prefill_dv_one<Tr, D, 128, false>(p, mask, varlen, s);
                   break;
     }
     return hipErrorInvalidValue;

@@ -326,9 +326,8 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
                     "head dims E=%lld, Ev=%lld: each must be one of 64, 96, 128, or E == Ev a multiple "
                     "of 8 up to 128 for bf16/fp16 without a mask",
                     (long long)s.E, (long long)s.Ev);
-    if (s.E != s.Ev && (dtype == SDPA_F32 || attn_mask))
-        return fail(SDPA_ERR_UNSUPPORTED,
-                    "E != Ev (%lld and %lld) needs bf16/fp16 inputs and no attn_mask", (long long)s.E,
+    if (s.E != s.Ev && dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "E != Ev (%lld and %lld) needs bf16/fp16 inputs", (long long)s.E,
                     (long long)s.Ev);
     const int eb = elem_bytes(dtype);
     if ((st = check_vector_layout(*q, eb, "q")) != SDPA_OK) return st;
@@ -449,8 +448,10 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     if (n_seqs == 0 || max_seqlen_q == 0 || Hq == 0 || total_q == 0) return ok();
     if (!cu_seqlens_q || !cu_seqlens_k)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must not be NULL");
-    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %d and %d)", E, Ev);
-    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d is not one of 64, 96, 128", E);
+    if (!supported_head_dim(E) || !supported_head_dim(Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%d, Ev=%d: each must be one of 64, 96, 128", E, Ev);
+    if (E != Ev && dtype == SDPA_F32)
+        return fail(SDPA_ERR_UNSUPPORTED, "E != Ev (%d and %d) needs bf16/fp16 inputs", E, Ev);
     if (!q || !out || !lse || (total_k > 0 && (!k || !v)))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
     const int64_t vec = 16 / elem_bytes(dtype);
