@@ -96,3 +96,66 @@ def test_random_configuration(ci):
     eo = np.abs(go[fo] - ro[fo]).max(initial=0.0)
     el = np.abs(gl[fl] - rl[fl]).max(initial=0.0)
     assert eo <= tol_o and el <= tol_l, f"{c}: out err {eo:.3e}, lse err {el:.3e}"
+
+
+def draw_value_dim(rng):
+    """A masked or packed configuration with value rows of another width (Ev != E)."""
+    dtype = rng.choice(["bf16", "fp16"])
+    E, Ev = rng.sample([64, 96, 128], 2)
+    hkv = rng.choice([1, 2])
+    group = rng.choice([1, 2, 4])
+    packed = rng.random() < 0.4
+    lengths = [rng.choice([0, 1, 31, 64, 65, 130, 257]) for _ in range(rng.choice([1, 2, 4]))]
+    return dict(dtype=dtype, E=E, Ev=Ev, Hq=hkv * group, Hkv=hkv, B=rng.choice([1, 2]),
+                L=rng.choice([1, 7, 100, 129, 200]), S=rng.choice([1, 63, 64, 200, 333, 512]),
+                causal=rng.random() < 0.5, scale=rng.choice([None, 1.0, -0.25]), packed=packed,
+                lengths=lengths, mask=None if packed else (rng.choice(["float", "bool"]),
+                                                         rng.choice(["full", "row", "head", "batch"])))
+
+
+VCASES = [draw_value_dim(random.Random(5000 + i)) for i in range(24)]
+
+
+@pytest.mark.parametrize("ci", range(len(VCASES)))
+def test_random_value_dim_configuration(ci):
+    c = VCASES[ci]
+    gqa = c["Hq"] != c["Hkv"]
+    tol_o, tol_l = TOL[c["dtype"]]
+    if c["packed"]:
+        lengths = c["lengths"]
+        cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+        tot = int(cu[-1])
+        q, k, v = inputs.randn_qkv((tot, c["Hq"], c["E"]), (tot, c["Hkv"], c["E"]), (tot, c["Hkv"], c["Ev"]),
+                                   c["dtype"], seed=ci + 300)
+        if tot == 0:
+            return
+        out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), is_causal=c["causal"],
+                                     scale=c["scale"], enable_gqa=gqa)
+        torch.cuda.synchronize()
+        pieces = []
+        for i, n in enumerate(lengths):
+            a = int(cu[i])
+            if n == 0:
+                continue
+            qs, ks, vs = (t[a:a + n].permute(1, 0, 2).contiguous() for t in (q, k, v))
+            ro, rl = O.sdpa(qs, ks, vs, is_causal=c["causal"], scale=c["scale"], enable_gqa=gqa)
+            pieces.append((out[a:a + n].permute(1, 0, 2), lse[:, a:a + n], ro, rl))
+    else:
+        q, k, v = inputs.randn_qkv((c["B"], c["Hq"], c["L"], c["E"]), (c["B"], c["Hkv"], c["S"], c["E"]),
+                                   (c["B"], c["Hkv"], c["S"], c["Ev"]), c["dtype"], seed=ci + 300)
+        m = make_mask(*c["mask"], c["B"], c["Hq"], c["L"], c["S"], seed=ci + 307)
+        out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), attn_mask=m.to(DEV), is_causal=c["causal"],
+                              scale=c["scale"], enable_gqa=gqa)
+        torch.cuda.synchronize()
+        mm = m.numpy() if m.dtype == torch.bool else m.double().numpy()
+        ro, rl = O.sdpa(q, k, v, attn_mask=mm, is_causal=c["causal"], scale=c["scale"], enable_gqa=gqa)
+        pieces = [(out, lse, ro, rl)]
+    for o, l, ro, rl in pieces:
+        go, gl = o.detach().cpu().double().numpy(), l.detach().cpu().double().numpy()
+        assert go.shape == ro.shape and gl.shape == rl.shape, (go.shape, ro.shape)
+        empty = np.isneginf(rl)
+        assert np.isneginf(gl[empty]).all() and (go[empty] == 0).all(), f"{c}: empty rows"
+        fo, fl = np.isfinite(ro), np.isfinite(rl)
+        eo = np.abs(go[fo] - ro[fo]).max(initial=0.0)
+        el = np.abs(gl[fl] - rl[fl]).max(initial=0.0)
+        assert eo <= tol_o and el <= tol_l, f"{c}: out err {eo:.3e}, lse err {el:.3e}"
