@@ -7,7 +7,8 @@ float or bool mask in a random broadcast shape, a scale (default, unit,
 negative) and a split count for decode shapes, then compares output and lse
 with the float64 oracle at the fixed bars and checks that nothing outside
 `out` was written.  The configurations are drawn from a fixed seed, so every
-run tests the same cases.
+run tests the same cases.  A second set draws value rows of another width
+(Ev != E) with a float or bool mask, or as packed ragged segments.
 """
 import random
 
