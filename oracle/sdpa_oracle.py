@@ -109,8 +109,9 @@ def _expand_kv(query, key, value, enable_gqa):
     return key, value
 
 
-def logits(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
-    """The (..., L, S) float64 logits scale * q.k + bias, with every mask folded into the bias."""
+def _logit_parts(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
+    """The (..., L, S) float64 scaled scores scale * q.k and the bias (every mask folded),
+    kept apart so that a bias common to a row's keys cancels exactly in the softmax."""
     q = _f64(query)
     k = _f64(key)
     k, _ = _expand_kv(q, k, k, enable_gqa)
@@ -124,10 +125,18 @@ def logits(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=F
         bias = bias + causal_bias(L, S)
     with np.errstate(invalid="ignore", over="ignore"):
         if E == 0:
-            s = np.zeros(np.broadcast_shapes(q.shape[:-2], k.shape[:-2]) + (L, S))
-            return s + bias
-        s = np.matmul(q, np.swapaxes(k, -1, -2))
-        return resolve_scale(E, scale) * s + bias
+            cs = np.zeros(np.broadcast_shapes(q.shape[:-2], k.shape[:-2]) + (L, S))
+        else:
+            cs = resolve_scale(E, scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    shape = np.broadcast_shapes(cs.shape, bias.shape)
+    return np.broadcast_to(cs, shape), np.broadcast_to(bias, shape)
+
+
+def logits(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
+    """The (..., L, S) float64 logits scale * q.k + bias, with every mask folded into the bias."""
+    cs, bias = _logit_parts(query, key, attn_mask, is_causal, scale, enable_gqa)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return cs + bias
 
 
 def _row_classes(ell):
@@ -140,12 +149,30 @@ def _row_classes(ell):
     return nan_row, inf_row, empty_row, normal
 
 
-def _softmax_parts(ell):
-    """Row max m, unnormalised weights w = exp(l - m), row sum, and row classes."""
+def _softmax_parts(cs, bias):
+    """Row max m, unnormalised weights w = exp(l - m), row sum, and row classes.
+
+    The shifted logit l_j - m is formed as (b_j - b_k) + (cs_j - cs_k) with k the
+    key of the largest logit: a bias shared by the row's keys (a padding mask's
+    lowest float added to every key) then cancels exactly, as the exactref.ai
+    "Padding masks" section says it does in exact arithmetic, instead of
+    swallowing the scores when the two are added in float64."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        ell = cs + bias
     nan_row, inf_row, empty_row, normal = _row_classes(ell)
     with np.errstate(invalid="ignore", over="ignore"):
-        m = np.where(normal, np.max(np.where(np.isnan(ell), -np.inf, ell), axis=-1, initial=-np.inf), 0.0)
-        w = np.exp(ell - m[..., None])
+        if ell.shape[-1] == 0:   # no keys: every row is empty
+            m = np.zeros(ell.shape[:-1])
+            w = np.zeros(ell.shape)
+        else:
+            fin = np.where(np.isfinite(ell), ell, -np.inf)
+            kmax = np.argmax(fin, axis=-1)[..., None]
+            m = np.where(normal, np.take_along_axis(ell, kmax, axis=-1)[..., 0], 0.0)
+            bk = np.take_along_axis(bias, kmax, axis=-1)
+            ck = np.take_along_axis(cs, kmax, axis=-1)
+            d = (bias - bk) + (cs - ck)
+            d = np.where(np.isfinite(ell), d, ell - m[..., None])
+            w = np.exp(d)
     w = np.where(normal[..., None], w, 0.0)
     rowsum = w.sum(axis=-1)
     return m, w, rowsum, (nan_row, inf_row, empty_row, normal)
@@ -153,8 +180,8 @@ def _softmax_parts(ell):
 
 def weights(query, key, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
     """The materialised (..., L, S) attention weights P (NaN rows for NaN/+inf logits, 0 rows when empty)."""
-    ell = logits(query, key, attn_mask, is_causal, scale, enable_gqa)
-    _, w, rowsum, (nan_row, inf_row, _, normal) = _softmax_parts(ell)
+    _, w, rowsum, (nan_row, inf_row, _, normal) = _softmax_parts(
+        *_logit_parts(query, key, attn_mask, is_causal, scale, enable_gqa))
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(normal[..., None], w / np.where(normal, rowsum, 1.0)[..., None], 0.0)
     p = np.where((nan_row | inf_row)[..., None], np.nan, p)
@@ -178,9 +205,9 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scal
     if not enable_gqa and q.ndim >= 3 and k.ndim >= 3 and q.shape[-3] != k.shape[-3] \
             and k.shape[-3] != 1 and q.shape[-3] != 1:
         raise ValueError("query and key heads differ: pass enable_gqa=True")
-    ell = logits(q, k, attn_mask, is_causal, scale, enable_gqa)
     _, vv = _expand_kv(q, k, v, enable_gqa)
-    m, w, rowsum, (nan_row, inf_row, empty_row, normal) = _softmax_parts(ell)
+    m, w, rowsum, (nan_row, inf_row, empty_row, normal) = _softmax_parts(
+        *_logit_parts(q, k, attn_mask, is_causal, scale, enable_gqa))
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(normal[..., None], w / np.where(normal, rowsum, 1.0)[..., None], 0.0)
         p = np.where((nan_row | inf_row)[..., None], np.nan, p)

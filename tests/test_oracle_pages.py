@@ -160,22 +160,26 @@ def test_empty_head_dim_gives_mask_only_logits():
 
 
 def test_padding_mask_with_lowest_float():
-    """exactref.ai "Padding masks": the float64 oracle gives PyTorch's [1.5], [1.0].
-
-    The page's exact answer for query 0 is ~1.119, but its printed finite range
-    for a correct implementation that rounds the logits is [1.4999989, 1.5000012];
-    in float64 the score is erased by the huge mask value just as in float32.
-    """
+    """exactref.ai "Padding masks": a padding mask adds float32's lowest value to
+    hidden keys.  In exact arithmetic that shift cancels in the softmax, so query 0
+    (every key padded) weights the values by its scores: the page prints the exact
+    value rounded to float32 as 1.119202971458435 (PyTorch, which rounds the
+    logits, gives the equal-weight 1.5), and 1.0 for query 1.  The oracle gives
+    the exact values, bit for bit after rounding to float32."""
     low = float(np.finfo(np.float32).min)
     rows = {(r[0], int(r[1])): float(r[2]) for r in _golden("exactref_padding_mask.txt")}
     query = np.array([[[1.0], [0.5]]])
     key = np.array([[[1.0], [-1.0]]])
     value = np.array([[[1.0], [2.0]]])
     mask = np.array([[[low, low], [0.0, low]]], dtype=np.float32)
-    out, _ = O.sdpa(query, key, value, attn_mask=mask)
-    assert out[0, 0, 0] == rows[("pytorch", 0)]
-    assert out[0, 1, 0] == rows[("pytorch", 1)]
-    assert rows[("finite_range_low", 0)] <= out[0, 0, 0] <= rows[("finite_range_high", 0)]
+    out, lse = O.sdpa(query, key, value, attn_mask=mask)
+    assert np.float32(out[0, 0, 0]) == np.float32(rows[("rounded", 0)])
+    assert np.float32(out[0, 1, 0]) == np.float32(rows[("rounded", 1)])
+    exact0 = (math.exp(1.0) + 2 * math.exp(-1.0)) / (math.exp(1.0) + math.exp(-1.0))
+    assert out[0, 0, 0] == pytest.approx(exact0, rel=1e-15)
+    # lse: the padded logits' common value plus log(e + 1/e) (row 0), 0.5 plus log(1 + ~0) (row 1)
+    assert lse[0, 0] == low + math.log(math.exp(1.0) + math.exp(-1.0))
+    assert lse[0, 1] == 0.5
 
 
 def _brute(q, k, v, bias, scale):
