@@ -95,26 +95,82 @@ def load_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0):
-    """The float64 oracle on the host cores, on whole heads of the headline workload."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def _cpu_info():
+    """(model name from /proc/cpuinfo, cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def oracle_timing(calls, work, unit, sample):
+    """The float64 oracle on the host cores: one warm-up call, then the whole sample
+    (``calls``, a list of thunks) timed 3 times; the median gives ``work`` / s in ``unit``."""
+    from threadpoolctl import threadpool_limits
+    model, cores = _cpu_info()
+    with threadpool_limits(limits=cores):
+        calls[0]()
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for c in calls:
+                c()
+            times.append(time.perf_counter() - t0)
+    med = sorted(times)[1]
+    return {"value": round(work / med, 6), "unit": unit, "cores": cores, "cpu": model, "kind": "oracle",
+            "median_of": 3, "seconds": round(med, 3), "sample": sample}
+
+
+def cpu_baseline(n_heads=24):
+    """The float64 oracle on whole heads of the headline workload (median of 3 passes)."""
     from oracle import sdpa_oracle as O
     from transformer_attention_04_amd import inputs
     q, k, v = inputs.workload_inputs("bf16_causal_e128")
     B, H, L, E = q.shape
     per_head_flops = flops_prefill(1, 1, L, L, E, True)[0]
-    done, t0 = 0, time.perf_counter()
-    order = [(b, h) for b in range(B) for h in range(H)]
-    while done < len(order) and time.perf_counter() - t0 < budget_s:
-        b, h = order[done]
-        O.sdpa(q[b, h], k[b, h], v[b, h], is_causal=True)
-        done += 1
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": round(per_head_flops * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of {B * H} heads (causal, L=S={L}, E={E}) in {dt:.1f} s, float64 numpy"}
+    heads = [(i // H, i % H) for i in range(min(n_heads, B * H))]
+    calls = [lambda b=b, h=h: O.sdpa(q[b, h], k[b, h], v[b, h], is_causal=True) for b, h in heads]
+    return oracle_timing(calls, per_head_flops * len(heads) / 1e12, "TFLOP/s",
+                         f"{len(heads)} of {B * H} heads (causal, L=S={L}, E={E}), float64 numpy")
+
+
+def cpu_secondary():
+    """The oracle beside the secondary workloads, each on a bounded sample (median of 3)."""
+    from oracle import sdpa_oracle as O
+    from transformer_attention_04_amd import inputs
+    res = {}
+    q, k, v = inputs.workload_inputs("bf16_neox_e96")
+    f = flops_prefill(1, 1, 2048, 2048, 96, True)[0]
+    calls = [lambda h=h: O.sdpa(q[0, h], k[0, h], v[0, h], is_causal=True) for h in range(4)]
+    res["bf16_neox_e96"] = oracle_timing(calls, 4 * f / 1e12, "TFLOP/s", "4 of 128 heads, scale 1/sqrt(96)")
+    bias = inputs.alibi_causal_bias(64, 2048, 2048).numpy()
+    calls = [lambda h=h: O.sdpa(q[0, h], k[0, h], v[0, h], attn_mask=bias[h], is_causal=True) for h in range(4)]
+    res["bf16_neox_e96 alibi+causal"] = oracle_timing(calls, 4 * f / 1e12, "TFLOP/s", "4 of 128 heads")
+    del q, k, v, bias
+    w = inputs.WORKLOADS["fp16_varlen_e64"]
+    lengths = inputs.segment_lengths(seed=w["len_seed"])[:8]
+    qv, kv, vv, cu = inputs.varlen_inputs(lengths, 8, 8, 64, "fp16", seed=w["seed"])
+    cu8 = cu.numpy()
+    fl = sum(4 * 64 * l * (l + 1) // 2 for l in lengths) * 8
+    res["fp16_varlen_e64"] = oracle_timing([lambda: O.sdpa_varlen(qv[0], kv[0], vv[0], cu8, is_causal=True)],
+                                           fl / 1e12, "TFLOP/s", f"the first 8 of the 32 segments ({sum(lengths)} "
+                                           "tokens, 8 heads)")
+    q, k, v = inputs.workload_inputs("fp32_single_head")
+    res["fp32_single_head"] = oracle_timing([lambda: O.sdpa(q, k, v)], 1.0, "calls/s", "the whole workload")
+    # decode: 2 sequences of the workload's shape (32768 keys, Hq=32 over Hkv=8, E=128, bf16 values)
+    q, k, v = inputs.randn_qkv((2, 32, 1, 128), (2, 8, 32768, 128), (2, 8, 32768, 128), "bf16", seed=0)
+    groups = [(b, g) for b in range(2) for g in range(8)]
+    nbytes = len(groups) * (2 * 2 * 32768 * 128 + 2 * 2 * 4 * 128)
+    calls = [lambda b=b, g=g: O.sdpa(q[b, 4 * g:4 * g + 4], k[b, g:g + 1], v[b, g:g + 1]) for b, g in groups]
+    res["bf16_gqa_decode"] = oracle_timing(calls, nbytes / 1e9, "GB/s",
+                                           "16 key/value-head groups of the same shape (2 sequences, seed 0)")
+    return res
 
 
 def bench_prefill(name, steps, warmup, scale=None, mask=None, device="cuda"):
@@ -420,6 +476,15 @@ def main(argv=None):
         "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline(),
         "secondary": secondary,
     }
+    if not a.no_cpu_baseline and run_all:
+        cpu = cpu_secondary()
+        beside = {"bf16_neox_e96 scale=1/sqrt96": "bf16_neox_e96", "bf16_neox_e96 alibi+causal":
+                  "bf16_neox_e96 alibi+causal", "fp16_varlen_e64": "fp16_varlen_e64",
+                  "fp32_single_head": "fp32_single_head", "bf16_gqa_decode": "bf16_gqa_decode",
+                  "bf16_gqa_decode paged": "bf16_gqa_decode"}
+        for name, key in beside.items():
+            if name in secondary:
+                secondary[name]["cpu_oracle"] = cpu[key]
     print(json.dumps(line), flush=True)
     return 0
 

@@ -142,10 +142,12 @@ sdpa_status sdpa_fwd_workspace_size(sdpa_dtype dtype,
  *        only to key segment s; with is_causal, key j of the segment is kept
  *        for query i of the segment when j <= i (local indices).
  *   max_seqlen_q, max_seqlen_k
- *        upper bounds of the segment lengths; they size the launch.  Query rows
- *        of a segment beyond max_seqlen_q are not computed, and offsets are
- *        clamped to [0, total] on the device, so bad offsets never read or
- *        write out of bounds.
+ *        upper bounds of the segment lengths, which the caller must keep: they
+ *        size the launch.  If a segment is longer anyway, its query rows
+ *        beyond max_seqlen_q are not computed (left unwritten) and its keys
+ *        beyond max_seqlen_k are not attended, in sdpa_fwd_varlen and
+ *        sdpa_bwd_varlen alike; offsets are clamped to [0, total] on the
+ *        device, so bad offsets never read or write out of bounds.
  *   out  packed (total_q, Hq, Ev), dtype
  *   lse  (Hq, total_q) float32: element (h, t) at lse + h*lse_stride_head + t
  *
@@ -168,9 +170,14 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype,
 
 /*
  * sdpa_fwd_paged -- attention of new query rows against a paged key/value
- * cache (the serving layout of vLLM-style engines the pages mention): the
- * cached keys of a sequence live in fixed-size pages of a shared pool, listed
- * in order by the sequence's row of a block table.  Decode steps (L * Hq / Hkv
+ * cache: the cached keys of a sequence live in fixed-size pages of a shared
+ * pool, listed in order by the sequence's row of a block table.  This is the
+ * serving layout behind the paged KV cache and PagedAttention that the
+ * hourtab.com "xFormers developer on retainer" page names in its "Related
+ * retainer posts" (FlashInfer, vLLM), where sequences of a batch read pages
+ * outside their own allocation; the decode it serves is the memory-bound
+ * generation step of the khchao.com NN Lab page, "Arithmetic Intensity of
+ * Autoregressive Decoding".  Decode steps (L * Hq / Hkv
  * <= 16 rows per cache head) run the split-KV kernel and its merge; longer
  * chunks of new rows (chunked prefill) run the single-pass kernel, which reads
  * the pages itself and needs no workspace.

@@ -45,7 +45,8 @@ tolerances come out 8.1e-6 (ulps=2) and 1.24e-5 (ulps=8) against the page's
 
 Named algorithms (``algorithm=Blocked(...)``): the page budgets for them the
 roundings its default omits, and this option adds exactly those: the weights
-rounded to the input format before the value product, online-softmax rescaling
+rounded to the input format before the value product (optionally also in the
+row sum the output is divided by), online-softmax rescaling
 of the running sums (one rescale per key block after the first, each an exp
 within ulps and a rounded product; the exp error cancels between value sum and
 row sum in the output but not in the logsumexp), and the output formed with a
@@ -90,6 +91,8 @@ class Blocked:
 
     block_n:     keys per block (rescales per row = key blocks - 1)
     round_weights: weights rounded to the input format before the value product
+    round_row_sum: the row sum that divides the output adds those rounded weights
+                 (the logsumexp still takes the unrounded ones)
     reciprocal:  output = value sum * (1 / row sum)
     Implementation allowances (0 / 1: off):
     shift_slack: the shift may trail the row maximum by this much (natural-log units)
@@ -103,6 +106,7 @@ class Blocked:
     """
     block_n: int = 64
     round_weights: bool = True
+    round_row_sum: bool = False
     reciprocal: bool = True
     shift_slack: float = 0.0
     extra_logit_roundings: int = 0
@@ -416,6 +420,9 @@ def _row_model(q, k, v, bias, sc, fmt, ulps, standard, alg):
     if alg is not None and alg.round_weights and fmt != "fp32":
         wv = _round(w, fmt)
     vsum = _values(wv, v, standard, n_resc)
+    ls = (np.maximum(row_sum[0], 2.0 ** -149), np.maximum(row_sum[1], 2.0 ** -149))   # for lse
+    if alg is not None and alg.round_row_sum and wv is not w:
+        row_sum = _accumulate(wv, 1, standard, n_extra=n_resc)
     rs = (np.maximum(row_sum[0], 2.0 ** -149), np.maximum(row_sum[1], 2.0 ** -149))
     if alg is not None and alg.reciprocal:
         inv = _round(_iv_div_pos((np.ones(L), np.ones(L)), rs))
@@ -424,10 +431,9 @@ def _row_model(q, k, v, bias, sc, fmt, ulps, standard, alg):
         o = _round(_iv_div_pos(vsum, (rs[0][:, None], rs[1][:, None])))
     o = (np.where(has[:, None], o[0], 0.0), np.where(has[:, None], o[1], 0.0))   # no kept key: 0
     # logsumexp sees the row sum with the rescale factors' exp errors (they cancel in the output)
-    ls = rs
     if n_resc:
         f = (1 + (ulps + 0.5) * 2.0 ** -23) ** n_resc
-        ls = (_rd(rs[0] / f, "fp32"), _ru(rs[1] * f, "fp32"))
+        ls = (_rd(ls[0] / f, "fp32"), _ru(ls[1] * f, "fp32"))
     lse = _round(_iv_add(m, _log_within(ls, ulps, extra=slack)), extra=slack)
     for _ in range(alg.extra_lse_roundings if alg is not None else 0):
         lse = _round(lse)
@@ -442,7 +448,7 @@ def _split_model(q, k, v, bias, sc, fmt, ulps, standard, alg):
     rounded product with ln 2)."""
     S = k.shape[0]
     bounds = list(range(0, S, alg.split_size)) + [S]
-    inner = Blocked(alg.block_n, alg.round_weights, alg.reciprocal, alg.shift_slack,
+    inner = Blocked(alg.block_n, alg.round_weights, alg.round_row_sum, alg.reciprocal, alg.shift_slack,
                     alg.extra_logit_roundings, alg.extra_shift_roundings, alg.extra_lse_roundings, 0)
     parts = [_row_model(q, k[a:b], v[a:b], bias[:, a:b], sc, fmt, ulps, standard, inner)
              for a, b in zip(bounds[:-1], bounds[1:])]

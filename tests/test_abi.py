@@ -106,37 +106,29 @@ def test_gqa_rules(lib):
     assert st == S.SDPA_ERR_INVALID_ARGUMENT
 
 
-def test_unsupported_head_dims(lib):
-    # other head dims (multiples of 8 up to 128) run unmasked on bf16/fp16 only, with E == Ev
-    st, _ = call(lib, *qkv(E=80), dtype=S.SDPA_F32)
-    assert st == S.SDPA_ERR_UNSUPPORTED
-    st, _ = call(lib, *qkv(E=80), mask=t4((1, 1, 16, 32)))
-    assert st == S.SDPA_ERR_UNSUPPORTED
+def test_head_dim_limits(lib):
+    """Head dims E and Ev must be multiples of 8 up to 128 (E = 0 included); calls
+    outside that are refused before anything is launched."""
     for e in (4, 84, 136, 256):
         st, _ = call(lib, *qkv(E=e))
         assert st == S.SDPA_ERR_UNSUPPORTED, e
-    st, _ = call(lib, *qkv(E=64, Ev=80))
-    assert st == S.SDPA_ERR_UNSUPPORTED
-    st, _ = call(lib, *qkv(E=80, Ev=64))
-    assert st == S.SDPA_ERR_UNSUPPORTED
-    # the split-KV decode takes head dims 64, 96, 128 only
-    q, k, v = qkv(L=1, E=80)
-    n = ctypes.c_size_t(0)
-    st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
-                                     None, 0, 0, 2, ctypes.byref(n))
-    assert st == S.SDPA_ERR_UNSUPPORTED
-    st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
-                                     None, 0, 0, 0, ctypes.byref(n))
-    assert st == S.SDPA_OK and n.value == 0
-    # E != Ev runs on the 16-bit kernels only (masked or not), with head dims 64/96/128
-    st, msg = call(lib, *qkv(E=64, Ev=128), dtype=S.SDPA_F32)
-    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
-    st, msg = call(lib, *qkv(E=128, Ev=64), dtype=S.SDPA_F32, mask=t4((1, 1, 16, 32)))
-    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
-    st, msg = call(lib, *qkv(E=128, Ev=80), mask=t4((1, 1, 16, 32)))
-    assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg
-    st, _ = call(lib, *qkv(E=0))
-    assert st == S.SDPA_ERR_UNSUPPORTED
+        st, _ = call(lib, *qkv(E=e), dtype=S.SDPA_F32)
+        assert st == S.SDPA_ERR_UNSUPPORTED, e
+    for ev in (12, 132):
+        st, msg = call(lib, *qkv(E=64, Ev=ev))
+        assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg, ev
+        st, msg = call(lib, *qkv(E=128, Ev=ev), dtype=S.SDPA_F32, mask=t4((1, 1, 16, 32)))
+        assert st == S.SDPA_ERR_UNSUPPORTED and "Ev" in msg, ev
+    # the split-KV decode takes head dims 64, 96, 128 only; others run single-pass (no workspace)
+    for E, Ev in ((80, 80), (0, 64), (64, 40)):
+        q, k, v = qkv(L=1, E=E, Ev=Ev)
+        n = ctypes.c_size_t(0)
+        st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                         None, 0, 0, 2, ctypes.byref(n))
+        assert st == S.SDPA_ERR_UNSUPPORTED, (E, Ev)
+        st = lib.sdpa_fwd_workspace_size(S.SDPA_BF16, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                         None, 0, 0, 0, ctypes.byref(n))
+        assert st == S.SDPA_OK and n.value == 0, (E, Ev)
 
 
 def test_layout_requirements(lib):
@@ -205,9 +197,9 @@ def test_varlen_argument_errors(lib):
     assert varlen(Hkv=2) == S.SDPA_ERR_INVALID_ARGUMENT
     assert varlen(Hkv=3, gqa=1) == S.SDPA_ERR_INVALID_ARGUMENT
     assert varlen(cq=None) == S.SDPA_ERR_INVALID_ARGUMENT
-    assert varlen(E=80, Ev=80) == S.SDPA_ERR_UNSUPPORTED
-    assert varlen(E=64, Ev=80) == S.SDPA_ERR_UNSUPPORTED
-    assert varlen(dtype=S.SDPA_F32, E=64, Ev=128) == S.SDPA_ERR_UNSUPPORTED
+    assert varlen(E=84, Ev=84) == S.SDPA_ERR_UNSUPPORTED
+    assert varlen(E=64, Ev=136) == S.SDPA_ERR_UNSUPPORTED
+    assert varlen(dtype=S.SDPA_F32, E=132, Ev=128) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(q=FAKE + 4) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(kt=510) == S.SDPA_ERR_UNSUPPORTED
     assert varlen(n=-1) == S.SDPA_ERR_INVALID_ARGUMENT
@@ -245,7 +237,11 @@ def test_paged_plan_rules(lib):
     assert ws(L=4, splits=2)[0] == S.SDPA_OK
     assert ws(ps=48)[0] == S.SDPA_ERR_UNSUPPORTED
     assert ws(ps=8)[0] == S.SDPA_ERR_UNSUPPORTED
-    assert ws(E=64, Ev=128)[0] == S.SDPA_ERR_UNSUPPORTED
+    st, n = ws(L=4, E=64, Ev=128)          # Ev != E decode: split-KV with Ev-wide partials
+    assert st == S.SDPA_OK and n > 4 * 8 * 4 * 128 * 4
+    assert ws(L=1, E=40, Ev=40) == (S.SDPA_OK, 0)   # other head dims: single pass, decode steps too
+    assert ws(L=1, E=40, Ev=40, splits=2)[0] == S.SDPA_ERR_UNSUPPORTED
+    assert ws(E=84, Ev=84)[0] == S.SDPA_ERR_UNSUPPORTED
     assert ws(dtype=S.SDPA_F32)[0] == S.SDPA_ERR_UNSUPPORTED
     assert ws(splits=-1)[0] == S.SDPA_ERR_INVALID_ARGUMENT
 
@@ -261,13 +257,12 @@ def test_varlen_backward_argument_errors(lib):
                                    p, st, sh, a["cq"], a["ck"], a["n"], a["mq"], a["mk"], a["Hq"], a["Hkv"],
                                    a["E"], a["Ev"], a["tq"], a["tk"], a["causal"], None, a["gqa"],
                                    p, st, sh, p, st, sh, p, st, sh, a["ws"], a["wsb"], None)
-    assert call(dtype=S.SDPA_F32) == S.SDPA_ERR_UNSUPPORTED
     assert call(dtype=S.SDPA_BOOL) == S.SDPA_ERR_INVALID_ARGUMENT
     assert call(Hkv=2) == S.SDPA_ERR_INVALID_ARGUMENT        # grouped heads need enable_gqa
     assert call(Hkv=3, gqa=1) == S.SDPA_ERR_INVALID_ARGUMENT
     assert call(cq=None) == S.SDPA_ERR_INVALID_ARGUMENT
-    assert call(E=128, Ev=64) == S.SDPA_ERR_UNSUPPORTED
-    assert call(E=80, Ev=80) == S.SDPA_ERR_UNSUPPORTED
+    assert call(E=128, Ev=136) == S.SDPA_ERR_UNSUPPORTED       # head dims up to 128
+    assert call(E=12, Ev=12) == S.SDPA_ERR_UNSUPPORTED         # multiples of 8
     assert call(ptr=FAKE + 8) == S.SDPA_ERR_UNSUPPORTED       # misaligned base
     assert call(st=1020) == S.SDPA_ERR_UNSUPPORTED            # stride not a multiple of 8
     assert call(wsb=8 * 365 * 4) == S.SDPA_ERR_INVALID_ARGUMENT   # workspace too small
@@ -292,7 +287,7 @@ def test_paged_varlen_argument_errors(lib):
     assert call(gqa=0) == S.SDPA_ERR_INVALID_ARGUMENT          # 8 query heads over 2 cache heads
     assert call(Hq=5) == S.SDPA_ERR_INVALID_ARGUMENT           # not a multiple of the cache heads
     assert call(kc=t4((64, 2, 48, 128)), vc=t4((64, 2, 48, 128))) == S.SDPA_ERR_UNSUPPORTED  # page size
-    assert call(vc=t4((64, 2, 64, 64))) == S.SDPA_ERR_UNSUPPORTED                           # E != Ev
+    assert call(vc=t4((64, 2, 64, 84))) == S.SDPA_ERR_UNSUPPORTED                           # Ev % 8 != 0
     assert call(vc=t4((63, 2, 64, 128))) == S.SDPA_ERR_INVALID_ARGUMENT                     # pools differ
     assert call(bts=8) == S.SDPA_ERR_INVALID_ARGUMENT           # max_blocks > table stride
     assert call(cu=None) == S.SDPA_ERR_INVALID_ARGUMENT

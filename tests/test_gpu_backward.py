@@ -25,7 +25,12 @@ def _np(t):
     return t.detach().cpu().double().numpy()
 
 
-def bwd_bar(ref):
+def bwd_bar(ref, dtype="bf16"):
+    """bf16/fp16: 2^-6 max|ref| + 1e-3 (the derivation above).  fp32 (the vector-ALU
+    backward: every step in fp32, P from exp of the rounded logit minus lse, sums over
+    at most a few hundred terms, each within a few float32 ulps): 2^-14 max|ref| + 1e-5."""
+    if dtype == "fp32":
+        return 2.0 ** -14 * float(np.abs(ref).max(initial=0.0)) + 1e-5
     return 2.0 ** -6 * float(np.abs(ref).max(initial=0.0)) + 1e-3
 
 
@@ -43,15 +48,16 @@ def run_bwd(q, k, v, g, dtype, **kw):
     return (dq, dk, dv), O.sdpa_backward(q, k, v, g, **kw)
 
 
-def assert_bwd(gpu, ref, what):
+def assert_bwd(gpu, ref, what, dtype="bf16"):
     errs = []
     for a, r, n in zip(gpu, ref, ("dq", "dk", "dv")):
         a = _np(a)
         assert a.shape == r.shape, (what, n, a.shape, r.shape)
         assert np.isfinite(a).all(), f"{what}: non-finite {n}"
         e = float(np.abs(a - r).max(initial=0.0))
-        errs.append((e, e / bwd_bar(r)))
-        assert e <= bwd_bar(r), f"{what}: max |{n} error| {e:.3e} > {bwd_bar(r):.3e} (max|ref| {np.abs(r).max():.3e})"
+        bar = bwd_bar(r, dtype)
+        errs.append((e, e / bar))
+        assert e <= bar, f"{what}: max |{n} error| {e:.3e} > {bar:.3e} (max|ref| {np.abs(r).max(initial=0):.3e})"
     print(f"{what}: max error (fraction of the bar) " +
           " ".join(f"{n} {e:.2e} ({f:.2f})" for n, (e, f) in zip(("dq", "dk", "dv"), errs)))
     return errs
@@ -208,3 +214,53 @@ def test_backward_random_configuration(ci):
         kw["attn_mask"] = fm if c["mask"] == "float" else bm
     gpu, ref = run_bwd(q, k, v, g, c["dtype"], **kw)
     assert_bwd(gpu, ref, f"case {ci}: {c}")
+
+
+VEC_DIMS = [(64, 128), (128, 64), (40, 40), (0, 32), (96, 24), (64, 64), (128, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("E,Ev", VEC_DIMS)
+def test_backward_vector_alu(dtype, E, Ev):
+    """fp32 inputs, value rows of another width (Ev != E) and other head dims (E = 0
+    included) run on the vector-ALU backward: masks (float with -inf entries and an
+    empty row, bool), causal, grouped heads, signed and unit scales, ragged tiles."""
+    if dtype != "fp32" and E == Ev and E in (64, 128):
+        pytest.skip("bf16/fp16 with E == Ev in {64, 96, 128} run the matrix-core backward (tests above)")
+    B, Hq, Hkv, L, Sk = 2, 4, 2, 150, 170
+    q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, Ev), dtype, seed=E * 3 + Ev)
+    g = inputs.randn_qkv((B, Hq, L, Ev), (1, 1, 1, 8), (1, 1, 1, 8), dtype, seed=E * 3 + Ev + 1)[0]
+    gen = torch.Generator().manual_seed(E + Ev)
+    fm = torch.randn((1, Hq, L, Sk), generator=gen)
+    fm[torch.rand((1, Hq, L, Sk), generator=gen) < 0.1] = float("-inf")
+    fm[..., 7, :] = float("-inf")
+    bm = torch.rand((B, 1, L, Sk), generator=gen) < 0.8
+    for m, causal, scale in ((None, False, None), (None, True, -0.3), (fm, True, None), (bm, False, 1.0)):
+        gpu, ref = run_bwd(q, k, v, g, dtype, attn_mask=m, is_causal=causal, scale=scale, enable_gqa=True)
+        assert_bwd(gpu, ref, f"{dtype} E={E} Ev={Ev} mask={None if m is None else m.dtype} causal={causal} "
+                             f"scale={scale}", dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("E,Ev", [(64, 64), (40, 72)])
+def test_backward_vector_alu_packed(dtype, E, Ev):
+    """Packed segments on the vector-ALU backward, causal and not, grouped heads."""
+    lengths = [1, 37, 128, 129, 300]
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    tot = sum(lengths)
+    q, k, v = inputs.randn_qkv((1, tot, 4, E), (1, tot, 2, E), (1, tot, 2, Ev), dtype, seed=E + Ev + 90)
+    g = inputs.randn_qkv((1, tot, 4, Ev), (1, 1, 1, 8), (1, 1, 1, 8), dtype, seed=E + Ev + 91)[0]
+    qd, kd, vd, gd, cud = (t.to(DEV) for t in (q, k, v, g, cu))
+    for causal in (False, True):
+        out, lse = S.sdpa_fwd_varlen(qd, kd, vd, cud, max_seqlen_q=300, max_seqlen_k=300, is_causal=causal,
+                                     enable_gqa=True)
+        dq, dk, dv = S.sdpa_bwd_varlen(qd, kd, vd, out, lse, gd, cud, max_seqlen_q=300, max_seqlen_k=300,
+                                       is_causal=causal, enable_gqa=True)
+        torch.cuda.synchronize()
+        c = cu.tolist()
+        for i in range(len(lengths)):
+            a, b = c[i], c[i + 1]
+            seg = [t[0, a:b].permute(1, 0, 2)[None] for t in (q, k, v, g)]
+            ref = O.sdpa_backward(*seg, is_causal=causal, enable_gqa=True)
+            gpu = [t[0, a:b].permute(1, 0, 2)[None] for t in (dq, dk, dv)]
+            assert_bwd(gpu, ref, f"{dtype} E={E} Ev={Ev} causal={causal} segment {i}", dtype)

@@ -114,7 +114,31 @@ def draw_value_dim(rng):
                                                          rng.choice(["full", "row", "head", "batch"])))
 
 
-VCASES = [draw_value_dim(random.Random(5000 + i)) for i in range(24)]
+def _draw_with_key_lengths(rng):
+    c = draw_value_dim(rng)
+    # packed key segments of their own lengths (cu_seqlens_k differs from cu_seqlens_q)
+    c["lengths_k"] = [rng.choice([0, 1, 17, 64, 100, 300]) for _ in c["lengths"]]
+    return c
+
+
+VCASES = [_draw_with_key_lengths(random.Random(5000 + i)) for i in range(24)]
+
+
+def _packed_pieces(q, k, v, out, lse, lengths, lengths_k, causal, scale, gqa):
+    """(gpu out, gpu lse, oracle out, oracle lse) per segment of a packed call whose query
+    and key segments have their own lengths (causal top-left within a segment)."""
+    cq = np.concatenate([[0], np.cumsum(lengths)]).astype(int)
+    ck = np.concatenate([[0], np.cumsum(lengths_k)]).astype(int)
+    pieces = []
+    for i, n in enumerate(lengths):
+        if n == 0:
+            continue
+        a, c0, nk = cq[i], ck[i], lengths_k[i]
+        qs = q[a:a + n].permute(1, 0, 2).contiguous()
+        ks, vs = (t[c0:c0 + nk].permute(1, 0, 2).contiguous() for t in (k, v))
+        ro, rl = O.sdpa(qs, ks, vs, is_causal=causal, scale=scale, enable_gqa=gqa)
+        pieces.append((out[a:a + n].permute(1, 0, 2), lse[:, a:a + n], ro, rl))
+    return pieces
 
 
 @pytest.mark.parametrize("ci", range(len(VCASES)))
@@ -123,24 +147,19 @@ def test_random_value_dim_configuration(ci):
     gqa = c["Hq"] != c["Hkv"]
     tol_o, tol_l = TOL[c["dtype"]]
     if c["packed"]:
-        lengths = c["lengths"]
+        lengths, lengths_k = c["lengths"], c["lengths_k"]
         cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
-        tot = int(cu[-1])
-        q, k, v = inputs.randn_qkv((tot, c["Hq"], c["E"]), (tot, c["Hkv"], c["E"]), (tot, c["Hkv"], c["Ev"]),
+        cuk = torch.tensor([0] + list(np.cumsum(lengths_k)), dtype=torch.int32)
+        tot, totk = int(cu[-1]), int(cuk[-1])
+        q, k, v = inputs.randn_qkv((tot, c["Hq"], c["E"]), (totk, c["Hkv"], c["E"]), (totk, c["Hkv"], c["Ev"]),
                                    c["dtype"], seed=ci + 300)
-        if tot == 0:
-            return
-        out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), is_causal=c["causal"],
-                                     scale=c["scale"], enable_gqa=gqa)
+        out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), cuk.to(DEV),
+                                     is_causal=c["causal"], scale=c["scale"], enable_gqa=gqa)
         torch.cuda.synchronize()
-        pieces = []
-        for i, n in enumerate(lengths):
-            a = int(cu[i])
-            if n == 0:
-                continue
-            qs, ks, vs = (t[a:a + n].permute(1, 0, 2).contiguous() for t in (q, k, v))
-            ro, rl = O.sdpa(qs, ks, vs, is_causal=c["causal"], scale=c["scale"], enable_gqa=gqa)
-            pieces.append((out[a:a + n].permute(1, 0, 2), lse[:, a:a + n], ro, rl))
+        if tot == 0:   # no query token: nothing to compute, and nothing comes back
+            assert out.shape == (0, c["Hq"], c["Ev"]) and lse.shape == (c["Hq"], 0)
+            return
+        pieces = _packed_pieces(q, k, v, out, lse, lengths, lengths_k, c["causal"], c["scale"], gqa)
     else:
         q, k, v = inputs.randn_qkv((c["B"], c["Hq"], c["L"], c["E"]), (c["B"], c["Hkv"], c["S"], c["E"]),
                                    (c["B"], c["Hkv"], c["S"], c["Ev"]), c["dtype"], seed=ci + 300)
@@ -160,3 +179,28 @@ def test_random_value_dim_configuration(ci):
         eo = np.abs(go[fo] - ro[fo]).max(initial=0.0)
         el = np.abs(gl[fl] - rl[fl]).max(initial=0.0)
         assert eo <= tol_o and el <= tol_l, f"{c}: out err {eo:.3e}, lse err {el:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("E,Ev", [(64, 64), (128, 128), (64, 128), (128, 96)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_key_segments_of_their_own_lengths(dtype, E, Ev, causal):
+    """cu_seqlens_k != cu_seqlens_q: query segments [5, 130, 0, 64, 300] against key
+    segments [200, 7, 33, 64, 1] (more keys than queries, fewer, an empty query
+    segment, equal, a single key), causal top-left within each segment, GQA 4:2."""
+    lengths, lengths_k = [5, 130, 0, 64, 300], [200, 7, 33, 64, 1]
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    cuk = torch.tensor([0] + list(np.cumsum(lengths_k)), dtype=torch.int32)
+    q, k, v = inputs.randn_qkv((sum(lengths), 4, E), (sum(lengths_k), 2, E), (sum(lengths_k), 2, Ev), dtype,
+                               seed=E + Ev + causal)
+    out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), cuk.to(DEV), max_seqlen_q=300,
+                                 max_seqlen_k=200, is_causal=causal, enable_gqa=True)
+    torch.cuda.synchronize()
+    tol_o, tol_l = TOL[dtype]
+    for o, l, ro, rl in _packed_pieces(q, k, v, out, lse, lengths, lengths_k, causal, None, True):
+        go, gl = o.detach().cpu().double().numpy(), l.detach().cpu().double().numpy()
+        empty = np.isneginf(rl)
+        assert np.isneginf(gl[empty]).all() and (go[empty] == 0).all()
+        fo, fl = np.isfinite(ro), np.isfinite(rl)
+        assert np.abs(go[fo] - ro[fo]).max(initial=0.0) <= tol_o
+        assert np.abs(gl[fl] - rl[fl]).max(initial=0.0) <= tol_l

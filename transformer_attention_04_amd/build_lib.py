@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["sdpa_api.cpp", "prefill_bf16.hip", "prefill_f16.hip", "prefill_f32.hip", "decode.hip",
+SOURCES = ["sdpa_api.cpp", "prefill_bf16.hip", "prefill_f16.hip", "prefill_f32.hip", "decode.hip", "backward_vec.hip",
            "backward.hip"]
 
 # Packed fp32 VALU instructions are kept out of every kernel.  Floating-point

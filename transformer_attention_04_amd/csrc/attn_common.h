@@ -121,7 +121,7 @@ struct BwdParams {
     int B, Hq, Hkv, group, L, S;
     int n_qtiles;   // 128-row query tiles
     int n_ktiles;   // 128-key tiles
-    int elem;       // ELEM_BF16 or ELEM_F16
+    int elem;       // ELEM_BF16 or ELEM_F16 (the vector-ALU backward also ELEM_F32)
     float scale;    // signed
     // Optional mask, as in the forward: float32 bias or uint8 keep flags,
     // element (b, h, i, j) at b*m_sb + h*m_sh + i*m_sr + j (0 strides broadcast)
@@ -135,6 +135,7 @@ struct BwdParams {
     const int* cu_q;
     const int* cu_k;
     int64_t total_q, total_k;
+    int e, ev;      // head dims of query/key rows and value rows
 };
 
 hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,
@@ -145,6 +146,8 @@ hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int elem, int D, hipStream_t stream);
 hipError_t launch_backward(const BwdParams& p, int D, bool causal, int mask, bool varlen, hipStream_t stream);
+// The vector-ALU backward (any element type, head dims up to 128, Ev != E).
+hipError_t launch_backward_vec(const BwdParams& p, bool causal, int mask, hipStream_t stream);
 
 // Tile sizes the host needs for grids and workspace.
 constexpr int kPrefillBlockM = 128;  // query rows per MFMA workgroup

@@ -315,18 +315,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
 template <typename Tr, int D, int DV>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t s) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
-    if constexpr (D == DV) {
-        if (p.block_table) {
-            if (p.rows <= 4)
-                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 4, true>), grid, dim3(256), 0, s, p);
-            else if (p.rows <= 8)
-                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 8, true>), grid, dim3(256), 0, s, p);
-            else
-                hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 16, true>), grid, dim3(256), 0, s, p);
-            goto merge;
-        }
-    } else {
-        if (p.block_table) return hipErrorInvalidValue;  // paged caches have E == Ev
+    if (p.block_table) {
+        if (p.rows <= 4)
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 4, true>), grid, dim3(256), 0, s, p);
+        else if (p.rows <= 8)
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 8, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 16, true>), grid, dim3(256), 0, s, p);
+        goto merge;
     }
     if (p.rows <= 4)
         hipLaunchKernelGGL((decode_split_kernel<Tr, D, DV, 4, false>), grid, dim3(256), 0, s, p);

@@ -41,6 +41,12 @@ struct BF16 {
         bf16x2_t v = {(__bf16)a, (__bf16)b};
         return __builtin_bit_cast(uint32_t, v);
     }
+    // acc + both halves of a packed pair, in fp32 (v_dot2c against (1, 1))
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+    }
 };
 
 struct F16 {
@@ -62,6 +68,11 @@ struct F16 {
         typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
         f16x2_t v = {(_Float16)a, (_Float16)b};
         return __builtin_bit_cast(uint32_t, v);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
+                                      acc, false);
     }
 };
 

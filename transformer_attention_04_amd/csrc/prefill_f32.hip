@@ -11,12 +11,17 @@
 // the E-long dot product well below that of one sequential FMA chain.  Keys
 // and values stream through LDS 32 rows at a time.  The running max is kept
 // in logit units and subtracted before multiplying by log2(e).
+//
+// Padded instances (PADE): head dims E and Ev that are multiples of 8 up to 128
+// (E = 0 included) run at a width D of 64 or 128: columns of Q and K from E on,
+// and of V from Ev on, are never read and stand as 0 (the dot products only gain
+// exact zeros), and output columns from Ev on are never written.
 #include "attn_common.h"
 #include "device_utils.h"
 
 namespace sdpa {
 
-template <int D, bool CAUSAL, int MASK, bool VARLEN>
+template <int D, bool CAUSAL, int MASK, bool VARLEN, bool PADE = false>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
     constexpr int BM = kF32BlockM;
     constexpr int BN = 32;
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
         const int64_t c = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
         const int64_t d = min(max((int64_t)p.cu_k[b + 1], c), p.total_k);
         Lb = (int)min(e - a, (int64_t)p.L);
-        Sb = (int)(d - c);
+        Sb = (int)min(d - c, (int64_t)p.S);  // at most max_seqlen_k, as the backward
         qo = a * p.q_sr + (int64_t)h * p.q_sh;
         ko = c * p.k_sr + (int64_t)kvh * p.k_sh;
         vo = c * p.v_sr + (int64_t)kvh * p.v_sh;
@@ -71,7 +76,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
     const float* qp = (const float*)p.q + qo + (int64_t)min(row, Lb - 1) * p.q_sr;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        qv[i] = valid ? *(const float4*)(qp + i * 16 + part * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool qin = valid && (!PADE || i * 16 + part * 4 < p.e);
+        qv[i] = qin ? *(const float4*)(qp + i * 16 + part * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float* mrow_f = (const float*)p.mask + mo + (int64_t)min(row, Lb - 1) * p.m_sr;
@@ -84,10 +90,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
         for (int c = tid; c < NCH; c += 256) {
             const int r = c / (D / 4), col = (c % (D / 4)) * 4;
             const bool in = key0 + r < Sb;
+            const bool kin = in && (!PADE || col < p.e);
+            const bool vin = in && (!PADE || col < p.dv);
             *(float4*)(Ks + r * RS + col) =
-                in ? *(const float4*)(kp + (int64_t)(key0 + r) * p.k_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+                kin ? *(const float4*)(kp + (int64_t)(key0 + r) * p.k_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
             *(float4*)(Vs + r * RS + col) =
-                in ? *(const float4*)(vp + (int64_t)(key0 + r) * p.v_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+                vin ? *(const float4*)(vp + (int64_t)(key0 + r) * p.v_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         __syncthreads();
         float lg[BN];
@@ -154,51 +162,52 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
             } else {
                 r = make_float4(ov[i].x / l_run, ov[i].y / l_run, ov[i].z / l_run, ov[i].w / l_run);
             }
-            *(float4*)(op + i * 16 + part * 4) = r;
+            if (!PADE || i * 16 + part * 4 < p.dv) *(float4*)(op + i * 16 + part * 4) = r;
         }
         if (part == 0) p.lse[lo + row] = (l_run == 0.f) ? kNegInf : m_run + logf(l_run);
     }
 }
 
-template <int D, bool CAUSAL, int MASK, bool VARLEN>
+template <int D, bool CAUSAL, int MASK, bool VARLEN, bool PADE>
 static hipError_t launch_f32_one(const AttnParams& p, hipStream_t stream) {
     const long long grid = (long long)p.n_qtiles * p.Hq * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, MASK, VARLEN>), dim3((unsigned)grid), dim3(256),
+    hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, MASK, VARLEN, PADE>), dim3((unsigned)grid), dim3(256),
                        0, stream, p);
     return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_f32_d(const AttnParams& p, bool causal, int mask, bool varlen,
-                               hipStream_t s) {
-    if (varlen) {
-        if (mask != MASK_NONE) return hipErrorInvalidValue;
-        return causal ? launch_f32_one<D, true, MASK_NONE, true>(p, s)
-                      : launch_f32_one<D, false, MASK_NONE, true>(p, s);
-    }
+template <int D, bool CAUSAL, bool PADE>
+static hipError_t launch_f32_c(const AttnParams& p, int mask, bool varlen, hipStream_t s) {
+    if (varlen)
+        return mask == MASK_NONE ? launch_f32_one<D, CAUSAL, MASK_NONE, true, PADE>(p, s) : hipErrorInvalidValue;
     switch (mask) {
-        case MASK_NONE:
-            return causal ? launch_f32_one<D, true, MASK_NONE, false>(p, s)
-                          : launch_f32_one<D, false, MASK_NONE, false>(p, s);
-        case MASK_FLOAT:
-            return causal ? launch_f32_one<D, true, MASK_FLOAT, false>(p, s)
-                          : launch_f32_one<D, false, MASK_FLOAT, false>(p, s);
-        case MASK_BOOL:
-            return causal ? launch_f32_one<D, true, MASK_BOOL, false>(p, s)
-                          : launch_f32_one<D, false, MASK_BOOL, false>(p, s);
+        case MASK_NONE: return launch_f32_one<D, CAUSAL, MASK_NONE, false, PADE>(p, s);
+        case MASK_FLOAT: return launch_f32_one<D, CAUSAL, MASK_FLOAT, false, PADE>(p, s);
+        case MASK_BOOL: return launch_f32_one<D, CAUSAL, MASK_BOOL, false, PADE>(p, s);
     }
     return hipErrorInvalidValue;
 }
 
+template <int D, bool PADE>
+static hipError_t launch_f32_d(const AttnParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
+    return causal ? launch_f32_c<D, true, PADE>(p, mask, varlen, s) : launch_f32_c<D, false, PADE>(p, mask, varlen, s);
+}
+
 hipError_t launch_prefill_f32(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                               hipStream_t s) {
-    switch (D) {
-        case 64: return launch_f32_d<64>(p, causal, mask, varlen, s);
-        case 96: return launch_f32_d<96>(p, causal, mask, varlen, s);
-        case 128: return launch_f32_d<128>(p, causal, mask, varlen, s);
+    (void)D;
+    if (p.e == p.dv) {
+        switch (p.e) {
+            case 64: return launch_f32_d<64, false>(p, causal, mask, varlen, s);
+            case 96: return launch_f32_d<96, false>(p, causal, mask, varlen, s);
+            case 128: return launch_f32_d<128, false>(p, causal, mask, varlen, s);
+        }
     }
-    return hipErrorInvalidValue;
+    if (p.e < 0 || p.e > 128 || p.e % 8 != 0 || p.dv < 0 || p.dv > 128 || p.dv % 8 != 0)
+        return hipErrorInvalidValue;
+    return max(p.e, p.dv) <= 64 ? launch_f32_d<64, true>(p, causal, mask, varlen, s)
+                                : launch_f32_d<128, true>(p, causal, mask, varlen, s);
 }
 
 }  // namespace sdpa

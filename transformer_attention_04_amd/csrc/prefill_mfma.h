@@ -123,7 +123,7 @@ void prefill_mfma_kernel(AttnParams p) {
         const int64_t c = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
         const int64_t d = min(max((int64_t)p.cu_k[b + 1], c), p.total_k);
         Lb = (int)min(e - a, (int64_t)p.L);
-        Sb = (int)(d - c);
+        Sb = (int)min(d - c, (int64_t)p.S);  // at most max_seqlen_k, as the backward
         qo = a * p.q_sr + (int64_t)h * p.q_sh;
         ko = c * p.k_sr + (int64_t)kvh * p.k_sh;
         vo = c * p.v_sr + (int64_t)kvh * p.v_sh;
@@ -167,7 +167,7 @@ void prefill_mfma_kernel(AttnParams p) {
     // rows (rows are only 2E bytes apart), and stores of rows past the tile's
     // valid rows would land in them instead of being dropped.
     const int qk_bytes = PADE ? p.e * 2 : D * 2;
-    const int v_bytes = PADE ? p.e * 2 : DV * 2;
+    const int v_bytes = PADE ? p.dv * 2 : DV * 2;
     const int q_rs = (int)(p.q_sr * 2);
     const auto qrs = make_rsrc((const uint16_t*)p.q + qo + (int64_t)q0 * p.q_sr, (qrows - 1) * q_rs + qk_bytes);
     uint4 qreg[NKK];
@@ -211,24 +211,25 @@ void prefill_mfma_kernel(AttnParams p) {
                 if (!okp && k16 < Sb) bad |= 1 << g;
                 const int nv = okp ? min(16, Sb - k16) : 0;
                 const int64_t row = (int64_t)(okp ? pg : 0) * p.k_sb + (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.k_sr;
-                kr[g] = make_rsrc(kbase + row, nv > 0 ? (nv - 1) * k_rs + D * 2 : 0);
+                kr[g] = make_rsrc(kbase + row, nv > 0 ? (nv - 1) * k_rs + qk_bytes : 0);
             }
             bad_ld = bad;
             const int ch = tid & 15;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                kbuf[i] = buf_load16(kr[i], ch < D / 8 ? (tid >> 4) * k_rs + ch * 16 : 0x7ffffff0);
+                kbuf[i] = buf_load16(kr[i], (ch < D / 8 && (!PADE || ch * 8 < p.e)) ? (tid >> 4) * k_rs + ch * 16
+                                                                                     : 0x7ffffff0);
             const int wv = __builtin_amdgcn_readfirstlane(wave);
             const int k16 = key0 + 16 * wv;
             const int pg = k16 < Sb ? p.block_table[(int64_t)b * p.bt_stride + (k16 >> p.page_shift)] : 0;
             const bool okp = (unsigned)pg < (unsigned)p.n_pages;
             const int nv = okp ? min(16, Sb - k16) : 0;
             const int64_t vrow = (int64_t)(okp ? pg : 0) * p.v_sb + (int64_t)(k16 & ((1 << p.page_shift) - 1)) * p.v_sr;
-            const auto vr = make_rsrc(vbase + vrow, nv > 0 ? (nv - 1) * v_rs + DV * 2 : 0);
+            const auto vr = make_rsrc(vbase + vrow, nv > 0 ? (nv - 1) * v_rs + v_bytes : 0);
             const int kq = lane & 3, dc = lane >> 2;
+            const bool vin = dc < DV / 8 && (!PADE || dc * 8 < p.dv);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vbuf[r] = buf_load16(vr, dc < DV / 8 ? (kq * 4 + r) * v_rs + dc * 16 : 0x7ffffff0);
+            for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, vin ? (kq * 4 + r) * v_rs + dc * 16 : 0x7ffffff0);
             return;
         }
         const int rows = min(BN, Sb - key0);
@@ -242,7 +243,7 @@ void prefill_mfma_kernel(AttnParams p) {
         }
         if (VIT == 256 || tid < VIT) {
             const int kg = tid % (BN / 4), dc = tid / (BN / 4);
-            const bool vin = !PADE || dc * 8 < p.e;
+            const bool vin = !PADE || dc * 8 < p.dv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) vbuf[r] = buf_load16(vr, vin ? (kg * 4 + r) * v_rs + dc * 16 : 0x7ffffff0);
         }
@@ -311,7 +312,8 @@ void prefill_mfma_kernel(AttnParams p) {
     // Running shift in log2 units (-inf until the row sees a kept key) and this
     // lane's share of the row sum relative to it.
     float sh_run = kNegInf;
-    float l_run = 0.f;
+    float l_run = 0.f;    // row sum of the fp32 weights (for lse)
+    float lr_run = 0.f;   // row sum of the weights rounded to 16 bits (normalises the output)
     // log2-domain logit = t * cfac, with t the raw score (or the fp32 logit when a
     // float mask is added).
     const float cfac = (MASK == MASK_FLOAT) ? kLog2e : p.scale_log2;
@@ -451,6 +453,7 @@ void prefill_mfma_kernel(AttnParams p) {
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
                 }
+                float r4[4];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -460,6 +463,7 @@ void prefill_mfma_kernel(AttnParams p) {
                         pb.y = Tr::pack2(s[kb][c * 8 + 2], s[kb][c * 8 + 3]);
                         pb.z = Tr::pack2(s[kb][c * 8 + 4], s[kb][c * 8 + 5]);
                         pb.w = Tr::pack2(s[kb][c * 8 + 6], s[kb][c * 8 + 7]);
+                        r4[kb * 2 + c] = Tr::sum2(pb.w, Tr::sum2(pb.z, Tr::sum2(pb.y, Tr::sum2(pb.x, 0.f))));
                         const int lchunk = kb * 4 + c * 2 + hh;
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
@@ -468,6 +472,7 @@ void prefill_mfma_kernel(AttnParams p) {
                             acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb), acc[db]);
                         }
                     }
+                lr_run = fmaf(lr_run, alpha, (r4[0] + r4[1]) + (r4[2] + r4[3]));
             };
             if (edge || MASK == MASK_BOOL)
                 softmax_pv(std::integral_constant<bool, true>{});
@@ -479,8 +484,12 @@ void prefill_mfma_kernel(AttnParams p) {
     }
 
     // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
+    // The output divides by the sum of the same rounded weights that multiplied V
+    // (a row dominated by one weight then keeps that weight's rounding out of
+    // its output); lse takes the sum of the fp32 weights.
     const float l_tot = pair32_sum(l_run);
-    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
+    const float lr_tot = pair32_sum(lr_run);
+    const float inv = (lr_tot == 0.f) ? 0.f : 1.f / lr_tot;
     const int o_rs = (int)(p.o_sr * 2);
     const auto ors = make_rsrc((uint16_t*)p.o + oo + (int64_t)q0 * p.o_sr, (qrows - 1) * o_rs + v_bytes);
 #pragma unroll
@@ -491,7 +500,7 @@ void prefill_mfma_kernel(AttnParams p) {
             uint2 st;
             st.x = Tr::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
             st.y = Tr::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-            if (!PADE || d < p.e) buf_store8(st, ors, lrow * o_rs + d * 2);
+            if (!PADE || d < p.dv) buf_store8(st, ors, lrow * o_rs + d * 2);
         }
     if (hh == 0) {
         const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
@@ -592,30 +601,55 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
     return hipErrorInvalidValue;
 }
 
-// Other head dims E (a multiple of 8 up to 128, E == Ev; unmasked batched calls):
-// the four-wave kernel for the next multiple of 32, reading and writing E columns.
-template <typename Tr, int DP>
-hipError_t launch_prefill_pad(const AttnParams& p, bool causal, hipStream_t s) {
-    return causal ? launch_prefill_one<Tr, DP, DP, true, MASK_NONE, false, false, true>(p, s)
-                  : launch_prefill_one<Tr, DP, DP, false, MASK_NONE, false, false, true>(p, s);
+// Other head dims (E and Ev multiples of 8 up to 128, E = 0 included, and Ev != E
+// on a paged cache): the four-wave kernel at width W, the next multiple of 32
+// of the larger one, reading E columns of Q and K and Ev of V (the rest load as
+// 0, so the dot products only gain exact zeros) and writing Ev columns; every
+// mask kind, packed batches and paged caches.
+template <typename Tr, int W, bool CAUSAL>
+hipError_t launch_prefill_pad_c(const AttnParams& p, int mask, bool varlen, hipStream_t s) {
+    if (p.block_table) {
+        if (mask != MASK_NONE) return hipErrorInvalidValue;
+        return varlen ? launch_prefill_one<Tr, W, W, CAUSAL, MASK_NONE, true, true, true>(p, s)
+                      : launch_prefill_one<Tr, W, W, CAUSAL, MASK_NONE, false, true, true>(p, s);
+    }
+    if (varlen)
+        return mask == MASK_NONE ? launch_prefill_one<Tr, W, W, CAUSAL, MASK_NONE, true, false, true>(p, s)
+                                 : hipErrorInvalidValue;
+    switch (mask) {
+        case MASK_NONE: return launch_prefill_one<Tr, W, W, CAUSAL, MASK_NONE, false, false, true>(p, s);
+        case MASK_FLOAT: return launch_prefill_one<Tr, W, W, CAUSAL, MASK_FLOAT, false, false, true>(p, s);
+        case MASK_BOOL: return launch_prefill_one<Tr, W, W, CAUSAL, MASK_BOOL, false, false, true>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename Tr, int W>
+hipError_t launch_prefill_pad(const AttnParams& p, bool causal, int mask, bool varlen, hipStream_t s) {
+    return causal ? launch_prefill_pad_c<Tr, W, true>(p, mask, varlen, s)
+                  : launch_prefill_pad_c<Tr, W, false>(p, mask, varlen, s);
 }
 
 template <typename Tr>
 hipError_t launch_prefill_t(const AttnParams& p, int D, bool causal, int mask, bool varlen,
                             hipStream_t s) {
-    switch (D) {
-        case 64: return launch_prefill_d<Tr, 64>(p, causal, mask, varlen, s);
-        case 96: return launch_prefill_d<Tr, 96>(p, causal, mask, varlen, s);
-        case 128: return launch_prefill_d<Tr, 128>(p, causal, mask, varlen, s);
+    (void)D;
+    const auto exact = [](int e) { return e == 64 || e == 96 || e == 128; };
+    // exact instances; a paged cache with Ev != E takes the padded instance
+    if (exact(p.e) && exact(p.dv) && !(p.block_table && p.e != p.dv)) {
+        switch (p.e) {
+            case 64: return launch_prefill_d<Tr, 64>(p, causal, mask, varlen, s);
+            case 96: return launch_prefill_d<Tr, 96>(p, causal, mask, varlen, s);
+            case 128: return launch_prefill_d<Tr, 128>(p, causal, mask, varlen, s);
+        }
     }
-    if (D < 8 || D > 128 || D % 8 != 0 || p.e != D || p.dv != D || mask != MASK_NONE || varlen ||
-        p.block_table)
+    if (p.e < 0 || p.e > 128 || p.e % 8 != 0 || p.dv < 0 || p.dv > 128 || p.dv % 8 != 0)
         return hipErrorInvalidValue;
-    switch ((D + 31) / 32) {
-        case 1: return launch_prefill_pad<Tr, 32>(p, causal, s);
-        case 2: return launch_prefill_pad<Tr, 64>(p, causal, s);
-        case 3: return launch_prefill_pad<Tr, 96>(p, causal, s);
-        case 4: return launch_prefill_pad<Tr, 128>(p, causal, s);
+    switch ((max(max(p.e, p.dv), 1) + 31) / 32) {
+        case 1: return launch_prefill_pad<Tr, 32>(p, causal, mask, varlen, s);
+        case 2: return launch_prefill_pad<Tr, 64>(p, causal, mask, varlen, s);
+        case 3: return launch_prefill_pad<Tr, 96>(p, causal, mask, varlen, s);
+        case 4: return launch_prefill_pad<Tr, 128>(p, causal, mask, varlen, s);
     }
     return hipErrorInvalidValue;
 }

@@ -460,7 +460,8 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     uint4 qreg[NKK];  // Q^T operand of the current tile
     f32x16_t acc[NDB];
     float sh_run;     // running shift, log2 units (-inf until a kept key)
-    float l_run;      // this lane's share of the row sum relative to it
+    float l_run;      // this lane's share of the row sum relative to it (fp32 weights, for lse)
+    float lr_run;     // the same over the weights rounded to 16 bits (normalises the output)
     const float cfac = FMASK ? kLog2e : p.scale_log2;  // log2-domain factor of a score (or logit)
     f32x16_t sA[2], sB[2];   // scores of block t and t + 1, roles swapping each iteration
     // current item
@@ -624,24 +625,31 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // masks: the bias (or bool mask) of block t + 1 applied to its scores
         // between the last NBRD products (the wait for its load at the first)
         {
-            float p8[8];
+            float p8[8], r4[4];
             MaskRead bq;
             static_for<NOP>([&](auto jt) {
                 constexpr int j = decltype(jt)::value;
                 issue(std::integral_constant<int, NOP + j + LA>{});
                 fence();
                 acc[j % NDB] = Tr::mfma32(as_vec8<Tr>(opq[NOP + j]), as_vec8<Tr>(pb[j / NDB]), acc[j % NDB]);
-                // row-sum items [9 j / NOP, 9 (j + 1) / NOP): 8 partial sums and the update
-                static_for<(9 * (j + 1)) / NOP - (9 * j) / NOP>([&](auto it) {
-                    constexpr int w = (9 * j) / NOP + decltype(it)::value;
+                // row-sum items [13 j / NOP, 13 (j + 1) / NOP): 8 partial sums of the fp32
+                // weights, 4 of the rounded ones (the P^T operand chunks), and the updates
+                static_for<(13 * (j + 1)) / NOP - (13 * j) / NOP>([&](auto it) {
+                    constexpr int w = (13 * j) / NOP + decltype(it)::value;
                     if constexpr (w < 8) {
                         p8[w] = (s_cur[w >> 2][(w & 3) * 4 + 0] + s_cur[w >> 2][(w & 3) * 4 + 1]) +
                                 (s_cur[w >> 2][(w & 3) * 4 + 2] + s_cur[w >> 2][(w & 3) * 4 + 3]);
                         pp_pin(p8[w]);
+                    } else if constexpr (w < 12) {
+                        const uint4 u = pb[w - 8];
+                        r4[w - 8] = Tr::sum2(u.w, Tr::sum2(u.z, Tr::sum2(u.y, Tr::sum2(u.x, 0.f))));
+                        pp_pin(r4[w - 8]);
                     } else {
                         const float tsum = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
                         l_run = fmaf(l_run, alpha, tsum);
+                        lr_run = fmaf(lr_run, alpha, (r4[0] + r4[1]) + (r4[2] + r4[3]));
                         pp_pin(l_run);
+                        pp_pin(lr_run);
                     }
                 });
                 if constexpr (ANYMASK) {
@@ -722,6 +730,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
         sh_run = kNegInf;
         l_run = 0.f;
+        lr_run = 0.f;
         if (!ANYMASK && has_next) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): Q area reads done
             load_q(nP, ns);
@@ -798,9 +807,13 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // Blocks past this wave's rows: loads and barriers only.
         for (int t = last_tile + 1; t < nsteps; ++t) step_end(t, false);
 
-        // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even.
+        // Epilogue: O = O^T / l per lane (this lane's query), rounded to nearest-even,
+        // with l the sum of the same rounded weights that multiplied V (a row dominated
+        // by one weight then keeps that weight's rounding out of its output); lse takes
+        // the sum of the fp32 weights.
         const float l_tot = pair32_sum(l_run);
-        const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
+        const float lr_tot = pair32_sum(lr_run);
+        const float inv = (lr_tot == 0.f) ? 0.f : 1.f / lr_tot;
         const int o_rs = (int)(p.o_sr * 2);
         int lrow = wrow0 + lq;
         asm volatile("" : "+v"(lrow));  // per-lane store offsets computed here, not kept across the loop

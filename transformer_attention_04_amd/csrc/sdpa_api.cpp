@@ -49,6 +49,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // unit last stride, 16-byte aligned base, and every outer stride (of a dim
 // with more than one element) a multiple of 16 bytes.
 sdpa_status check_vector_layout(const sdpa_tensor4& t, int ebytes, const char* name) {
+    if (t.size[3] == 0) return SDPA_OK;  // zero-width rows: nothing is read or written
     const int64_t vec = 16 / ebytes;
     if (t.size[3] > 1 && t.stride[3] != 1)
         return fail(SDPA_ERR_UNSUPPORTED, "%s: the last dimension must have stride 1", name);
@@ -62,8 +63,17 @@ sdpa_status check_vector_layout(const sdpa_tensor4& t, int ebytes, const char* n
 }
 
 bool supported_head_dim(int64_t e) { return e == 64 || e == 96 || e == 128; }
-// Other head dims the single-pass 16-bit kernel takes unmasked, zero-padded in registers.
-bool padded_head_dim(int64_t e) { return e >= 8 && e <= 128 && e % 8 == 0; }
+// Head dims the forward kernels take: E and Ev multiples of 8 up to 128 (E = 0
+// included: the scores are empty sums).  E and Ev in {64, 96, 128} run exact
+// instances, the others padded ones (zeros past E and Ev).
+bool forward_dims(int64_t e, int64_t ev) {
+    return e >= 0 && e <= 128 && e % 8 == 0 && ev >= 0 && ev <= 128 && ev % 8 == 0;
+}
+// The matrix-core backward takes bf16/fp16 with E == Ev in {64, 96, 128}; the
+// vector-ALU backward every other supported call (fp32, Ev != E, other dims).
+bool matrix_core_backward(sdpa_dtype dtype, int64_t e, int64_t ev) {
+    return dtype != SDPA_F32 && e == ev && supported_head_dim(e);
+}
 
 struct Plan {
     bool decode = false;
@@ -168,6 +178,10 @@ sdpa_status check_shapes(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_ten
 }
 
 sdpa_status resolve_scale(const double* scale, int64_t E, double* out) {
+    if (E == 0) {  // the scores are empty sums (0) and the logits the mask alone: no scale applies
+        *out = 1.0;
+        return SDPA_OK;
+    }
     const double s = scale ? *scale : 1.0 / std::sqrt((double)E);
     if (!std::isfinite(s)) return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be finite");
     *out = s;
@@ -230,10 +244,17 @@ sdpa_status paged_plan(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tenso
                     (long long)pp.page_size);
     pp.page_shift = shift;
     const int64_t group = pp.Hkv > 0 ? pp.Hq / pp.Hkv : 1;
-    if (pp.E != pp.Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev");
-    if (!supported_head_dim(pp.E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim must be 64, 96 or 128");
+    if (!forward_dims(pp.E, pp.Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be a multiple of 8 up to 128",
+                    (long long)pp.E, (long long)pp.Ev);
     if (num_splits < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "num_splits must be 0 or positive");
-    if (pp.L * group > sdpa::kDecodeMaxRows) {
+    // the split-KV decode kernel takes head dims in {64, 96, 128}; other dims always
+    // run the single-pass kernel, decode steps included
+    const bool exact = supported_head_dim(pp.E) && supported_head_dim(pp.Ev);
+    if (!exact && num_splits > 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "split-KV needs head dims in {64, 96, 128} (got E=%lld, Ev=%lld)",
+                    (long long)pp.E, (long long)pp.Ev);
+    if (pp.L * group > sdpa::kDecodeMaxRows || !exact) {
         // chunked prefill: the single-pass kernel reads the pages itself, no workspace
         if (num_splits > 0)
             return fail(SDPA_ERR_UNSUPPORTED,
@@ -320,15 +341,9 @@ sdpa_status sdpa_fwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
     if (s.B * s.Hq * s.L == 0) return ok();  // nothing to compute
-    if (!(supported_head_dim(s.E) && supported_head_dim(s.Ev)) &&
-        !(padded_head_dim(s.E) && s.E == s.Ev && dtype != SDPA_F32 && !attn_mask))
-        return fail(SDPA_ERR_UNSUPPORTED,
-                    "head dims E=%lld, Ev=%lld: each must be one of 64, 96, 128, or E == Ev a multiple "
-                    "of 8 up to 128 for bf16/fp16 without a mask",
+    if (!forward_dims(s.E, s.Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be a multiple of 8 up to 128",
                     (long long)s.E, (long long)s.Ev);
-    if (s.E != s.Ev && dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "E != Ev (%lld and %lld) needs bf16/fp16 inputs", (long long)s.E,
-                    (long long)s.Ev);
     const int eb = elem_bytes(dtype);
     if ((st = check_vector_layout(*q, eb, "q")) != SDPA_OK) return st;
     if (s.S > 0) {
@@ -448,21 +463,21 @@ sdpa_status sdpa_fwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     if (n_seqs == 0 || max_seqlen_q == 0 || Hq == 0 || total_q == 0) return ok();
     if (!cu_seqlens_q || !cu_seqlens_k)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must not be NULL");
-    if (!supported_head_dim(E) || !supported_head_dim(Ev))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%d, Ev=%d: each must be one of 64, 96, 128", E, Ev);
-    if (E != Ev && dtype == SDPA_F32)
-        return fail(SDPA_ERR_UNSUPPORTED, "E != Ev (%d and %d) needs bf16/fp16 inputs", E, Ev);
-    if (!q || !out || !lse || (total_k > 0 && (!k || !v)))
+    if (!forward_dims(E, Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%d, Ev=%d: each must be a multiple of 8 up to 128", E, Ev);
+    // (zero-width rows are never touched, so their tensors may be empty and NULL)
+    if ((E > 0 && !q) || (Ev > 0 && !out) || !lse || (total_k > 0 && ((E > 0 && !k) || (Ev > 0 && !v))))
         return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
     const int64_t vec = 16 / elem_bytes(dtype);
     const void* ptrs[4] = {q, k, v, out};
     const int64_t strides[8] = {q_stride_tok, q_stride_head, k_stride_tok, k_stride_head,
                                 v_stride_tok, v_stride_head, o_stride_tok, o_stride_head};
+    const bool used[4] = {E > 0, E > 0, Ev > 0, Ev > 0};  // zero-width rows are never read or written
     for (int i = 0; i < 4; ++i)
-        if (ptrs[i] && !aligned16(ptrs[i]))
+        if (used[i] && ptrs[i] && !aligned16(ptrs[i]))
             return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
     for (int i = 0; i < 8; ++i)
-        if (strides[i] % vec != 0)
+        if (used[i / 2] && strides[i] % vec != 0)
             return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
     double sc;
     sdpa_status st;
@@ -629,22 +644,24 @@ sdpa_status sdpa_fwd_paged_varlen(sdpa_dtype dtype, const void* q, int64_t q_str
     while (shift < 30 && ((int64_t)1 << shift) < ps) ++shift;
     if (ps < 16 || ((int64_t)1 << shift) != ps)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size must be a power of two >= 16 (got %lld)", (long long)ps);
-    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev");
-    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim must be 64, 96 or 128");
+    if (!forward_dims(E, Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be a multiple of 8 up to 128",
+                    (long long)E, (long long)Ev);
     if (bt_stride < max_blocks) return fail(SDPA_ERR_INVALID_ARGUMENT, "need 0 <= max_blocks <= bt_stride");
     if ((int64_t)max_blocks * ps > INT32_MAX || n_pages > INT32_MAX)
         return fail(SDPA_ERR_UNSUPPORTED, "cache too large for 32-bit key indices");
     if (n_seqs == 0 || total_q == 0 || Hq == 0 || max_seqlen_q == 0) return ok();
     if (!cu_seqlens_q || !block_table || !seq_lens)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q, block_table and seq_lens must not be NULL");
-    if (!q || !out || !lse) return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
+    if ((E > 0 && !q) || (Ev > 0 && !out) || !lse)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
     const int eb = elem_bytes(dtype);
     const int64_t vec = 16 / eb;
-    if (!aligned16(q) || !aligned16(out))
+    if ((E > 0 && !aligned16(q)) || (Ev > 0 && !aligned16(out)))
         return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
     const int64_t strides[4] = {q_stride_tok, q_stride_head, o_stride_tok, o_stride_head};
     for (int i = 0; i < 4; ++i)
-        if (strides[i] % vec != 0)
+        if ((i < 2 ? E : Ev) > 0 && strides[i] % vec != 0)
             return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
     sdpa_status st;
     if (n_pages > 0) {
@@ -695,7 +712,6 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     if (st != SDPA_OK) return st;
     if (attn_mask && mask_dtype != SDPA_F32 && mask_dtype != SDPA_BOOL)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "attn_mask must be SDPA_F32 (added) or SDPA_BOOL (keep)");
-    if (dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "the backward kernels take bf16 or fp16");
     if (!out || !lse || !dout || !dq || !dk || !dv)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv descriptors must not be NULL");
     const int64_t want_o[4] = {s.B, s.Hq, s.L, s.Ev};
@@ -712,11 +728,9 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     }
     if (lse->size[3] != 1) return fail(SDPA_ERR_INVALID_ARGUMENT, "lse must be (B, Hq, L, 1)");
     if (s.B * s.Hq * s.L == 0 && s.B * s.Hkv * s.S == 0) return ok();  // nothing to compute
-    if (s.E != s.Ev)
-        return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %lld and %lld)", (long long)s.E,
-                    (long long)s.Ev);
-    if (!supported_head_dim(s.E))
-        return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not one of 64, 96, 128", (long long)s.E);
+    if (!forward_dims(s.E, s.Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%lld, Ev=%lld: each must be a multiple of 8 up to 128",
+                    (long long)s.E, (long long)s.Ev);
     const int eb = elem_bytes(dtype);
     const sdpa_tensor4* vec_t[8] = {q, k, v, out, dout, dq, dk, dv};
     const char* vec_n[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
@@ -758,8 +772,9 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     p.L = (int)s.L; p.S = (int)s.S;
     p.n_qtiles = (int)((s.L + 127) / 128);
     p.n_ktiles = (int)((s.S + 127) / 128);
-    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16;
+    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : dtype == SDPA_F16 ? sdpa::ELEM_F16 : sdpa::ELEM_F32;
     p.scale = (float)sc;
+    p.e = (int)s.E; p.ev = (int)s.Ev;
     int mask_kind = sdpa::MASK_NONE;
     if (attn_mask) {
         mask_kind = mask_dtype == SDPA_F32 ? sdpa::MASK_FLOAT : sdpa::MASK_BOOL;
@@ -772,7 +787,9 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
         p.mask_vec = ((uintptr_t)attn_mask->data % mal == 0) && p.m_sb % mvec == 0 && p.m_sh % mvec == 0 &&
                      p.m_sr % mvec == 0 && s.S % mvec == 0;
     }
-    hipError_t e = sdpa::launch_backward(p, (int)s.E, is_causal != 0, mask_kind, false, (hipStream_t)stream);
+    hipError_t e = matrix_core_backward(dtype, s.E, s.Ev)
+                       ? sdpa::launch_backward(p, (int)s.E, is_causal != 0, mask_kind, false, (hipStream_t)stream)
+                       : sdpa::launch_backward_vec(p, is_causal != 0, mask_kind, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -796,9 +813,8 @@ sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
                             void* dk, int64_t dk_stride_tok, int64_t dk_stride_head, void* dv,
                             int64_t dv_stride_tok, int64_t dv_stride_head, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    if (dtype != SDPA_F16 && dtype != SDPA_BF16)
-        return fail(dtype == SDPA_F32 ? SDPA_ERR_UNSUPPORTED : SDPA_ERR_INVALID_ARGUMENT,
-                    "the backward kernels take bf16 or fp16");
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16 && dtype != SDPA_F32)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16");
     if (n_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq < 0 || Hkv < 0 || E < 0 || Ev < 0 ||
         total_q < 0 || total_k < 0)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "sizes must be non-negative");
@@ -813,11 +829,13 @@ sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     if (n_seqs == 0 || Hq == 0 || (total_q == 0 && total_k == 0)) return ok();
     if (!cu_seqlens_q || !cu_seqlens_k)
         return fail(SDPA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must not be NULL");
-    if (E != Ev) return fail(SDPA_ERR_UNSUPPORTED, "the kernels need E == Ev (got %d and %d)", E, Ev);
-    if (!supported_head_dim(E)) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d is not one of 64, 96, 128", E);
+    if (!forward_dims(E, Ev))
+        return fail(SDPA_ERR_UNSUPPORTED, "head dims E=%d, Ev=%d: each must be a multiple of 8 up to 128", E, Ev);
     const void* ptrs[8] = {q, k, v, out, dout, dq, dk, dv};
     for (int i = 0; i < 8; ++i) {
-        const bool need = (i == 1 || i == 2 || i == 6 || i == 7) ? total_k > 0 : total_q > 0;
+        // zero-width rows (E = 0: q, k, dq, dk; Ev = 0: v, out, dout, dv) are never touched
+        const bool width = (i == 0 || i == 1 || i == 5 || i == 6) ? E > 0 : Ev > 0;
+        const bool need = width && ((i == 1 || i == 2 || i == 6 || i == 7) ? total_k > 0 : total_q > 0);
         if (need && !ptrs[i]) return fail(SDPA_ERR_INVALID_ARGUMENT, "data pointers must not be NULL");
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(SDPA_ERR_UNSUPPORTED, "packed tensors need 16-byte aligned base pointers");
@@ -828,8 +846,9 @@ sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
                                  v_stride_head, o_stride_tok, o_stride_head, do_stride_tok, do_stride_head,
                                  dq_stride_tok, dq_stride_head, dk_stride_tok, dk_stride_head, dv_stride_tok,
                                  dv_stride_head};
+    const bool swidth[8] = {E > 0, E > 0, Ev > 0, Ev > 0, Ev > 0, E > 0, E > 0, Ev > 0};
     for (int i = 0; i < 16; ++i)
-        if (strides[i] % vec != 0)
+        if (swidth[i / 2] && strides[i] % vec != 0)
             return fail(SDPA_ERR_UNSUPPORTED, "packed strides must be multiples of %lld elements", (long long)vec);
     double sc;
     sdpa_status st;
@@ -857,9 +876,12 @@ sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
     p.L = max_seqlen_q; p.S = max_seqlen_k;
     p.n_qtiles = (max_seqlen_q + 127) / 128;
     p.n_ktiles = (max_seqlen_k + 127) / 128;
-    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : sdpa::ELEM_F16;
+    p.elem = dtype == SDPA_BF16 ? sdpa::ELEM_BF16 : dtype == SDPA_F16 ? sdpa::ELEM_F16 : sdpa::ELEM_F32;
     p.scale = (float)sc;
-    hipError_t e = sdpa::launch_backward(p, E, is_causal != 0, sdpa::MASK_NONE, true, (hipStream_t)stream);
+    p.e = E; p.ev = Ev;
+    hipError_t e = matrix_core_backward(dtype, E, Ev)
+                       ? sdpa::launch_backward(p, E, is_causal != 0, sdpa::MASK_NONE, true, (hipStream_t)stream)
+                       : sdpa::launch_backward_vec(p, is_causal != 0, sdpa::MASK_NONE, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SDPA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -348,9 +348,8 @@ def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False,
     """
     lib = load_library()
     _require_gpu(query, key, value, out, lse, grad, attn_mask)
-    if query.dtype not in (torch.float16, torch.bfloat16) or any(
-            t.dtype != query.dtype for t in (key, value, out, grad)):
-        raise ValueError("the backward takes float16 or bfloat16 query, key, value, out and grad")
+    if query.dtype not in _DTYPE or any(t.dtype != query.dtype for t in (key, value, out, grad)):
+        raise ValueError("query, key, value, out and grad must share one of float32, float16, bfloat16")
     q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
     if k4.shape[0] != q4.shape[0] or v4.shape[0] != q4.shape[0]:
         raise ValueError("query, key and value must share the batch dimensions")
@@ -387,8 +386,8 @@ def sdpa_bwd_varlen(q, k, v, out, lse, grad, cu_seqlens_q, cu_seqlens_k=None, ma
     """
     lib = load_library()
     _require_gpu(q, k, v, out, lse, grad, cu_seqlens_q, cu_seqlens_k)
-    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in (k, v, out, grad)):
-        raise ValueError("the backward takes float16 or bfloat16 q, k, v, out and grad")
+    if q.dtype not in _DTYPE or any(t.dtype != q.dtype for t in (k, v, out, grad)):
+        raise ValueError("q, k, v, out and grad must share one of float32, float16, bfloat16")
     batched = q.dim() == 4
     q3, k3, v3, o3, g3 = (t[0] if t.dim() == 4 else t for t in (q, k, v, out, grad))
     l2 = lse[0] if lse.dim() == 3 else lse
@@ -469,13 +468,15 @@ def sdpa_fwd_bmhk(query, key, value, is_causal=False, scale=None, num_splits=0):
 
 
 def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                    dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False):
+                    dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False, out=None, lse=None):
     """Packed variable-length attention with a block-diagonal (optionally causal) mask.
 
     q (total_q, Hq, E) or (1, total_q, Hq, E) -- the BMHK layout of the
     insureai360 xFormers tutorial, section 4; k, v likewise; cu_seqlens are
     int32 device tensors of n_seqs + 1 offsets.  Returns out shaped like q
     (with Ev) and lse (Hq, total_q) (or (1, Hq, total_q) for 4-D input).
+    ``out`` (total_q, Hq, Ev) and ``lse`` (Hq, total_q) may be passed in
+    (written in place; the returned tensors are views of them).
     """
     lib = load_library()
     _require_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
@@ -503,8 +504,19 @@ def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k=None, max_seqlen_q=None,
         if t.shape[-1] > 1 and t.stride(-1) != 1:
             raise ValueError("the last dimension must have stride 1")
     dev = q.device
-    out3 = torch.empty((total_q, Hq, Ev), dtype=q.dtype, device=dev)
-    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if out is None:
+        out3 = torch.empty((total_q, Hq, Ev), dtype=q.dtype, device=dev)
+    else:
+        out3 = out[0] if out.dim() == 4 else out
+        if tuple(out3.shape) != (total_q, Hq, Ev) or out3.dtype != q.dtype or out3.stride(-1) != 1:
+            raise ValueError(f"out must be ({total_q}, {Hq}, {Ev}) {q.dtype} with unit last stride")
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    else:
+        lse = lse[0] if lse.dim() == 3 else lse
+        if tuple(lse.shape) != (Hq, total_q) or lse.dtype != torch.float32 or lse.stride(1) != 1:
+            raise ValueError(f"lse must be ({Hq}, {total_q}) float32 with unit last stride")
+    _require_gpu(out3, lse)
     with torch.cuda.device(dev):
         _check(lib.sdpa_fwd_varlen(
             _DTYPE[q.dtype], q3.data_ptr(), q3.stride(0), q3.stride(1),
