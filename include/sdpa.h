@@ -16,9 +16,10 @@
  * head h / (Hq / Hkv).  A row with no kept key has output 0 and lse -inf.  The
  * output has the inputs' dtype, rounded to nearest-even; lse is float32.
  *
- * Entry points: sdpa_fwd (+ _workspace_size), sdpa_fwd_varlen, sdpa_fwd_paged
- * (+ _workspace_size), sdpa_fwd_paged_varlen, sdpa_bwd (+ _workspace_size), sdpa_bwd_varlen
- * (+ _workspace_size), sdpa_last_error, sdpa_abi_version.
+ * Entry points: sdpa_fwd (+ _workspace_size), sdpa_fwd_noalloc, sdpa_fwd_varlen,
+ * sdpa_fwd_paged (+ _workspace_size), sdpa_fwd_paged_varlen, sdpa_bwd
+ * (+ _workspace_size), sdpa_bwd_varlen (+ _workspace_size), sdpa_last_error,
+ * sdpa_abi_version.
  *
  * Conventions for every entry point
  *  - All data pointers are DEVICE pointers (HIP global memory) owned by the
@@ -127,6 +128,35 @@ sdpa_status sdpa_fwd_workspace_size(sdpa_dtype dtype,
                                     const sdpa_tensor4* v,
                                     const sdpa_tensor4* attn_mask, int is_causal,
                                     int enable_gqa, int num_splits, size_t* bytes);
+
+/*
+ * sdpa_fwd_noalloc -- sdpa_fwd for callers that cannot allocate device memory
+ * while they run (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as sdpa_fwd without the
+ * workspace: the scratch memory the split-KV decode needs (its per-split
+ * partial outputs and logsumexps) comes from a device array inside the
+ * library, SDPA_NOALLOC_SCRATCH_BYTES on each device, which the library holds
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *
+ *   - A call whose sdpa_fwd_workspace_size exceeds SDPA_NOALLOC_SCRATCH_BYTES
+ *     returns SDPA_ERR_UNSUPPORTED before anything is launched (fewer
+ *     num_splits, or sdpa_fwd with a workspace, lift it); for the decode
+ *     workload B=64, Hq=32, Hkv=8, S=32768, E=128 the automatic split count
+ *     needs about 4.2 MB.
+ *   - The array of the device current at the call is used (looked up on the
+ *     first call on that device); stream must belong to that device.
+ *   - Calls on one device share its array: calls that overlap on one device
+ *     (other streams, other threads) race and must be serialised by the
+ *     caller.  Each call writes every partial it reads, so nothing carries
+ *     over from one call to the next.
+ */
+#define SDPA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+sdpa_status sdpa_fwd_noalloc(sdpa_dtype dtype,
+                             const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                             const sdpa_tensor4* attn_mask, sdpa_dtype mask_dtype,
+                             double dropout_p, int is_causal, const double* scale, int enable_gqa,
+                             const sdpa_tensor4* out, const sdpa_tensor4* lse, int num_splits,
+                             void* stream);
 
 /*
  * sdpa_fwd_varlen -- packed variable-length attention with a block-diagonal
@@ -353,7 +383,9 @@ sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype,
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);
 
-/* Interface version, bumped when a signature or a meaning above changes. */
+/* Interface version, bumped when a signature or a meaning above changes (5:
+ * sdpa_fwd_noalloc; head dims 0..128 in steps of 8 and Ev != E on every path;
+ * fp32 gradients). */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "api_internal.h"
 #include "attn_common.h"
 
 namespace {
@@ -297,9 +298,19 @@ sdpa_status paged_plan(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tenso
 
 }  // namespace
 
+namespace sdpa {
+sdpa_status record_error(sdpa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+}  // namespace sdpa
+
 extern "C" {
 
-int sdpa_abi_version(void) { return 4; }
+int sdpa_abi_version(void) { return 5; }
 
 const char* sdpa_last_error(void) { return g_err; }
 

@@ -20,7 +20,7 @@ SDPA_OK, SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED, SDPA_ERR_DEVICE = 0, 1
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_BOOL = 0, 1, 2, 3
 _DTYPE = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
 
-EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_varlen", "sdpa_fwd_paged",
+EXPORTED = ("sdpa_fwd", "sdpa_fwd_workspace_size", "sdpa_fwd_noalloc", "sdpa_fwd_varlen", "sdpa_fwd_paged",
             "sdpa_fwd_paged_workspace_size", "sdpa_fwd_paged_varlen", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_bwd_varlen",
             "sdpa_bwd_varlen_workspace_size", "sdpa_last_error",
             "sdpa_abi_version")
@@ -62,6 +62,9 @@ def load_library():
                              ctypes.POINTER(dbl), ctypes.c_int, P, P, vp, ctypes.c_size_t,
                              ctypes.c_int, vp]
     lib.sdpa_fwd.restype = ctypes.c_int
+    lib.sdpa_fwd_noalloc.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, dbl, ctypes.c_int,
+                                     ctypes.POINTER(dbl), ctypes.c_int, P, P, ctypes.c_int, vp]
+    lib.sdpa_fwd_noalloc.restype = ctypes.c_int
     lib.sdpa_fwd_workspace_size.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.sdpa_fwd_workspace_size.restype = ctypes.c_int
@@ -232,6 +235,36 @@ def sdpa_fwd(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, 
                             int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), do, dl,
                             ws_ptr, nbytes.value, int(num_splits), _stream(dev)))
     return o4.reshape(*query.shape[:-1], Ev), l4.reshape(*query.shape[:-1])
+
+
+def sdpa_fwd_noalloc(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+                     enable_gqa=False, num_splits=0, out=None, lse=None):
+    """sdpa_fwd through the allocation-free C entry point: the split-KV scratch is
+    the library's own device array (no workspace).  ``out`` and ``lse`` are
+    allocated here only when not given; the C call allocates nothing."""
+    lib = load_library()
+    _require_gpu(query, key, value, attn_mask, out, lse)
+    if query.dtype not in _DTYPE or key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("query, key and value must share one of float32, float16, bfloat16")
+    q4, k4, v4 = _as4d(query), _as4d(key), _as4d(value)
+    k4, v4 = _expand_batch(q4, k4), _expand_batch(q4, v4)
+    B, Hq, L, _ = q4.shape
+    S, Ev = v4.shape[2], v4.shape[3]
+    m4, mdt = _mask_4d(attn_mask, q4, S)
+    dev = query.device
+    if out is None:
+        out = torch.empty((B, Hq, L, Ev), dtype=query.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, L, 1), dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (B, Hq, L, Ev) or tuple(lse.shape) != (B, Hq, L, 1):
+        raise ValueError("out must be (B, Hq, L, Ev) and lse (B, Hq, L, 1)")
+    dm = _desc(m4) if m4 is not None else None
+    with torch.cuda.device(dev):
+        _check(lib.sdpa_fwd_noalloc(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4),
+                                    ctypes.byref(dm) if dm is not None else None, mdt, float(dropout_p),
+                                    int(bool(is_causal)), _scale_arg(scale), int(bool(enable_gqa)), _desc(out),
+                                    _desc(lse), int(num_splits), _stream(dev)))
+    return out.reshape(*query.shape[:-1], Ev), lse.reshape(*query.shape[:-1])
 
 
 def sdpa_fwd_paged(query, k_cache, v_cache, block_table, seq_lens, max_seq_len=None, is_causal=False,
