@@ -71,6 +71,40 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(BUILD, "asan", "libsdpa_asan.so")
+
+
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime (to preload into a
+    process that loads the sanitized library)."""
+    out = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                         stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    if not out or not os.path.exists(out):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc's clang was not found")
+    return out
+
+
+def build_host_asan(jobs: int | None = None) -> str:
+    """libsdpa with its C interface (sdpa_api.cpp: argument checks, plans, launch
+    choice) built with AddressSanitizer and UndefinedBehaviorSanitizer, linked with
+    the kernel objects of the regular build (built first if missing)."""
+    hipcc = _hipcc()
+    out_dir = os.path.dirname(ASAN_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    kernel_objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "sdpa_api.cpp"]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(jobs)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libasan"]
+    api_obj = os.path.join(out_dir, "sdpa_api.o")
+    _run([hipcc, *san, "-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-I",
+          os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, "sdpa_api.cpp"), "-o", api_obj])
+    tmp = ASAN_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, "-o", tmp, api_obj, *kernel_objs])
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("-j", "--jobs", type=int, default=None)
