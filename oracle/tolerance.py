@@ -63,6 +63,21 @@ split-KV decoding does).
 
 Rows the page calls special (a NaN or +inf logit, no kept key) and elements
 whose exact value is not finite must be matched exactly.
+
+The backward (``analyse_backward``; the page's "scaled_dot_product_attention.
+backward" section, its tolerance() paragraph) takes the same readings through
+the gradient program the page lists: the forward's scores, scale factor,
+logits, shift, exp within ``ulps`` and row sum; the weights P = w / row sum,
+one rounding each; dP = grad V^T and D_i = sum_j P_ij dP_ij accumulated; dP - D
+rounded; dS = P (dP - D) rounded; grad_value = P^T grad, dS K and dS^T Q
+accumulated (each over the copies grouped heads or broadcasting made of its
+input as well: one longer sum); the scale product rounded; the rounding to the
+output format.  Its named algorithm (``BlockedBackward``) adds what the page
+says such algorithms budget: P formed without a division by the row sum, as
+exp(l - lse) from the forward's logsumexp (any value the forward's own model
+allows), D from the forward's output (D_i = grad_i . O_i, O any output the
+forward's model allows), P and dS rounded to the input format before their
+products, and the base-2 exponent's extra roundings.
 """
 from __future__ import annotations
 
@@ -74,7 +89,8 @@ import numpy as np
 
 from .sdpa_oracle import _expand_kv, _f64, _row_classes, logits, resolve_scale, sdpa
 
-__all__ = ["Blocked", "Analysis", "analyse", "tolerance", "finite_range", "covers"]
+__all__ = ["Blocked", "Analysis", "analyse", "tolerance", "finite_range", "covers",
+           "BlockedBackward", "BackwardAnalysis", "analyse_backward"]
 
 # Formats: (significant bits p, minimum normal exponent, largest finite value)
 FORMATS = {
@@ -126,7 +142,20 @@ def _ulp(x, fmt):
 
 
 def _rd(x, fmt):
-    """Largest grid value <= x (-inf below the finite range, the largest finite value above it)."""
+    """Largest grid value <= x (-inf below the finite range, the largest finite value above it).
+    float32 through numpy's own float32 conversion (nearest, then one step down where that
+    lies above x); other formats by scaling to the grid spacing (``_rd_grid``)."""
+    x = np.asarray(x, dtype=np.float64)
+    if fmt != "fp32":
+        return _rd_grid(x, fmt)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = x.astype(np.float32)
+        y = np.where(y.astype(np.float64) > x, np.nextafter(y, np.float32(-np.inf)), y)
+    return y.astype(np.float64)
+
+
+def _rd_grid(x, fmt):
+    """``_rd`` for any format of FORMATS, from the grid spacing."""
     x = np.asarray(x, dtype=np.float64)
     _, _, fmax = FORMATS[fmt]
     pos = np.where(x >= 0, x, 0.0)
@@ -149,7 +178,16 @@ def _ru(x, fmt):
 def _rn(x, fmt):
     """Nearest grid value, ties to even; IEEE overflow past the largest value plus half an ulp."""
     x = np.asarray(x, dtype=np.float64)
-    lo, hi = _rd(x, fmt), _ru(x, fmt)
+    if fmt == "fp32":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float32).astype(np.float64)
+    return _rn_grid(x, fmt)
+
+
+def _rn_grid(x, fmt):
+    """``_rn`` for any format of FORMATS, from ``_rd_grid``."""
+    x = np.asarray(x, dtype=np.float64)
+    lo, hi = _rd_grid(x, fmt), -_rd_grid(-x, fmt)
     _, _, fmax = FORMATS[fmt]
     with np.errstate(invalid="ignore"):
         dl, dh = x - lo, hi - x
@@ -257,8 +295,10 @@ def _round(x, fmt="fp32", extra=0.0):
         a = _add(lo, -_mul(_add(np.abs(lo), extra, +1), u, +1), -1)
         b = _add(hi, _mul(_add(np.abs(hi), extra, +1), u, +1), +1)
         edge = (a < -fmax) | (b > fmax)
-        rlo = np.where(edge, _rn(lo, fmt), _rd(a, fmt))
-        rhi = np.where(edge, _rn(hi, fmt), _ru(b, fmt))
+        rlo, rhi = _rd(a, fmt), _ru(b, fmt)
+        if edge.any():
+            rlo = np.where(edge, _rn(lo, fmt), rlo)
+            rhi = np.where(edge, _rn(hi, fmt), rhi)
         rlo = np.where(np.isinf(lo), lo, rlo)
         rhi = np.where(np.isinf(hi), hi, rhi)
     return rlo, rhi
@@ -369,12 +409,16 @@ def _scores(q, k, standard):
         s = q @ k.T
         mag = np.abs(q) @ np.abs(k).T
         return _rd(s - g * mag, "fp32"), _ru(s + g * mag, "fp32")
-    prod = q[:, None, :] * k[None, :, :]      # exact: two float32-grid values
-    return _accumulate(_round((prod, prod)), 2, standard)
+    chunk = max(1, (1 << 22) // max(1, S * E))
+    parts = []
+    for r in range(0, L, chunk):
+        prod = q[r:r + chunk, None, :] * k[None, :, :]      # exact: two float32-grid values
+        parts.append(_accumulate(_round((prod, prod)), 2, standard))
+    return np.concatenate([p_[0] for p_ in parts]), np.concatenate([p_[1] for p_ in parts])
 
 
 def _values(w, v, standard, n_extra):
-    """Enclosure of sum_j w_j v_j (L, Ev) for interval weights w (L, S) >= 0."""
+    """Enclosure of sum_j w_j v_j (L, Ev) for interval w (L, S) and exact v (S, Ev)."""
     S = v.shape[0]
     if standard == "any_order":
         slo, shi, mag = _prod_any(w[0], w[1], v)
@@ -523,13 +567,14 @@ def analyse(query, key, value, attn_mask=None, is_causal=False, scale=None, enab
     zero_q = np.zeros(q.shape[:-1] + (0,))
     bias = logits(zero_q, np.zeros(k.shape[:-1] + (0,)), attn_mask, is_causal, scale, enable_gqa)
     lead = np.broadcast_shapes(ell.shape[:-2], vv.shape[:-2], q.shape[:-2], out.shape[:-2])
-    qb = np.broadcast_to(q, lead + (L, E)).reshape(-1, L, E)
-    kb = np.broadcast_to(kk, lead + (S, E)).reshape(-1, S, E)
-    vb = np.broadcast_to(vv, lead + (S, Ev)).reshape(-1, S, Ev)
-    bb = np.broadcast_to(bias, lead + (L, S)).reshape(-1, L, S)
-    ob = np.broadcast_to(out, lead + (L, Ev)).reshape(-1, L, Ev)
-    lb = np.broadcast_to(lse, lead + (L,)).reshape(-1, L)
-    eb = np.broadcast_to(ell, lead + (L, S)).reshape(-1, L, S)
+    N = int(np.prod(lead, dtype=np.int64))
+    qb = np.broadcast_to(q, lead + (L, E)).reshape(N, L, E)
+    kb = np.broadcast_to(kk, lead + (S, E)).reshape(N, S, E)
+    vb = np.broadcast_to(vv, lead + (S, Ev)).reshape(N, S, Ev)
+    bb = np.broadcast_to(bias, lead + (L, S)).reshape(N, L, S)
+    ob = np.broadcast_to(out, lead + (L, Ev)).reshape(N, L, Ev)
+    lb = np.broadcast_to(lse, lead + (L,)).reshape(N, L)
+    eb = np.broadcast_to(ell, lead + (L, S)).reshape(N, L, S)
     sc = _scale_interval(E, scale)
 
     lo = np.empty(ob.shape)
@@ -586,3 +631,216 @@ def covers(computed_out, computed_lse, query, key, value, attn_mask=None, is_cau
     if computed_lse is not None:
         res.append(a.covers(lse=computed_lse))
     return tuple(res)
+
+
+# ------------------------------------------------------------------ the backward
+
+@dataclass(frozen=True)
+class BlockedBackward:
+    """A FlashAttention-style backward, with the roundings the page's default omits.
+
+    forward:      the forward (a Blocked, or None for the page's default budget) whose
+                  output O and logsumexp the backward reads: P_ij = exp(l_ij - lse_i) with
+                  lse_i any value that forward may return (the row sum enters through the
+                  logsumexp instead of a division), and D_i = grad_i . O_i with O_i any
+                  output it may return
+    round_inputs: P (in the product for grad_value) and dS (in the products for grad_query
+                  and grad_key) rounded to the input format (not for float32 inputs)
+    extra_logit_roundings, extra_lse_roundings: further roundings of each logit and of
+                  the logsumexp (an exponent formed in base 2 through scale * log2 e and
+                  lse * log2 e, each rounded)
+    """
+    forward: Blocked | None = None
+    round_inputs: bool = True
+    extra_logit_roundings: int = 0
+    extra_lse_roundings: int = 0
+
+
+def _contract(a, b, standard):
+    """Enclosure of a @ b for interval a (R, K) and exact b (K, C), every product rounded
+    and the K terms accumulated (normal orders or any order); rows in chunks for the
+    (R, K, C) temporaries of the normal orders."""
+    R, K = a[0].shape
+    C = b.shape[1]
+    if K == 0 or R == 0 or C == 0:
+        z = np.zeros((R, C))
+        return z, z
+    if standard == "any_order":
+        return _values(a, b, standard, 0)
+    chunk = max(1, (1 << 22) // max(1, K * C))
+    parts = [_values((a[0][r:r + chunk], a[1][r:r + chunk]), b, standard, 0) for r in range(0, R, chunk)]
+    return np.concatenate([p_[0] for p_ in parts]), np.concatenate([p_[1] for p_ in parts])
+
+
+def _bwd_head(q, k, v, g, bias, sc, fmt, ulps, standard, alg, fwd_o, fwd_lse):
+    """One (batch, head): enclosures of the weights P as they enter grad_value and of dS as
+    it enters grad_query and grad_key, both (L, S).  q (L, E), k (S, E), v (S, Ev) and the
+    output gradient g (L, Ev) are exact values; bias (L, S) as in the forward model (-inf for
+    every key of a special row); fwd_o (lo, hi) (L, Ev) and fwd_lse (lo, hi) (L,) are the
+    forward's enclosures (used by a BlockedBackward only)."""
+    kept = np.isfinite(bias)
+    has = kept.any(axis=1)
+    s = _scores(q, k, standard)
+    if q.shape[1] == 0:
+        x = (bias, bias)
+    else:
+        x = _iv_mul(s, sc)
+        x = (_add(x[0], bias, -1), _add(x[1], bias, +1))
+    ell = _round(x)
+    dP = _scores(g, v, standard)                      # grad_i . v_j
+    if alg is None:
+        ell = (np.where(kept, ell[0], -np.inf), np.where(kept, ell[1], -np.inf))
+        m = (np.max(ell[0], axis=1, initial=-np.inf), np.max(ell[1], axis=1, initial=-np.inf))
+        m = (np.where(has, m[0], 0.0), np.where(has, m[1], 0.0))
+        d = _round((_add(ell[0], -m[1][:, None], -1), _add(ell[1], -m[0][:, None], +1)))
+        w = _exp_within(d, ulps)
+        w = (np.where(kept, w[0], 0.0), np.where(kept, w[1], 0.0))
+        rs = _accumulate(w, 1, standard)
+        rs = (np.maximum(rs[0], 2.0 ** -149), np.maximum(rs[1], 2.0 ** -149))
+        P = _round(_iv_div_pos(w, (rs[0][:, None], rs[1][:, None])))
+        D = _accumulate(_round(_iv_mul(P, dP)), 1, standard)
+    else:
+        for _ in range(alg.extra_logit_roundings):
+            ell = _round(ell)
+        lse = fwd_lse
+        for _ in range(alg.extra_lse_roundings):
+            lse = _round(lse)
+        lse = (np.where(has, lse[0], 0.0), np.where(has, lse[1], 0.0))
+        with np.errstate(invalid="ignore"):
+            d = _round((_add(ell[0], -lse[1][:, None], -1), _add(ell[1], -lse[0][:, None], +1)))
+        d = (np.where(kept, d[0], -np.inf), np.where(kept, d[1], -np.inf))
+        P = _exp_within(d, ulps)
+        P = (np.where(kept, P[0], 0.0), np.where(kept, P[1], 0.0))
+        if g.shape[1] == 0:
+            D = (np.zeros(q.shape[0]), np.zeros(q.shape[0]))
+        else:
+            D = _accumulate(_round(_iv_mul((g, g), fwd_o)), 1, standard)
+    t = _round((_add(dP[0], -D[1][:, None], -1), _add(dP[1], -D[0][:, None], +1)))
+    dS = _round(_iv_mul(P, t))
+    dS = (np.where(kept, dS[0], 0.0), np.where(kept, dS[1], 0.0))
+    if alg is not None and alg.round_inputs and fmt != "fp32":
+        P, dS = _round(P, fmt), _round(dS, fmt)
+    return P, dS
+
+
+@dataclass
+class BackwardAnalysis:
+    """Per gradient ("grad_query", "grad_key", "grad_value"): the exact value rounded to the
+    output format, the range a correct implementation may return and the tolerance."""
+    rounded: dict
+    low: dict
+    high: dict
+    tolerance: dict
+
+    def covers(self, **computed):
+        """Elementwise coverage of computed gradients, by name (grad_query=..., ...)."""
+        res = {}
+        for name, c in computed.items():
+            c = _f64(c)
+            lo, hi = self.low[name], self.high[name]
+            with np.errstate(invalid="ignore"):
+                res[name] = (np.isnan(lo) & np.isnan(c)) | ((c >= lo) & (c <= hi))
+        return res
+
+
+def _head_index(shape, expand, lead):
+    """Flat index of the input copy each (flattened) head of ``lead`` reads: the input's
+    leading dims numbered, grouped heads repeated (``expand``), broadcast to ``lead``."""
+    idx = np.arange(int(np.prod(shape, dtype=np.int64))).reshape(shape)
+    if expand > 1:
+        idx = np.repeat(idx, expand, axis=-1)
+    return np.broadcast_to(idx, lead).reshape(-1)
+
+
+def analyse_backward(query, key, value, grad, attn_mask=None, is_causal=False, scale=None, enable_gqa=False, *,
+                     dtype="fp32", ulps=2, standard="normal", algorithm=None, out=None, lse=None):
+    """The tolerance analysis of the attention backward on these inputs (module docstring,
+    "The backward").  ``algorithm`` is None (the page's default budget) or a
+    BlockedBackward(...); the other arguments as for ``analyse``.  With a BlockedBackward,
+    ``out`` and ``lse`` may give the forward's output and logsumexp the backward is handed
+    (values, in the forward's shapes): they are then used as they are, instead of every
+    value the forward's model allows."""
+    from .sdpa_oracle import sdpa_backward
+    if dtype not in FORMATS:
+        raise ValueError("dtype must be fp32, bf16 or fp16")
+    q, k, v, g = _f64(query), _f64(key), _f64(value), _f64(grad)
+    exact = dict(zip(("grad_query", "grad_key", "grad_value"),
+                     sdpa_backward(q, k, v, g, attn_mask=attn_mask, is_causal=is_causal, scale=scale,
+                                   enable_gqa=enable_gqa)))
+    ell = logits(q, k, attn_mask, is_causal, scale, enable_gqa)
+    kk, vv = _expand_kv(q, k, v, enable_gqa)
+    E = q.shape[-1]
+    L, S, Ev = ell.shape[-2], ell.shape[-1], vv.shape[-1]
+    zero_q = np.zeros(q.shape[:-1] + (0,))
+    bias = logits(zero_q, np.zeros(k.shape[:-1] + (0,)), attn_mask, is_causal, scale, enable_gqa)
+    lead = np.broadcast_shapes(ell.shape[:-2], vv.shape[:-2], q.shape[:-2], g.shape[:-2])
+    N = int(np.prod(lead, dtype=np.int64))
+    qb = np.broadcast_to(q, lead + (L, E)).reshape(N, L, E)
+    kb = np.broadcast_to(kk, lead + (S, E)).reshape(N, S, E)
+    vb = np.broadcast_to(vv, lead + (S, Ev)).reshape(N, S, Ev)
+    gb = np.broadcast_to(g, lead + (L, Ev)).reshape(N, L, Ev)
+    bb = np.broadcast_to(bias, lead + (L, S)).reshape(N, L, S)
+    eb = np.broadcast_to(ell, lead + (L, S)).reshape(N, L, S)
+    sc = _scale_interval(E, scale)
+    if algorithm is not None:
+        if out is None or lse is None:
+            fa = analyse(q, k, v, attn_mask, is_causal, scale, enable_gqa, dtype=dtype, ulps=ulps,
+                         standard=standard, algorithm=algorithm.forward)
+        o_lo, o_hi = (fa.low, fa.high) if out is None else (_f64(out), _f64(out))
+        l_lo, l_hi = (fa.lse_low, fa.lse_high) if lse is None else (_f64(lse), _f64(lse))
+        fo = (np.broadcast_to(o_lo, lead + (L, Ev)).reshape(N, L, Ev),
+              np.broadcast_to(o_hi, lead + (L, Ev)).reshape(N, L, Ev))
+        fl = (np.broadcast_to(l_lo, lead + (L,)).reshape(N, L),
+              np.broadcast_to(l_hi, lead + (L,)).reshape(N, L))
+    heads = []
+    for n in range(N):
+        normal = _row_classes(eb[n])[3]
+        bn = np.where(normal[:, None], bb[n], -np.inf)
+        fwd = (None, None) if algorithm is None else ((fo[0][n], fo[1][n]), (fl[0][n], fl[1][n]))
+        heads.append(_bwd_head(qb[n], kb[n], vb[n], gb[n], bn, sc, dtype, ulps, standard, algorithm, *fwd))
+    # which input copy each head reads (grouped heads repeat key/value heads along the head axis)
+    rep = q.shape[-3] // k.shape[-3] if (enable_gqa and q.ndim >= 3 and k.ndim >= 3 and k.shape[-3] > 0
+                                        and q.shape[-3] != k.shape[-3]) else 1
+    qi = _head_index(q.shape[:-2], 1, lead)
+    ki = _head_index(k.shape[:-2], rep, lead)
+    vi = _head_index(v.shape[:-2], rep, lead)
+
+    def gather(index, count, rows, cols, term):
+        """For each input copy c: the enclosure of sum over the heads n reading c of
+        term(n) = (interval a (rows, K_n), exact b (K_n, cols)), one accumulation."""
+        out_lo = np.zeros((count, rows, cols))
+        out_hi = np.zeros((count, rows, cols))
+        for c in range(count):
+            ns = np.flatnonzero(index == c)
+            if ns.size == 0:
+                continue
+            ts = [term(n) for n in ns]
+            a = (np.concatenate([t[0][0] for t in ts], axis=1), np.concatenate([t[0][1] for t in ts], axis=1))
+            b = np.concatenate([t[1] for t in ts], axis=0)
+            out_lo[c], out_hi[c] = _contract(a, b, standard)
+        return out_lo, out_hi
+
+    nq = int(np.prod(q.shape[:-2], dtype=np.int64))
+    nk = int(np.prod(k.shape[:-2], dtype=np.int64))
+    nv = int(np.prod(v.shape[:-2], dtype=np.int64))
+    sums = {
+        "grad_query": gather(qi, nq, L, E, lambda n: (heads[n][1], kb[n])),
+        "grad_key": gather(ki, nk, S, E, lambda n: ((heads[n][1][0].T, heads[n][1][1].T), qb[n])),
+        "grad_value": gather(vi, nv, S, Ev, lambda n: ((heads[n][0][0].T, heads[n][0][1].T), gb[n])),
+    }
+    shapes = {"grad_query": q.shape, "grad_key": k.shape, "grad_value": v.shape}
+    rounded, low, high, tol = {}, {}, {}, {}
+    for name, r in sums.items():
+        if name != "grad_value":
+            r = _round(_iv_mul(r, (sc[0], sc[1])))      # the scale product
+        if dtype != "fp32":
+            r = _round(r, dtype)
+        x = exact[name]
+        special = ~np.isfinite(x)
+        lo = np.where(special, x, r[0].reshape(shapes[name]))
+        hi = np.where(special, x, r[1].reshape(shapes[name]))
+        rd = _rn(x, dtype)
+        with np.errstate(invalid="ignore"):
+            tl = np.where(np.isfinite(rd), np.maximum(hi - rd, rd - lo), 0.0)
+        rounded[name], low[name], high[name], tol[name] = rd, lo, hi, np.nan_to_num(tl)
+    return BackwardAnalysis(rounded, low, high, tol)

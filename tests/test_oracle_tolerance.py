@@ -123,7 +123,7 @@ def emulate_page(q, k, v, bias, scale, fmt, order="index", ulps=2, seed=0):
     c = np.float32(scale)                                             # the scale factor
     prod = (q32[:, None, :] * k32[None, :, :]).astype(np.float32)      # products rounded
     s = _sum32(prod, 2, order, rng) if q32.shape[1] else np.zeros((q32.shape[0], k32.shape[0]), np.float32)
-    with np.errstate(invalid="ignore", over="ignore"):
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
         ell = (s.astype(np.float64) * np.float64(c) + np.asarray(bias, np.float64)).astype(np.float32)  # one rounding
         m = np.max(ell, axis=1)
         d = (ell - m[:, None]).astype(np.float32)                    # the shift
@@ -466,6 +466,9 @@ def test_grid_helpers_against_numpy_float32():
     f = x32.astype(np.float32)
     assert (lo == np.nextafter(f, np.float32(-np.inf)).astype(np.float64)).all()
     assert (hi == np.nextafter(f, np.float32(np.inf)).astype(np.float64)).all()
+    # the spacing-based grid code (used for bf16 and fp16) agrees on the float32 grid too
+    assert (T._rn_grid(x, "fp32") == x32).all()
+    assert (T._rd_grid(x, "fp32") == rd).all() and (-T._rd_grid(-x, "fp32") == ru).all()
     # bf16 and fp16 grids: nearest-even agrees with the casts
     y = (rng.standard_normal(5000) * 100).astype(np.float32).astype(np.float64)
     assert (T._rn(y, "fp16") == y.astype(np.float16).astype(np.float64)).all()
