@@ -22,15 +22,16 @@
 //                     from LDS with the transposing ds_read_b64_tr_b16.
 //   bwd_dkdv_kernel   one workgroup per 128 keys, over the query heads of the
 //                     key/value head and their 64-row query blocks, with two
-//                     roles per 32-key slice: one wavefront computes S = Q K^T
-//                     and dP = dO V^T (one key per lane) and dK^T += Q^T dS,
-//                     another S and dV^T += dO^T P; P and dS are B operands
-//                     from the score registers, dO^T and Q^T are read
-//                     transposed from LDS.
-// No atomics: each gradient element has one owner.  The price is that S is
-// computed three times and dP twice, 8 matrix products per kept (query, key)
-// pair and head dimension instead of the 5 of one shared pass; in exchange
-// every wavefront fits in 256 registers (two per SIMD).
+//                     roles per 32-key slice, sharing a SIMD: one wavefront
+//                     computes S = Q K^T (one key per lane) and P, hands P to
+//                     the other through LDS and accumulates dV^T += dO^T P;
+//                     the other computes dP = dO V^T, then dS = P (dP - D) and
+//                     dK^T += Q^T dS.  P and dS are B operands from registers,
+//                     dO^T and Q^T are read transposed from LDS.
+// No atomics: each gradient element has one owner.  The price is that S and
+// dP are computed twice (once per kernel), 7 matrix products per kept (query,
+// key) pair and head dimension instead of the 5 of one shared pass; in
+// exchange every wavefront fits in 256 registers (two per SIMD).
 //
 // Optional masks, as in the forward: a float32 bias enters the logit as
 // scale * s + bias, a bool mask sets P = 0 on the keys it drops; the dQ kernel
@@ -40,22 +41,32 @@
 // variable-length batches (block-diagonal mask) take each segment's first
 // token and lengths from cu_seqlens and address rows by token.
 //
-// LDS tiles are row-major with 8 elements of padding per row (16-byte row
-// reads conflict-free).  Rows are stored at position swap23(r) within each
-// 32-row group (bits 2 and 3 of the row index swapped): then register r of
-// lane l of a 32x32 product tile holds row 16(r/8) + 8(l/32) + r%8 of its
-// group, which is exactly the k-slot order of a B operand, and each group of
-// 4 consecutive natural rows stays at 4 consecutive positions, as the
-// transposing reads need.
+// LDS tiles are row-major with 8 elements of padding per row.  A product's
+// row m (the row a lane reads for the first product, and so the row of the
+// result) is stored at position rowpos(m): m's place within its group of 16
+// rows, written 4a + b, becomes 4b + a.  Then the 16 lanes of a 16-byte row
+// read touch 16 distinct positions of one group (distinct 4-bank groups at
+// these strides), and the four rows of a transposing read (4 consecutive
+// product rows) sit 4 positions apart, i.e. 16 banks apart, so the 32 lanes
+// of one 8-byte transposing read hit 64 distinct banks.  Natural row r is
+// product row swap23(r) (bits 2 and 3 of its index within a 32-row group
+// swapped): then register r of lane l of a 32x32 product tile holds natural
+// row 16(r/8) + 8(l/32) + r%8 of its group, which is exactly the k-slot order
+// of a B operand.
 #include "attn_common.h"
 #include "device_utils.h"
+
+#include <type_traits>
 
 namespace sdpa {
 
 namespace {
 
 __device__ __forceinline__ int bwd_swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-__device__ __forceinline__ int bwd_pos(int r) { return (r & ~31) | bwd_swap23(r & 31); }
+// LDS position of product row m (the 4 x 4 transpose of m's place in its 16-row group)
+__device__ __forceinline__ int bwd_rowpos(int m) { return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3); }
+// LDS position of natural row r: product row swap23(r)
+__device__ __forceinline__ int bwd_pos(int r) { return bwd_rowpos((r & ~31) | bwd_swap23(r & 31)); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -67,8 +78,8 @@ template <int RS>
 __device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int c, int col0, int lane) {
     const int i = lane & 15, g = (lane >> 4) & 1, hh = lane >> 5;
     const int col = col0 + 16 * g + 4 * (i & 3);
-    const uint16_t* a0 = tile + (16 * c + 4 * hh + (i >> 2)) * RS + col;
-    const uint16_t* a1 = tile + (16 * c + 8 + 4 * hh + (i >> 2)) * RS + col;
+    const uint16_t* a0 = tile + bwd_rowpos(16 * c + 4 * hh + (i >> 2)) * RS + col;
+    const uint16_t* a1 = tile + bwd_rowpos(16 * c + 8 + 4 * hh + (i >> 2)) * RS + col;
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(uint32_t)(uintptr_t)a0);
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -148,7 +159,8 @@ void bwd_dq_kernel(BwdParams p) {
     static_assert(NCH % 256 == 0, "chunks per thread");
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
     const int lq = lane & 31, hh = lane >> 5;
     const int nbh = p.Hq * p.B;
     const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest (causal) first
@@ -263,15 +275,17 @@ void bwd_dq_kernel(BwdParams p) {
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const uint4 ka = *(const uint4*)(Ks + (kb * 32 + lq) * RS + kk * 16 + hh * 8);
-                    const uint4 va = *(const uint4*)(Vs + (kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    const uint4 ka = *(const uint4*)(Ks + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                    const uint4 va = *(const uint4*)(Vs + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
                     s[kb] = Tr::mfma32(as_vec8<Tr>(ka), as_vec8<Tr>(qreg[kk]), s[kb]);
                     dp[kb] = Tr::mfma32(as_vec8<Tr>(va), as_vec8<Tr>(dreg[kk]), dp[kb]);
                 }
             // register r of block kb: key key0 + 32kb + 16(r/8) + 8hh + r%8, query my_row
             const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
+            // keys of register r are kept below lim (every key of a block inside the limits)
             int lim = Sb - (key0 + hh * 8);
             if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
+            if (!edge) lim = BN;
             uint4 pb[4];
             constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;  // bytes per mask element
             // this wave's rows of the mask from key key0 on (unused without a mask)
@@ -300,7 +314,7 @@ void bwd_dq_kernel(BwdParams p) {
                     else
                         pv = fast_exp2(fmaf(s[kb][r], c2, -lse2));
                     if constexpr (MASK == MASK_BOOL) pv = ((mk >> r) & 1u) ? pv : 0.f;
-                    if (edge) pv = (kb * 32 + (r >> 3) * 16 + (r & 7) < lim) ? pv : 0.f;
+                    pv = (kb * 32 + (r >> 3) * 16 + (r & 7) < lim) ? pv : 0.f;
                     ds[r] = pv * (dp[kb][r] - drow);
                 }
 #pragma unroll
@@ -343,10 +357,31 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// x += sum over kk of A_kk B_kk, with A_kk the 16-byte LDS read at row + 16 kk
+// (16-bit words) and B_kk = b[kk]: a chain of products into one accumulator.
+// BATCH: all reads are issued before the first product, which then waits for
+// the first read only (otherwise the compiler may wait for each read in turn).
+template <typename Tr, int N, int RS, bool BATCH>
+__device__ __forceinline__ void chain_product(const uint16_t* row, const uint4* b, f32x16_t& x) {
+    if constexpr (BATCH) {
+        uint4 a[N];
+#pragma unroll
+        for (int kk = 0; kk < N; ++kk) a[kk] = *(const uint4*)(row + kk * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < N; ++kk) x = Tr::mfma32(as_vec8<Tr>(a[kk]), as_vec8<Tr>(b[kk]), x);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < N; ++kk) x = Tr::mfma32(as_vec8<Tr>(*(const uint4*)(row + kk * 16)), as_vec8<Tr>(b[kk]), x);
+    }
+}
+
 // Eight wavefronts per 128 keys, two roles over the same 32-key slices:
-// wavefronts 0-3 own dK (S, dP, dS, dK^T += Q^T dS), wavefronts 4-7 own dV
-// (S, P, dV^T += dO^T P).  Each role fits two wavefronts per SIMD; S is
-// computed by both roles.
+// wavefronts 0-3 own dV (S, P, dV^T += dO^T P), wavefronts 4-7 own dK (dP,
+// dS, dK^T += Q^T dS); wavefronts w and w + 4 share a SIMD.  Each step (64
+// queries) has two phases split by a barrier: first P (written to LDS in
+// fp32, kept packed for the dV product) and dP, then the dV product and dS
+// with the dK product, so the two wavefronts of a SIMD carry like loads.
 template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool VARLEN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
@@ -359,10 +394,18 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int NCH = BN * D / 8;
     constexpr int NCH_T = (NCH + NT - 1) / NT;
+    constexpr int PX = 4 * 2 * 64 * 16;           // P exchange: 4 key slices x 2 query halves x 64 lanes x 16
+    // operand reads of a product chain issued together (the masked E = 128 instances
+    // lack the registers: there the compiler's own interleaving avoids spills)
+    constexpr bool kBatchReads = MASK == MASK_NONE || D < 128;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float pex[PX];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int role = __builtin_amdgcn_readfirstlane(wave >> 2);  // 0: dK, 1: dV
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
+    // role 0 forms P and accumulates dV; role 1 forms dP and dS and accumulates dK.
+    // Waves kw and kw + 4 (one of each role, same keys) share a SIMD.
+    const int role = __builtin_amdgcn_readfirstlane(wave >> 2);
     const int kw = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
     const int nbh = p.Hkv * p.B;
@@ -381,23 +424,22 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int my_key = wkey0 + lq;
     const bool wave_has_keys = kw * 32 < krows;
 
-    // K^T (and for dK, V^T) operands (lane: key lq, elements 16kk + 8hh .. +7)
+    // K^T (role 0) or V^T (role 1) operand (lane: key lq, elements 16kk + 8hh .. +7)
     const int k_rs = (int)(p.k_sr * 2), v_rs = (int)(p.v_sr * 2);
     const auto krs = make_rsrc((const uint16_t*)p.k + k_b + kvh * p.k_sh + (int64_t)k0 * p.k_sr,
                                (krows - 1) * k_rs + D * 2);
     const auto vrs = make_rsrc((const uint16_t*)p.v + v_b + kvh * p.v_sh + (int64_t)k0 * p.v_sr,
                                (krows - 1) * v_rs + D * 2);
     const int lkey = kw * 32 + lq;
-    uint4 kreg[NKK], vreg[NKK];
+    uint4 kvreg[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        kreg[kk] = buf_load16(krs, lkey * k_rs + (kk * 16 + hh * 8) * 2);
-        vreg[kk] = role == 0 ? buf_load16(vrs, lkey * v_rs + (kk * 16 + hh * 8) * 2) : zero4();
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+        kvreg[kk] = role == 0 ? buf_load16(krs, lkey * k_rs + (kk * 16 + hh * 8) * 2)
+                              : buf_load16(vrs, lkey * v_rs + (kk * 16 + hh * 8) * 2);
     const float c2 = p.scale * kLog2e;
     wait_vmem_all();  // as in the dQ kernel: no wait for these inside the loop
 
-    f32x16_t acc[NDB];  // dK^T (role 0) or dV^T (role 1): rows e, columns keys
+    f32x16_t acc[NDB];  // dV^T (role 0) or dK^T (role 1): rows e, columns keys
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
@@ -459,6 +501,9 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     };
 
+    // this wave's P exchange area of query half qb: float4 j of lane l at (j * 64 + l) * 4
+    float* const px = pex + kw * (2 * 64 * 16);
+
     if (nsteps > 0) {
         load_tile(0);
         store_tile(0);
@@ -473,104 +518,159 @@ void bwd_dkdv_kernel(BwdParams p) {
         const float* Ls = (const float*)(Gs + TILE);
         // causal: the wave's keys need queries >= wkey0
         const bool active = wave_has_keys && (!CAUSAL || qrow0 + BN - 1 >= wkey0);
+        uint4 pw[2][2];     // role 0: P of each query half, packed as B operands
+        f32x16_t dp[2];     // role 1: dP of each query half
+        // ---- phase 1: role 0 forms P = exp(l - lse) (into the exchange area and
+        // packed for its dV product), role 1 forms dP = dO V^T
+        if (active) {
+            if (role == 0) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    // mask values of this lane's key for the 16 queries of register r
+                    // (query 32qb + 16(r/8) + 8hh + r%8 of the block), loaded before the products
+                    float mb[16];
+                    uint32_t mk = ~0u;
+                    if constexpr (MASK != MASK_NONE) {
+                        constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
+                        const int qf = qrow0 + qb * 32, nq = Lb - qf;
+                        const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                                                                         (int64_t)qf * p.m_sr + wkey0) * MES,
+                                                  nq > 0 ? ((nq - 1) * (int)p.m_sr + (Sb - wkey0)) * MES : 0);
+                        mk = 0;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int off = ((16 * (r >> 3) + 8 * hh + (r & 7)) * (int)p.m_sr + lq) * MES;
+                            if constexpr (MASK == MASK_FLOAT)
+                                mb[r] = __uint_as_float(buf_load4(mr, off));
+                            else
+                                mk |= (buf_load1(mr, off) != 0 ? 1u : 0u) << r;
+                        }
+                    }
+                    f32x16_t sc = f32x16_t{};
+                    chain_product<Tr, NKK, RS, kBatchReads>(Qs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8, kvreg, sc);
+                    // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
+                    const int qbase = qb * 32 + 8 * hh;
+                    const bool edge = (qrow0 + BN > Lb) || (CAUSAL && qrow0 < wkey0 + 31);
+                    float w[16];
+                    // two copies, with and without the edge test (see the dQ kernel)
+                    auto weights = [&](auto edge_c) {
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const float4 la = *(const float4*)(Ls + qbase + 16 * half);
+                        const float4 lb = *(const float4*)(Ls + qbase + 16 * half + 4);
+                        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int r = 8 * half + j;
+                            float e;
+                            if constexpr (MASK == MASK_FLOAT)
+                                e = fast_exp2(fmaf(fmaf(sc[r], p.scale, mb[r]), kLog2e, -lv[j]));
+                            else
+                                e = fast_exp2(fmaf(sc[r], c2, -lv[j]));
+                            if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
+                            if constexpr (decltype(edge_c)::value) {
+                                const int qi = qrow0 + qbase + 16 * half + j;
+                                const bool keep = qi < Lb && (!CAUSAL || qi >= my_key);
+                                e = keep ? e : 0.f;
+                            }
+                            w[r] = e;
+                        }
+                    }
+                    };
+                    if (edge)
+                        weights(std::true_type{});
+                    else
+                        weights(std::false_type{});
+                    float* pq = px + qb * (64 * 16);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *(float4*)(pq + (j * 64 + lane) * 4) = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2],
+                                                                           w[4 * j + 3]);
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        pw[qb][c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
+                        pw[qb][c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
+                        pw[qb][c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
+                        pw[qb][c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    dp[qb] = f32x16_t{};
+                    chain_product<Tr, NKK, RS, kBatchReads>(Gs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8, kvreg, dp[qb]);
+                }
+            }
+        }
+        __syncthreads();   // P of this step is in the exchange area
+        // ---- phase 2: role 0 dV^T += dO^T P; role 1 dS = P (dP - D), dK^T += Q^T dS
         if (active) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                // mask values of this lane's key for the 16 queries of register r
-                // (query 32qb + 16(r/8) + 8hh + r%8 of the block), loaded before the products
-                float mb[16];
-                uint32_t mk = ~0u;
-                if constexpr (MASK != MASK_NONE) {
-                    constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
-                    const int qf = qrow0 + qb * 32, nq = Lb - qf;
-                    const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
-                                                                     (int64_t)qf * p.m_sr + wkey0) * MES,
-                                              nq > 0 ? ((nq - 1) * (int)p.m_sr + (Sb - wkey0)) * MES : 0);
-                    mk = 0;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int off = ((16 * (r >> 3) + 8 * hh + (r & 7)) * (int)p.m_sr + lq) * MES;
-                        if constexpr (MASK == MASK_FLOAT)
-                            mb[r] = __uint_as_float(buf_load4(mr, off));
-                        else
-                            mk |= (buf_load1(mr, off) != 0 ? 1u : 0u) << r;
-                    }
-                }
-                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const uint4 qa = *(const uint4*)(Qs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
-                    s = Tr::mfma32(as_vec8<Tr>(qa), as_vec8<Tr>(kreg[kk]), s);
-                }
+                uint4 op[2];
                 if (role == 0) {
+                    op[0] = pw[qb][0];
+                    op[1] = pw[qb][1];
+                } else {
+                    const float* pq = px + qb * (64 * 16);
+                    const int qbase = qb * 32 + 8 * hh;
+                    float w[16];
 #pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) {
-                        const uint4 ga = *(const uint4*)(Gs + (qb * 32 + lq) * RS + kk * 16 + hh * 8);
-                        dp = Tr::mfma32(as_vec8<Tr>(ga), as_vec8<Tr>(vreg[kk]), dp);
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 e4 = *(const float4*)(pq + (j * 64 + lane) * 4);
+                        w[4 * j] = e4.x; w[4 * j + 1] = e4.y; w[4 * j + 2] = e4.z; w[4 * j + 3] = e4.w;
                     }
-                }
-                // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
-                const int qbase = qb * 32 + 8 * hh;
-                const bool edge = (qrow0 + BN > Lb) || (CAUSAL && qrow0 < wkey0 + 31);
-                float w[16];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const float4 la = *(const float4*)(Ls + qbase + 16 * half);
-                    const float4 lb = *(const float4*)(Ls + qbase + 16 * half + 4);
-                    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-                    float dv8[8];
-                    if (role == 0) {
+                    for (int half = 0; half < 2; ++half) {
                         const float4 da = *(const float4*)(Ls + BN + qbase + 16 * half);
                         const float4 db4 = *(const float4*)(Ls + BN + qbase + 16 * half + 4);
-                        dv8[0] = da.x; dv8[1] = da.y; dv8[2] = da.z; dv8[3] = da.w;
-                        dv8[4] = db4.x; dv8[5] = db4.y; dv8[6] = db4.z; dv8[7] = db4.w;
+                        const float dv8[8] = {da.x, da.y, da.z, da.w, db4.x, db4.y, db4.z, db4.w};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) w[8 * half + j] = w[8 * half + j] * (dp[qb][8 * half + j] - dv8[j]);
                     }
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int r = 8 * half + j;
-                        float e;
-                        if constexpr (MASK == MASK_FLOAT)
-                            e = fast_exp2(fmaf(fmaf(s[r], p.scale, mb[r]), kLog2e, -lv[j]));
-                        else
-                            e = fast_exp2(fmaf(s[r], c2, -lv[j]));
-                        if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
-                        if (edge) {
-                            const int qi = qrow0 + qbase + 16 * half + j;
-                            const bool keep = qi < Lb && (!CAUSAL || qi >= my_key);
-                            e = keep ? e : 0.f;
+                    for (int c = 0; c < 2; ++c) {
+                        op[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
+                        op[c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
+                        op[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
+                        op[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
+                    }
+                }
+                // over two 16-query chunks: role 0 reads dO^T, role 1 Q^T
+                const uint16_t* Xs = role == 0 ? Gs : Qs;
+                if constexpr (kBatchReads) {
+                    uint4 xa[2][NDB];   // all reads first: the products wait for the first only
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) xa[c][db] = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            acc[db] = Tr::mfma32(as_vec8<Tr>(xa[c][db]), as_vec8<Tr>(op[c]), acc[db]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const uint4 xa = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
+                            acc[db] = Tr::mfma32(as_vec8<Tr>(xa), as_vec8<Tr>(op[c]), acc[db]);
                         }
-                        w[r] = role == 0 ? e * (dp[r] - dv8[j]) : e;  // dS or P
-                    }
                 }
-                uint4 pw[2];
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    pw[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
-                    pw[c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
-                    pw[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
-                    pw[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
-                }
-                // dK^T += Q^T dS (role 0) or dV^T += dO^T P (role 1) over two 16-query chunks
-                const uint16_t* Xs = role == 0 ? Qs : Gs;
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const uint4 xa = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
-                        acc[db] = Tr::mfma32(as_vec8<Tr>(xa), as_vec8<Tr>(pw[c]), acc[db]);
-                    }
             }
         }
         if (st + 1 < nsteps) store_tile((st + 1) & 1);
         __syncthreads();
     }
 
-    // dK = scale * dK^T or dV = dV^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
-    const float f = role == 0 ? p.scale : 1.f;
-    const int o_rs = (int)((role == 0 ? p.dk_sr : p.dv_sr) * 2);
-    void* obase = role == 0 ? p.dk : p.dv;
-    const int64_t o_sb = role == 0 ? p.dk_sb : p.dv_sb, o_sh = role == 0 ? p.dk_sh : p.dv_sh;
-    const int64_t o_sr = role == 0 ? p.dk_sr : p.dv_sr;
+    // dV = dV^T or dK = scale * dK^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
+    const float f = role == 1 ? p.scale : 1.f;
+    const int o_rs = (int)((role == 1 ? p.dk_sr : p.dv_sr) * 2);
+    void* obase = role == 1 ? p.dk : p.dv;
+    const int64_t o_sb = role == 1 ? p.dk_sb : p.dv_sb, o_sh = role == 1 ? p.dk_sh : p.dv_sh;
+    const int64_t o_sr = role == 1 ? p.dk_sr : p.dv_sr;
     const auto ors = make_rsrc((uint16_t*)obase + (VARLEN ? kc * o_sr : b * o_sb) + kvh * o_sh + (int64_t)k0 * o_sr,
                                (krows - 1) * o_rs + D * 2);
 #pragma unroll
