@@ -157,6 +157,9 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int NCH = BN * D / 8;      // 16-byte chunks per block
     constexpr int NCH_T = NCH / 256;     // per thread
     static_assert(NCH % 256 == 0, "chunks per thread");
+    // operand reads issued in groups ahead of their products, where the registers allow
+    constexpr bool kBatchReads = D < 128;                     // score and dP operands
+    constexpr bool kBatchTr = MASK == MASK_NONE || D < 128;   // dQ product operands
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -271,15 +274,38 @@ void bwd_dq_kernel(BwdParams p) {
         const bool active = wave_has_rows && (!CAUSAL || key0 <= q0 + wrow0 + 31);
         if (active) {
             f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+            if constexpr (kBatchReads) {
+                // the operand reads of two head-dim chunks (8 reads) issued together
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
+                for (int k0 = 0; k0 < NKK; k0 += 2) {
+                    uint4 ka[2][2], va[2][2];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint4 ka = *(const uint4*)(Ks + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
-                    const uint4 va = *(const uint4*)(Vs + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
-                    s[kb] = Tr::mfma32(as_vec8<Tr>(ka), as_vec8<Tr>(qreg[kk]), s[kb]);
-                    dp[kb] = Tr::mfma32(as_vec8<Tr>(va), as_vec8<Tr>(dreg[kk]), dp[kb]);
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            ka[i][kb] = *(const uint4*)(Ks + bwd_rowpos(kb * 32 + lq) * RS + (k0 + i) * 16 + hh * 8);
+                            va[i][kb] = *(const uint4*)(Vs + bwd_rowpos(kb * 32 + lq) * RS + (k0 + i) * 16 + hh * 8);
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            s[kb] = Tr::mfma32(as_vec8<Tr>(ka[i][kb]), as_vec8<Tr>(qreg[k0 + i]), s[kb]);
+                            dp[kb] = Tr::mfma32(as_vec8<Tr>(va[i][kb]), as_vec8<Tr>(dreg[k0 + i]), dp[kb]);
+                        }
                 }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const uint4 ka = *(const uint4*)(Ks + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                        const uint4 va = *(const uint4*)(Vs + bwd_rowpos(kb * 32 + lq) * RS + kk * 16 + hh * 8);
+                        s[kb] = Tr::mfma32(as_vec8<Tr>(ka), as_vec8<Tr>(qreg[kk]), s[kb]);
+                        dp[kb] = Tr::mfma32(as_vec8<Tr>(va), as_vec8<Tr>(dreg[kk]), dp[kb]);
+                    }
+            }
             // register r of block kb: key key0 + 32kb + 16(r/8) + 8hh + r%8, query my_row
             const bool edge = (key0 + BN > Sb) || (CAUSAL && key0 + BN - 1 > q0 + wrow0);
             // keys of register r are kept below lim (every key of a block inside the limits)
@@ -326,13 +352,25 @@ void bwd_dq_kernel(BwdParams p) {
                 }
             }
             // dQ^T (rows e, columns queries) += K^T dS^T over the block's 4 key chunks
+            if constexpr (kBatchTr) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c) {
+                    uint4 a[NDB];   // one chunk's reads together
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const uint4 a = read_tr<RS>(Ks, c, db * 32, lane);
-                    acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb[c]), acc[db]);
+                    for (int db = 0; db < NDB; ++db) a[db] = read_tr<RS>(Ks, c, db * 32, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma32(as_vec8<Tr>(a[db]), as_vec8<Tr>(pb[c]), acc[db]);
                 }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const uint4 a = read_tr<RS>(Ks, c, db * 32, lane);
+                        acc[db] = Tr::mfma32(as_vec8<Tr>(a), as_vec8<Tr>(pb[c]), acc[db]);
+                    }
+            }
         }
         // the other stage was last read a step ago, before the last barrier
         if (t + 1 < ntiles) store_tile((t + 1) & 1);
