@@ -127,8 +127,9 @@ def oracle_timing(calls, work, unit, sample):
             "median_of": 3, "seconds": round(med, 3), "sample": sample}
 
 
-def cpu_baseline(n_heads=24):
-    """The float64 oracle on whole heads of the headline workload (median of 3 passes)."""
+def cpu_baseline(n_heads=64):
+    """The float64 oracle on whole heads of the headline workload (median of 3 passes;
+    by default all 64 heads, i.e. the whole workload: ~7 s a pass on 16 cores)."""
     from oracle import sdpa_oracle as O
     from transformer_attention_04_amd import inputs
     q, k, v = inputs.workload_inputs("bf16_causal_e128")
