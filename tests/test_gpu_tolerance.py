@@ -147,6 +147,19 @@ def test_fp32_path():
         check_covered(out, lse, q, k, v, "fp32", f"fp32 {kw}", F32, **kw)
 
 
+@pytest.mark.parametrize("E,Ev", [(96, 96), (128, 128), (40, 72)])
+def test_fp32_unit_scale_wide_heads(E, Ev):
+    """fp32 at scale 1 with wide heads (logits of size ~sqrt(E)): beyond the fixed 1e-5
+    bar's reach, so held to the per-element range instead; causal and not, grouped heads,
+    ragged tiles."""
+    q, k, v = inputs.randn_qkv((2, 4, 150, E), (2, 2, 170, E), (2, 2, 170, Ev), "fp32", seed=E + Ev)
+    for causal in (False, True):
+        kw = dict(is_causal=causal, scale=1.0, enable_gqa=True)
+        out, lse = S.sdpa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **kw)
+        torch.cuda.synchronize()
+        check_covered(out, lse, q, k, v, "fp32", f"fp32 E={E} Ev={Ev} {kw}", F32, **kw)
+
+
 def test_headline_shape_sampled():
     """bf16 causal B=4 H=16 L=S=2048 E=128 in the benchmark's launch configuration;
     two (batch, head) slices against their per-element tolerance."""
