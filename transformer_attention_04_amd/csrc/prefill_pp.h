@@ -127,6 +127,20 @@ __device__ __forceinline__ void pp_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// pp_barrier<vm> for a wave-uniform vm taken from {0, A, B, A + B} (the counts
+// the first item's waits use).
+template <int A, int B>
+__device__ __forceinline__ void pp_barrier_of(int vm) {
+    if (vm == A + B)
+        pp_barrier<A + B>();
+    else if (vm == B)
+        pp_barrier<B>();
+    else if (vm == A)
+        pp_barrier<A>();
+    else
+        pp_barrier<0>();
+}
+
 // One direct-to-LDS load: lane m's 16 bytes at byte offset voff of the buffer
 // land at LDS byte address m0 + 16 m.  Written as asm so that the compiler does
 // not track it; the waits for it are the explicit ones at slot barriers.  The
@@ -705,15 +719,27 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
 
     // Prologue: Q^T of the first item (float mask: the bias of the wave's
     // first block instead), K blocks 0-2 and V blocks 0-1.
+    // Without a mask the first scores need only Q^T and K block 0: the barrier
+    // waits for those, and K blocks 1-2 (K waves) and V blocks 0-1 (V waves) land
+    // during the first scores (a second barrier before the first step's
+    // products waits for K block 1 and V block 0).  vmcnt counts the loads in
+    // the order they were issued.
     int P = (int)blockIdx.x, s = 0;
+    int n_kv = 0;  // K or V blocks this wave loaded in the prologue
     if constexpr (ANYMASK) {
         bias_enter();
         bias_next();
     } else {
         load_q(P, 0);
     }
-    for (int i = 0; i < 3 - grp; ++i) load_next();
-    pp_barrier<0>();
+    for (int i = 0; i < 3 - grp; ++i) n_kv += load_next() ? 1 : 0;
+    if constexpr (ANYMASK) {
+        pp_barrier<0>();
+    } else {
+        const int later = grp == 0 ? max(n_kv - 1, 0) : n_kv;  // blocks allowed in flight
+        pp_barrier_of<NDMA, 2 * NDMA>(later * NDMA);
+    }
+    bool first_item = true;
     int cur = 0;  // ring stage of the current block
     auto advance = [](int st) { return st == NSTAGE - 1 ? 0 : st + 1; };
 
@@ -764,6 +790,12 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             load_q(nP, ns);
         }
         scores(cur, sA);  // unconditional, so that no score register stays live across items
+        if (!ANYMASK && first_item) {
+            // K block 1 (K waves) and V block 0 (V waves) before the first step
+            const int later = grp == 0 ? max(n_kv - 2, 0) : max(n_kv - 1, 0);
+            pp_barrier_of<NDMA, NQDMA>(later * NDMA + (has_next ? NQDMA : 0));
+        }
+        first_item = false;
         if (ANYMASK && last_tile >= 0) {
             // the bias of block 0 (loaded after this wave's last bias read), then
             // the next block's load into the area just read
