@@ -151,27 +151,41 @@ def test_backward_small_and_degenerate():
     assert_bwd(gpu, ref, "L<S causal (keys past the last query get 0)", ctx=ctx)
 
 
-def test_backward_headline_shape_sampled():
+def test_backward_headline_shape_full():
     """The bf16 causal B=4 H=16 L=S=2048 E=128 shape, in the launch configuration the
-    benchmark times; five (batch, head) slices checked against the oracle."""
+    benchmark times: gradients written into NaN-filled buffers, every (batch, head)
+    against the oracle's backward (per-tensor bar, the oracle's heads in a thread
+    pool), and two of them element by element against the per-element range."""
     q, k, v = inputs.workload_inputs("bf16_causal_e128")
     g = inputs.randn_qkv(tuple(q.shape), (1, 1, 1, 128), (1, 1, 1, 128), "bf16", seed=99)[0]
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
     out, lse = S.sdpa_fwd(qd, kd, vd, is_causal=True)
-    dq, dk, dv = S.sdpa_bwd(qd, kd, vd, out, lse, gd, is_causal=True)
+    grads = tuple(torch.full(t.shape, float("nan"), dtype=t.dtype, device=DEV) for t in (qd, kd, vd))
+    dq, dk, dv = S.sdpa_bwd(qd, kd, vd, out, lse, gd, is_causal=True, grads=grads)
     torch.cuda.synchronize()
+    assert all(a.data_ptr() == b.data_ptr() for a, b in zip((dq, dk, dv), grads))
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     oc, lc = _np(out), _np(lse).reshape(out.shape[:-1])
-    for b, h in [(0, 0), (1, 7), (2, 15), (3, 3), (3, 15)]:
-        ref = O.sdpa_backward(q[b, h], k[b, h], v[b, h], g[b, h], is_causal=True)
-        assert_bwd((dq[b, h], dk[b, h], dv[b, h]), ref, f"headline b={b} h={h}")
-    # per element on two slices (the model takes ~15 s a slice on the host), in parallel
+    B, H = q.shape[0], q.shape[1]
+
     def one(bh):
+        b, h = divmod(bh, H)
+        return bh, O.sdpa_backward(q[b, h], k[b, h], v[b, h], g[b, h], is_causal=True)
+
+    with ThreadPoolExecutor(8) as ex:
+        for bh, ref in ex.map(one, range(B * H)):
+            b, h = divmod(bh, H)
+            assert_bwd((dq[b, h], dk[b, h], dv[b, h]), ref, f"headline b={b} h={h}")
+
+    # per element on two heads (the model takes ~15 s a head on the host), in parallel
+    def per_element(bh):
         b, h = bh
         ctx = dict(qkvg=(q[b, h], k[b, h], v[b, h], g[b, h]), kw=dict(is_causal=True), dtype="bf16",
                    out=oc[b, h], lse=lc[b, h])
         check_bwd_covered((dq[b, h], dk[b, h], dv[b, h]), ctx, f"headline b={b} h={h}")
+
     with ThreadPoolExecutor(2) as ex:
-        list(ex.map(one, [(0, 0), (3, 15)]))
+        list(ex.map(per_element, [(0, 0), (3, 15)]))
 
 
 def _masks(shape, seed):

@@ -370,14 +370,15 @@ def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
 
 
 def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False, scale=None,
-             enable_gqa=False, workspace=None):
+             enable_gqa=False, workspace=None, grads=None):
     """Gradients of exact attention on the GPU: returns (grad_query, grad_key, grad_value).
 
     ``out`` and ``lse`` are sdpa_fwd's results for the same arguments (the
     optional float or bool ``attn_mask`` included) and ``grad`` the gradient
     with respect to ``out`` (exactref.ai "scaled_dot_product_attention.backward";
     the mask gets no gradient).  The outputs have the shapes and dtype of
-    query, key and value.
+    query, key and value; ``grads`` may pass them in as a tuple of contiguous
+    tensors (written in place).
     """
     lib = load_library()
     _require_gpu(query, key, value, out, lse, grad, attn_mask)
@@ -393,9 +394,16 @@ def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False,
     m4, mdt = _mask_4d(attn_mask, q4, S)
     dm = _desc(m4) if m4 is not None else None
     dev = query.device
-    dq4 = torch.empty((B, Hq, L, E), dtype=query.dtype, device=dev)
-    dk4 = torch.empty((B, Hkv, S, E), dtype=query.dtype, device=dev)
-    dv4 = torch.empty((B, Hkv, S, Ev), dtype=query.dtype, device=dev)
+    if grads is None:
+        dq4 = torch.empty((B, Hq, L, E), dtype=query.dtype, device=dev)
+        dk4 = torch.empty((B, Hkv, S, E), dtype=query.dtype, device=dev)
+        dv4 = torch.empty((B, Hkv, S, Ev), dtype=query.dtype, device=dev)
+    else:
+        want = ((B, Hq, L, E), (B, Hkv, S, E), (B, Hkv, S, Ev))
+        dq4, dk4, dv4 = (_as4d(t) for t in grads)
+        for t, shp in zip((dq4, dk4, dv4), want):
+            if tuple(t.shape) != shp or t.dtype != query.dtype or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"grads must be contiguous {query.dtype} tensors of shapes {want}")
     with torch.cuda.device(dev):
         nbytes = sdpa_bwd_workspace_size(q4, k4, v4, enable_gqa)
         if workspace is None or workspace.numel() < nbytes:
