@@ -417,9 +417,15 @@ __device__ __forceinline__ void chain_product(const uint16_t* row, const uint4* 
 // Eight wavefronts per 128 keys, two roles over the same 32-key slices:
 // wavefronts 0-3 own dV (S, P, dV^T += dO^T P), wavefronts 4-7 own dK (dP,
 // dS, dK^T += Q^T dS); wavefronts w and w + 4 share a SIMD.  Each step (64
-// queries) has two phases split by a barrier: first P (written to LDS in
-// fp32, kept packed for the dV product) and dP, then the dV product and dS
-// with the dK product, so the two wavefronts of a SIMD carry like loads.
+// queries) runs in two phases split by barriers, the dK role one step behind:
+// in phase A the dV role forms P of step t (the S product and its
+// exponentials; P written to LDS in fp32 and kept packed for the dV product)
+// while the dK role forms dS of step t - 1 and its dK product; in phase B the
+// dV role runs the dV product and the dK role dP of step t.  Both roles then
+// carry one product chain plus like vector work in phase A and one product
+// chain in phase B, so neither waits long at the barriers (with dS and the dK
+// product in the phase of the dV product, each role used to wait ~18% of a
+// step for the other).
 template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool VARLEN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
@@ -432,10 +438,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int NCH = BN * D / 8;
     constexpr int NCH_T = (NCH + NT - 1) / NT;
-    constexpr int PX = 4 * 2 * 64 * 16;           // P exchange: 4 key slices x 2 query halves x 64 lanes x 16
-    // operand reads of a product chain issued together (the masked E = 128 instances
-    // lack the registers: there the compiler's own interleaving avoids spills)
-    constexpr bool kBatchReads = MASK == MASK_NONE || D < 128;
+    constexpr int PX = 2 * 4 * 2 * 64 * 16;       // P exchange: 2 step parities x 4 key slices x 2 query halves x 64 lanes x 16
+    // operand reads of a product chain issued together
+    constexpr bool kBatchReads = true;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
     __shared__ __attribute__((aligned(16))) float pex[PX];
 
@@ -539,168 +544,198 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     };
 
-    // this wave's P exchange area of query half qb: float4 j of lane l at (j * 64 + l) * 4
-    float* const px = pex + kw * (2 * 64 * 16);
+    // this wave's P exchange area for the steps of parity x, query half qb:
+    // float4 j of lane l at (j * 64 + l) * 4
+    auto px_of = [&](int x, int qb) { return pex + x * (PX / 2) + kw * (2 * 64 * 16) + qb * (64 * 16); };
+    // causal: the wave's keys need queries >= wkey0
+    auto active_at = [&](int qrow0) { return wave_has_keys && (!CAUSAL || qrow0 + BN - 1 >= wkey0); };
+    // acc += X^T op over the two 16-query chunks of query half qb: X = dO (role
+    // 0, op = P) or Q (role 1, op = dS), read transposed from the stage at Xs
+    auto transposed_products = [&](const uint16_t* Xs, int qb, const uint4* op) {
+        uint4 xa[2][NDB];   // all reads first: the products wait for the first only
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) xa[c][db] = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = Tr::mfma32(as_vec8<Tr>(xa[c][db]), as_vec8<Tr>(op[c]), acc[db]);
+    };
 
     if (nsteps > 0) {
         load_tile(0);
         store_tile(0);
     }
     __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        if (st + 1 < nsteps) load_tile(st + 1);
-        int h, qrow0;
-        step_coords(st, h, qrow0);
-        const uint16_t* Qs = smem + (st & 1) * STAGE;
-        const uint16_t* Gs = Qs + TILE;
-        const float* Ls = (const float*)(Gs + TILE);
-        // causal: the wave's keys need queries >= wkey0
-        const bool active = wave_has_keys && (!CAUSAL || qrow0 + BN - 1 >= wkey0);
-        uint4 pw[2][2];     // role 0: P of each query half, packed as B operands
-        f32x16_t dp[2];     // role 1: dP of each query half
-        // ---- phase 1: role 0 forms P = exp(l - lse) (into the exchange area and
-        // packed for its dV product), role 1 forms dP = dO V^T
-        if (active) {
-            if (role == 0) {
+    // Iteration it: phase A, role 0 forms P of step it, role 1 dS and dK of step
+    // it - 1; barrier; phase B, role 0 the dV product of step it, role 1 dP of
+    // step it; barrier.  Both phases then carry like work on the two roles.
+    // The two roles run the same sequence of barriers in separate loops (their
+    // values then do not compete for registers).
+    if (role == 0) {
+        uint4 pw[2][2];   // P of the current step, packed as B operands
+        for (int it = 0; it <= nsteps; ++it) {
+            if (it + 1 < nsteps) load_tile(it + 1);
+            // phase A: P of step it
+            if (it < nsteps) {
+                int h, qrow0;
+                step_coords(it, h, qrow0);
+                const uint16_t* Qs = smem + (it & 1) * STAGE;
+                const float* Ls = (const float*)(Qs + 2 * TILE);
+                if (active_at(qrow0)) {
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    // mask values of this lane's key for the 16 queries of register r
-                    // (query 32qb + 16(r/8) + 8hh + r%8 of the block), loaded before the products
-                    float mb[16];
-                    uint32_t mk = ~0u;
-                    if constexpr (MASK != MASK_NONE) {
-                        constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
-                        const int qf = qrow0 + qb * 32, nq = Lb - qf;
-                        const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
-                                                                         (int64_t)qf * p.m_sr + wkey0) * MES,
-                                                  nq > 0 ? ((nq - 1) * (int)p.m_sr + (Sb - wkey0)) * MES : 0);
-                        mk = 0;
+                    for (int qb = 0; qb < 2; ++qb) {
+                        // mask values of this lane's key for the 16 queries of register r
+                        // (query 32qb + 16(r/8) + 8hh + r%8 of the block), loaded before the products
+                        float mb[16];
+                        uint32_t mk = ~0u;
+                        if constexpr (MASK != MASK_NONE) {
+                            constexpr int MES = MASK == MASK_FLOAT ? 4 : 1;
+                            const int qf = qrow0 + qb * 32, nq = Lb - qf;
+                            const auto mr = make_rsrc((const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh +
+                                                                             (int64_t)qf * p.m_sr + wkey0) * MES,
+                                                      nq > 0 ? ((nq - 1) * (int)p.m_sr + (Sb - wkey0)) * MES : 0);
+                            mk = 0;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int off = ((16 * (r >> 3) + 8 * hh + (r & 7)) * (int)p.m_sr + lq) * MES;
-                            if constexpr (MASK == MASK_FLOAT)
-                                mb[r] = __uint_as_float(buf_load4(mr, off));
-                            else
-                                mk |= (buf_load1(mr, off) != 0 ? 1u : 0u) << r;
-                        }
-                    }
-                    f32x16_t sc = f32x16_t{};
-                    chain_product<Tr, NKK, RS, kBatchReads>(Qs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8, kvreg, sc);
-                    // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
-                    const int qbase = qb * 32 + 8 * hh;
-                    const bool edge = (qrow0 + BN > Lb) || (CAUSAL && qrow0 < wkey0 + 31);
-                    float w[16];
-                    // two copies, with and without the edge test (see the dQ kernel)
-                    auto weights = [&](auto edge_c) {
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const float4 la = *(const float4*)(Ls + qbase + 16 * half);
-                        const float4 lb = *(const float4*)(Ls + qbase + 16 * half + 4);
-                        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int r = 8 * half + j;
-                            float e;
-                            if constexpr (MASK == MASK_FLOAT)
-                                e = fast_exp2(fmaf(fmaf(sc[r], p.scale, mb[r]), kLog2e, -lv[j]));
-                            else
-                                e = fast_exp2(fmaf(sc[r], c2, -lv[j]));
-                            if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
-                            if constexpr (decltype(edge_c)::value) {
-                                const int qi = qrow0 + qbase + 16 * half + j;
-                                const bool keep = qi < Lb && (!CAUSAL || qi >= my_key);
-                                e = keep ? e : 0.f;
+                            for (int r = 0; r < 16; ++r) {
+                                const int off = ((16 * (r >> 3) + 8 * hh + (r & 7)) * (int)p.m_sr + lq) * MES;
+                                if constexpr (MASK == MASK_FLOAT)
+                                    mb[r] = __uint_as_float(buf_load4(mr, off));
+                                else
+                                    mk |= (buf_load1(mr, off) != 0 ? 1u : 0u) << r;
                             }
-                            w[r] = e;
+                        }
+                        f32x16_t sc = f32x16_t{};
+                        chain_product<Tr, NKK, RS, kBatchReads>(Qs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8, kvreg, sc);
+                        // register r: query qrow0 + 32qb + 16(r/8) + 8hh + r%8, key my_key
+                        const int qbase = qb * 32 + 8 * hh;
+                        const bool edge = (qrow0 + BN > Lb) || (CAUSAL && qrow0 < wkey0 + 31);
+                        float w[16];
+                        // two copies, with and without the edge test (see the dQ kernel)
+                        auto weights = [&](auto edge_c) {
+#pragma unroll
+                            for (int half = 0; half < 2; ++half) {
+                                const float4 la = *(const float4*)(Ls + qbase + 16 * half);
+                                const float4 lb = *(const float4*)(Ls + qbase + 16 * half + 4);
+                                const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+#pragma unroll
+                                for (int j = 0; j < 8; ++j) {
+                                    const int r = 8 * half + j;
+                                    float e;
+                                    if constexpr (MASK == MASK_FLOAT)
+                                        e = fast_exp2(fmaf(fmaf(sc[r], p.scale, mb[r]), kLog2e, -lv[j]));
+                                    else
+                                        e = fast_exp2(fmaf(sc[r], c2, -lv[j]));
+                                    if constexpr (MASK == MASK_BOOL) e = ((mk >> r) & 1u) ? e : 0.f;
+                                    if constexpr (decltype(edge_c)::value) {
+                                        const int qi = qrow0 + qbase + 16 * half + j;
+                                        const bool keep = qi < Lb && (!CAUSAL || qi >= my_key);
+                                        e = keep ? e : 0.f;
+                                    }
+                                    w[r] = e;
+                                }
+                            }
+                        };
+                        if (edge)
+                            weights(std::true_type{});
+                        else
+                            weights(std::false_type{});
+                        float* pq = px_of(it & 1, qb);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *(float4*)(pq + (j * 64 + lane) * 4) = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2],
+                                                                               w[4 * j + 3]);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            pw[qb][c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
+                            pw[qb][c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
+                            pw[qb][c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
+                            pw[qb][c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
                         }
                     }
-                    };
-                    if (edge)
-                        weights(std::true_type{});
-                    else
-                        weights(std::false_type{});
-                    float* pq = px + qb * (64 * 16);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        *(float4*)(pq + (j * 64 + lane) * 4) = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2],
-                                                                           w[4 * j + 3]);
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        pw[qb][c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
-                        pw[qb][c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
-                        pw[qb][c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
-                        pw[qb][c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    dp[qb] = f32x16_t{};
-                    chain_product<Tr, NKK, RS, kBatchReads>(Gs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8, kvreg, dp[qb]);
                 }
             }
-        }
-        __syncthreads();   // P of this step is in the exchange area
-        // ---- phase 2: role 0 dV^T += dO^T P; role 1 dS = P (dP - D), dK^T += Q^T dS
-        if (active) {
+            __syncthreads();   // P of step it is in the exchange area
+            // phase B: dV^T += dO^T P of step it
+            if (it < nsteps) {
+                int h, qrow0;
+                step_coords(it, h, qrow0);
+                (void)h;
+                const uint16_t* Gs = smem + (it & 1) * STAGE + TILE;
+                if (active_at(qrow0)) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                uint4 op[2];
-                if (role == 0) {
-                    op[0] = pw[qb][0];
-                    op[1] = pw[qb][1];
-                } else {
-                    const float* pq = px + qb * (64 * 16);
-                    const int qbase = qb * 32 + 8 * hh;
-                    float w[16];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float4 e4 = *(const float4*)(pq + (j * 64 + lane) * 4);
-                        w[4 * j] = e4.x; w[4 * j + 1] = e4.y; w[4 * j + 2] = e4.z; w[4 * j + 3] = e4.w;
-                    }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const float4 da = *(const float4*)(Ls + BN + qbase + 16 * half);
-                        const float4 db4 = *(const float4*)(Ls + BN + qbase + 16 * half + 4);
-                        const float dv8[8] = {da.x, da.y, da.z, da.w, db4.x, db4.y, db4.z, db4.w};
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) w[8 * half + j] = w[8 * half + j] * (dp[qb][8 * half + j] - dv8[j]);
-                    }
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        op[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
-                        op[c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
-                        op[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
-                        op[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
-                    }
+                    for (int qb = 0; qb < 2; ++qb) transposed_products(Gs, qb, pw[qb]);
                 }
-                // over two 16-query chunks: role 0 reads dO^T, role 1 Q^T
-                const uint16_t* Xs = role == 0 ? Gs : Qs;
-                if constexpr (kBatchReads) {
-                    uint4 xa[2][NDB];   // all reads first: the products wait for the first only
+            }
+            if (it + 1 < nsteps) store_tile((it + 1) & 1);
+            __syncthreads();
+        }
+    } else {
+        f32x16_t dp[2];   // dP of the previous step, kept for its dS
+        for (int it = 0; it <= nsteps; ++it) {
+            if (it + 1 < nsteps) load_tile(it + 1);
+            // phase A: dS and dK of step it - 1
+            if (it > 0) {
+                // dS = P (dP - D) of step it - 1 (its P in the exchange area since the
+                // previous iteration, its Q, D still in their stage), dK^T += Q^T dS
+                int h, qrow0;
+                step_coords(it - 1, h, qrow0);
+                (void)h;
+                const uint16_t* Qs = smem + ((it - 1) & 1) * STAGE;
+                const float* Ls = (const float*)(Qs + 2 * TILE);
+                if (active_at(qrow0)) {
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
+                    for (int qb = 0; qb < 2; ++qb) {
+                        const float* pq = px_of((it - 1) & 1, qb);
+                        const int qbase = qb * 32 + 8 * hh;
+                        float w[16];
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db) xa[c][db] = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-                            acc[db] = Tr::mfma32(as_vec8<Tr>(xa[c][db]), as_vec8<Tr>(op[c]), acc[db]);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const uint4 xa = read_tr<RS>(Xs, qb * 2 + c, db * 32, lane);
-                            acc[db] = Tr::mfma32(as_vec8<Tr>(xa), as_vec8<Tr>(op[c]), acc[db]);
+                        for (int j = 0; j < 4; ++j) {
+                            const float4 e4 = *(const float4*)(pq + (j * 64 + lane) * 4);
+                            w[4 * j] = e4.x; w[4 * j + 1] = e4.y; w[4 * j + 2] = e4.z; w[4 * j + 3] = e4.w;
                         }
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const float4 da = *(const float4*)(Ls + BN + qbase + 16 * half);
+                            const float4 db4 = *(const float4*)(Ls + BN + qbase + 16 * half + 4);
+                            const float dv8[8] = {da.x, da.y, da.z, da.w, db4.x, db4.y, db4.z, db4.w};
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) w[8 * half + j] = w[8 * half + j] * (dp[qb][8 * half + j] - dv8[j]);
+                        }
+                        uint4 op[2];
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            op[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
+                            op[c].y = Tr::pack2(w[c * 8 + 2], w[c * 8 + 3]);
+                            op[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
+                            op[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
+                        }
+                        transposed_products(Qs, qb, op);
+                    }
                 }
             }
+            __syncthreads();   // step it - 1's stage is no longer read
+            // phase B: dP = dO V^T of step it
+            if (it < nsteps) {
+                int h, qrow0;
+                step_coords(it, h, qrow0);
+                (void)h;
+                const uint16_t* Gs = smem + (it & 1) * STAGE + TILE;
+                if (active_at(qrow0)) {
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        dp[qb] = f32x16_t{};
+                        chain_product<Tr, NKK, RS, kBatchReads>(Gs + bwd_rowpos(qb * 32 + lq) * RS + hh * 8,
+                                                                kvreg, dp[qb]);
+                    }
+                }
+            }
+            if (it + 1 < nsteps) store_tile((it + 1) & 1);
+            __syncthreads();
         }
-        if (st + 1 < nsteps) store_tile((st + 1) & 1);
-        __syncthreads();
     }
 
     // dV = dV^T or dK = scale * dK^T, rounded to nearest-even; lane: key lkey, e = 32db + 8g + 4hh + 0..3
