@@ -189,6 +189,25 @@ def test_varlen_edge_segments_and_gqa():
     assert_parity(out, lse.T, ro, rl.T, "bf16", "varlen edges + gqa")
 
 
+@pytest.mark.parametrize("n_seqs", [70, 300])
+def test_varlen_many_segments(n_seqs):
+    """Packed batches of many segments: 70 (the kernel's tile work list over two
+    chunks of 64 segments) and 300 (more than the list takes: the grid's own
+    order).  Lengths 0..300 drawn with a seeded generator, a few empty, GQA,
+    causal; every token compared."""
+    rng = np.random.default_rng(n_seqs)
+    lengths = [int(x) for x in rng.integers(0, 301, n_seqs)]
+    lengths[3] = 0
+    lengths[-1] = 300
+    q, _, _, cu = inputs.varlen_inputs(lengths, 4, 4, 64, "fp16", seed=n_seqs)
+    _, k, v, _ = inputs.varlen_inputs(lengths, 2, 2, 64, "fp16", seed=n_seqs + 1)
+    out, lse = S.sdpa_fwd_varlen(q[0].to(DEV), k[0].to(DEV), v[0].to(DEV), cu.to(DEV), is_causal=True,
+                                 enable_gqa=True)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa_varlen(q[0], k[0], v[0], cu.numpy(), is_causal=True, enable_gqa=True)
+    assert_parity(out, lse.T, ro, rl.T, "fp16", f"varlen {n_seqs} segments")
+
+
 # ------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])

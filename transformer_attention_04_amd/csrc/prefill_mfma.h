@@ -69,6 +69,62 @@ namespace sdpa {
 template <int D, int DV, bool CAUSAL, int MASK>
 constexpr int kPrefillWaves = (D <= 64 && DV <= 64 && CAUSAL && MASK == MASK_NONE) ? 3 : 2;
 
+// Packed batches (at most 4 x 64 segments): the g-th (segment, query tile)
+// of one head in the order the workgroups take them.  Tile index qt is the
+// level: every segment's tile qt_max first (segments in index order), then
+// every segment's tile qt_max - 1, and so on, so that the tiles with the most
+// key blocks start first, and the grid's workgroups past the last tile (the
+// grid holds max tiles x segments) come last, where they end at once instead
+// of holding places among the real tiles.  Each lane takes one segment of a
+// chunk of 64 (one load of its two offsets); the walk down the levels is
+// ballots and scalar counts.  Returns false when g is past the last tile;
+// else the segment, its tile and its first token and row count.
+constexpr int kPackedListMaxSegs = 256;
+__device__ __forceinline__ bool packed_tile(const AttnParams& p, int g, int& seg, int& qt, int64_t& tok0,
+                                            int& rows) {
+    const int lane = threadIdx.x & 63;
+    const int nch = (p.B + 63) / 64;
+    int nt[kPackedListMaxSegs / 64];   // tiles of this lane's segment in each chunk
+    int st[kPackedListMaxSegs / 64];   // its first token
+    int ln[kPackedListMaxSegs / 64];   // its rows
+#pragma unroll
+    for (int c = 0; c < kPackedListMaxSegs / 64; ++c) {
+        nt[c] = 0;
+        st[c] = 0;
+        ln[c] = 0;
+        const int i = c * 64 + lane;
+        if (c < nch && i < p.B) {
+            const int64_t a = min(max((int64_t)p.cu_q[i], (int64_t)0), p.total_q);
+            const int64_t e = min(max((int64_t)p.cu_q[i + 1], a), p.total_q);
+            st[c] = (int)a;
+            ln[c] = (int)min(e - a, (int64_t)p.L);
+            nt[c] = (ln[c] + kPrefillBlockM - 1) / kPrefillBlockM;
+        }
+    }
+    for (int t = p.n_qtiles - 1; t >= 0; --t) {
+#pragma unroll
+        for (int c = 0; c < kPackedListMaxSegs / 64; ++c) {
+            if (c >= nch) break;
+            const bool has = nt[c] > t;
+            const unsigned long long m = __ballot(has);
+            const int cnt = __popcll(m);
+            if (g < cnt) {
+                // the lane whose segment is the g-th set bit of m
+                const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+                const int src = __builtin_ctzll(__ballot(has && rank == g));
+                seg = c * 64 + src;
+                qt = t;
+                tok0 = __builtin_amdgcn_readlane(st[c], src);
+                rows = __builtin_amdgcn_readlane(ln[c], src);
+                return true;
+            }
+            g -= cnt;
+        }
+    }
+    return false;
+}
+
 template <typename Tr, int D, int DV, bool CAUSAL, int MASK, bool VARLEN, bool PAGED = false,
           bool PADE = false>
 __global__ __launch_bounds__(256)
@@ -97,11 +153,21 @@ void prefill_mfma_kernel(AttnParams p) {
     const int lq = lane & 31;
     const int hh = lane >> 5;
 
-    const int nbh = p.Hq * p.B;
-    const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);
-    const int bh = (int)(blockIdx.x % nbh);
-    const int h = bh % p.Hq;
-    const int b = bh / p.Hq;
+    int qt, h, b;
+    int64_t listed_a = 0;   // packed work list: the segment's first token and rows
+    int listed_rows = 0;
+    const bool listed = VARLEN && !PAGED && p.B <= kPackedListMaxSegs;
+    if (listed) {
+        // packed segments: a work list of the real tiles, the heaviest first
+        h = (int)(blockIdx.x % p.Hq);
+        if (!packed_tile(p, (int)(blockIdx.x / p.Hq), b, qt, listed_a, listed_rows)) return;
+    } else {
+        const int nbh = p.Hq * p.B;
+        qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);
+        const int bh = (int)(blockIdx.x % nbh);
+        h = bh % p.Hq;
+        b = bh / p.Hq;
+    }
     const int kvh = h / p.group;
 
     int Lb, Sb;
@@ -118,8 +184,8 @@ void prefill_mfma_kernel(AttnParams p) {
         oo = a * p.o_sr + (int64_t)h * p.o_sh;
         lo = (int64_t)h * p.lse_sh + a;
     } else if (VARLEN) {
-        const int64_t a = min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
-        const int64_t e = min(max((int64_t)p.cu_q[b + 1], a), p.total_q);
+        const int64_t a = listed ? listed_a : min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
+        const int64_t e = listed ? a + listed_rows : min(max((int64_t)p.cu_q[b + 1], a), p.total_q);
         const int64_t c = min(max((int64_t)p.cu_k[b], (int64_t)0), p.total_k);
         const int64_t d = min(max((int64_t)p.cu_k[b + 1], c), p.total_k);
         Lb = (int)min(e - a, (int64_t)p.L);
