@@ -8,9 +8,11 @@
 // share one row and each holds a quarter of its head dim, in 4-float runs
 // interleaved with period 16.  A score is therefore 16 partial dot products
 // (4 per lane) combined in a fixed tree, which keeps the rounding error of
-// the E-long dot product well below that of one sequential FMA chain.  Keys
-// and values stream through LDS 32 rows at a time.  The running max is kept
-// in logit units and subtracted before multiplying by log2(e).
+// the E-long dot product well below that of one sequential FMA chain (the
+// four lanes of a row combine theirs with quad DPP moves).  Keys and values
+// stream through LDS 32 rows at a time, the next block's loads in flight in
+// registers while a block is computed.  The running max is kept in logit
+// units and subtracted before multiplying by log2(e).
 //
 // Padded instances (PADE): head dims E and Ev that are multiples of 8 up to 128
 // (E = 0 included) run at a width D of 64 or 128: columns of Q and K from E on,
@@ -86,18 +88,35 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
     const float* vp = (const float*)p.v + vo;
 
     float m_run = kNegInf, l_run = 0.f;
-    for (int key0 = 0; key0 < kend; key0 += BN) {
-        for (int c = tid; c < NCH; c += 256) {
+    // the next block's keys and values travel in registers while this block
+    // is computed (NCH / 256 chunks of each per lane)
+    constexpr int NCT = (NCH + 255) / 256;
+    float4 kb[NCT], vb[NCT];
+    auto load_block = [&](int key0) {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) {
+            const int c = tid + 256 * i;
             const int r = c / (D / 4), col = (c % (D / 4)) * 4;
-            const bool in = key0 + r < Sb;
+            const bool in = c < NCH && key0 + r < Sb;
             const bool kin = in && (!PADE || col < p.e);
             const bool vin = in && (!PADE || col < p.dv);
-            *(float4*)(Ks + r * RS + col) =
-                kin ? *(const float4*)(kp + (int64_t)(key0 + r) * p.k_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-            *(float4*)(Vs + r * RS + col) =
-                vin ? *(const float4*)(vp + (int64_t)(key0 + r) * p.v_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+            kb[i] = kin ? *(const float4*)(kp + (int64_t)(key0 + r) * p.k_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+            vb[i] = vin ? *(const float4*)(vp + (int64_t)(key0 + r) * p.v_sr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    if (kend > 0) load_block(0);
+    for (int key0 = 0; key0 < kend; key0 += BN) {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) {
+            const int c = tid + 256 * i;
+            if (c < NCH) {
+                const int r = c / (D / 4), col = (c % (D / 4)) * 4;
+                *(float4*)(Ks + r * RS + col) = kb[i];
+                *(float4*)(Vs + r * RS + col) = vb[i];
+            }
         }
         __syncthreads();
+        if (key0 + BN < kend) load_block(key0 + BN);
         float lg[BN];
 #pragma unroll
         for (int j = 0; j < BN; ++j) {
@@ -110,9 +129,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnParams p) {
                 a2 = fmaf(qv[i].z, kv.z, a2);
                 a3 = fmaf(qv[i].w, kv.w, a3);
             }
+            // the four lanes of a row exchange partial sums within their quad
+            // (DPP quad permutations [1,0,3,2] and [2,3,0,1]); every lane ends
+            // with the same (p0 + p1) + (p2 + p3)
             float sc = (a0 + a1) + (a2 + a3);
-            sc += __shfl_xor(sc, 1, 64);
-            sc += __shfl_xor(sc, 2, 64);
+            sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0xB1, 0xF, 0xF, false));
+            sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x4E, 0xF, 0xF, false));
             const int key = key0 + j;
             float x;
             if (MASK == MASK_FLOAT)
