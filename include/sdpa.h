@@ -297,8 +297,10 @@ sdpa_status sdpa_fwd_paged_varlen(sdpa_dtype dtype, const void* q, int64_t q_str
  * recomputed from q, k and the forward's lse; D from the forward output
  * (D_i = dout_i . out_i, the definition's sum up to the rounding of out).
  *
- *   dtype      SDPA_BF16 or SDPA_F16 (SDPA_F32 returns SDPA_ERR_UNSUPPORTED).
- *   q, k, v    as for sdpa_fwd; E == Ev in {64, 96, 128}.
+ *   dtype      SDPA_BF16, SDPA_F16 or SDPA_F32.
+ *   q, k, v    as for sdpa_fwd (head dims E and Ev multiples of 8 up to 128).
+ *              bf16/fp16 with E == Ev in {64, 96, 128} run the matrix-core
+ *              kernels; every other call the vector-ALU ones (fp32 arithmetic).
  *   attn_mask, mask_dtype
  *              as for sdpa_fwd (NULL, or a float32 bias / bool keep mask
  *              broadcastable to (B, Hq, L, S), key stride 1).  The mask gets
@@ -313,8 +315,14 @@ sdpa_status sdpa_fwd_paged_varlen(sdpa_dtype dtype, const void* q, int64_t q_str
  *              written completely (rows no query reaches get 0), rounded to
  *              nearest-even.  They must not alias any input.
  *   workspace, workspace_bytes
- *              device scratch of at least sdpa_bwd_workspace_size() bytes,
- *              owned by the caller (the per-row D in float32).
+ *              device scratch owned by the caller, of at least
+ *              B * Hq * L * 4 + 256 bytes (the per-row D in float32).  With
+ *              sdpa_bwd_workspace_size() bytes, where that size also holds a
+ *              16-bit dS^T of B * Hq * S * (L rounded up to 128) elements
+ *              (matrix-core calls, at most 2 GiB of it), the dK/dV kernel
+ *              stores dS and dq = scale dS K takes one matrix product per
+ *              (query, key) pair; with less, dq recomputes S and dP (three
+ *              products).  Both give the same values.
  *   stream     hipStream_t or NULL; the call is asynchronous on it.
  *
  * Errors as for sdpa_fwd: argument problems are found on the host before any
@@ -373,8 +381,11 @@ sdpa_status sdpa_bwd_varlen(sdpa_dtype dtype, const void* q, int64_t q_stride_to
 sdpa_status sdpa_bwd_varlen_workspace_size(int32_t Hq, int64_t total_q, size_t* bytes);
 
 /*
- * sdpa_bwd_workspace_size -- bytes of workspace sdpa_bwd needs for these
- * shapes (B * Hq * L float32 values, plus alignment).  Host only.
+ * sdpa_bwd_workspace_size -- bytes of workspace for sdpa_bwd's faster
+ * schedule on these shapes: B * Hq * L float32 values plus alignment, and for
+ * matrix-core calls whose dS^T takes at most 2 GiB, that dS^T buffer too
+ * (sdpa_bwd runs the recomputing schedule when given less, down to
+ * B * Hq * L * 4 + 256 bytes).  Host only.
  */
 sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype,
                                     const sdpa_tensor4* q, const sdpa_tensor4* k,

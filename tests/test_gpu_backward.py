@@ -188,6 +188,32 @@ def test_backward_headline_shape_full():
         list(ex.map(per_element, [(0, 0), (3, 15)]))
 
 
+@pytest.mark.parametrize("dtype,E", [("fp16", 64), ("bf16", 96), ("bf16", 128)])
+def test_backward_schedules_agree(dtype, E):
+    """The schedule that stores dS^T (dQ from it in one product) and the one whose
+    dQ kernel recomputes S and dP give bit-identical gradients: both form the same
+    P, dP, D and dS, and add dQ's products in the same order (the stored schedule
+    only adds exact zeros past a slice's causal limit).  Ragged lengths (not
+    multiples of 64 or 128), causal or not, grouped heads, float and bool masks."""
+    cases = [(2, 4, 2, 200, 333, False, None), (1, 4, 4, 300, 300, True, None), (1, 2, 1, 65, 129, True, None),
+             (2, 2, 2, 150, 150, True, "float"), (1, 2, 2, 257, 190, False, "bool")]
+    for ci, (B, Hq, Hkv, L, Sk, causal, mk) in enumerate(cases):
+        q, k, v = inputs.randn_qkv((B, Hq, L, E), (B, Hkv, Sk, E), (B, Hkv, Sk, E), dtype, seed=ci + E)
+        g = inputs.randn_qkv((B, Hq, L, E), (1, 1, 1, E), (1, 1, 1, E), dtype, seed=ci + E + 50)[0]
+        m = None
+        if mk is not None:
+            m = _masks((B, Hq, L, Sk), seed=ci)[0 if mk == "float" else 1]
+        qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+        md = None if m is None else m.to(DEV)
+        out, lse = S.sdpa_fwd(qd, kd, vd, attn_mask=md, is_causal=causal, enable_gqa=True)
+        a = S.sdpa_bwd(qd, kd, vd, out, lse, gd, attn_mask=md, is_causal=causal, enable_gqa=True, store_ds=True)
+        b = S.sdpa_bwd(qd, kd, vd, out, lse, gd, attn_mask=md, is_causal=causal, enable_gqa=True, store_ds=False)
+        torch.cuda.synchronize()
+        for n, x, y in zip(("dq", "dk", "dv"), a, b):
+            assert torch.equal(x, y), (f"case {ci} {n}: schedules differ, max "
+                                       f"{float((x.float() - y.float()).abs().max()):.3e}")
+
+
 def _masks(shape, seed):
     g = torch.Generator().manual_seed(seed)
     fm = torch.randn(shape, generator=g)

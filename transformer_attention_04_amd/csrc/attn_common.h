@@ -136,6 +136,14 @@ struct BwdParams {
     const int* cu_k;
     int64_t total_q, total_k;
     int e, ev;      // head dims of query/key rows and value rows
+    // Optional dS^T store (batched calls, matrix-core kernels), 16-bit, in
+    // panels of 128 queries: element (b, h, key j, query i) at
+    // ((b * Hq + h) * ds_lp + (i & ~127)) * S + j * 128 + (i & 127), ds_lp a
+    // multiple of 128 covering L, so 64 keys of one panel are 16 contiguous
+    // KB.  Non-null: the dK/dV kernel writes dS there (zeros where no key is
+    // kept) and dQ = scale dS K is formed from it.
+    uint16_t* ds;
+    int64_t ds_lp;
 };
 
 hipError_t launch_prefill_bf16(const AttnParams& p, int D, bool causal, int mask, bool varlen,

@@ -94,6 +94,68 @@ __device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int c, int col0, 
 
 // ------------------------------------------------------------- D = dO . O
 
+// D_i = dO_i . O_i in fp32 for every query row of a batched call (the
+// schedule that stores dS needs it before the dK/dV kernel).  The same
+// arithmetic as the dQ kernel's own D: each half of a 32-lane pair takes
+// elements 16kk + 8hh .. +7 of its row in order, products accumulated by
+// fmaf, the two halves added; so both schedules see the same D.  The 128 rows
+// of O and dO travel to LDS first with whole rows per load instruction (a
+// lane-per-row load would touch 32 rows per instruction).
+template <typename Tr, int D>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdParams p) {
+    constexpr int NKK = D / 16;
+    constexpr int RW = D + 8;              // LDS row stride, 16-bit words
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int NCH_T = 128 * CPR / 256; // chunks per thread and tensor
+    static_assert(128 * CPR % 256 == 0, "chunks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t so[128 * RW];
+    __shared__ __attribute__((aligned(16))) uint16_t sg[128 * RW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hh = lane >> 5;
+    const int nbh = p.Hq * p.B;
+    const int qt = (int)(blockIdx.x / nbh), bh = (int)(blockIdx.x % nbh);
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int q0 = qt * 128;
+    if (q0 >= p.L) return;
+    const int qrows = min(128, p.L - q0);
+    const int lrow = wave * 32 + lq;
+    const int o_rs = (int)(p.o_sr * 2), do_rs = (int)(p.do_sr * 2);
+    const auto ors = make_rsrc((const uint16_t*)p.o + (int64_t)b * p.o_sb + h * p.o_sh + (int64_t)q0 * p.o_sr,
+                               (qrows - 1) * o_rs + D * 2);
+    const auto grs = make_rsrc((const uint16_t*)p.dout + (int64_t)b * p.do_sb + h * p.do_sh + (int64_t)q0 * p.do_sr,
+                               (qrows - 1) * do_rs + D * 2);
+    uint4 ov[NCH_T], gv[NCH_T];
+#pragma unroll
+    for (int i = 0; i < NCH_T; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, col = (c % CPR) * 8;
+        ov[i] = buf_load16(ors, r * o_rs + col * 2);   // rows past the last read 0
+        gv[i] = buf_load16(grs, r * do_rs + col * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH_T; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, col = (c % CPR) * 8;
+        *(uint4*)(so + r * RW + col) = ov[i];
+        *(uint4*)(sg + r * RW + col) = gv[i];
+    }
+    __syncthreads();
+    float dpart = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const uint4 o = *(const uint4*)(so + lrow * RW + kk * 16 + hh * 8);
+        const uint4 g = *(const uint4*)(sg + lrow * RW + kk * 16 + hh * 8);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dpart = fmaf(Tr::to_f32(ow[j] & 0xffffu), Tr::to_f32(gw[j] & 0xffffu), dpart);
+            dpart = fmaf(Tr::to_f32(ow[j] >> 16), Tr::to_f32(gw[j] >> 16), dpart);
+        }
+    }
+    const float dfull = pair32_sum(dpart);  // every lane takes part in the exchange
+    if (lrow < qrows && hh == 0) p.dsum[((int64_t)b * p.Hq + h) * p.L + q0 + lrow] = dfull;
+}
+
+
 // ------------------------------------------------------------------- dQ
 
 // Mask values of 8 consecutive keys starting at byte offset off of a
@@ -393,6 +455,157 @@ void bwd_dq_kernel(BwdParams p) {
         }
 }
 
+// ---------------------------------------------------------- dQ from dS^T
+
+// dQ = scale dS K for batched calls whose dK/dV kernel stored dS^T (one
+// workgroup per 128 query rows, 4 wavefronts x 32 rows): per 64-key block, K
+// and the block's dS^T rows (keys) x 128 query columns (16 contiguous KB of
+// the query tile's panel) travel to LDS through registers, and dQ^T += K^T
+// dS^T with both operands read transposed by ds_read_b64_tr_b16: one matrix
+// product per (query, key) pair where the recomputing dQ kernel needs three
+// (S, dP and this one).  The kernel moves more bytes per product than it
+// computes, so the loads run two blocks ahead (two register sets, used in
+// turn), which keeps twice as many bytes in flight as a one-block prefetch.
+// dS^T is stored for every key block up to the causal limit of a 128-row tile
+// (zeros where no key is kept), so no mask, scale or softmax work is left.
+template <typename Tr, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_ds_kernel(BwdParams p) {
+    constexpr int BM = 128, BN = 64;
+    constexpr int RS = D + 8;            // K tile row stride, 16-bit words
+    constexpr int RQ = BM + 8;           // dS^T tile row stride
+    constexpr int KTILE = BN * RS, STILE = BN * RQ;
+    constexpr int STAGE = KTILE + STILE;
+    constexpr int NDB = D / 32;
+    constexpr int KCH_T = BN * D / 8 / 256;   // 16-byte K chunks per thread
+    constexpr int SCH_T = BN * BM / 8 / 256;  // 16-byte dS^T chunks per thread
+    static_assert(BN * D / 8 % 256 == 0 && BN * BM / 8 % 256 == 0, "chunks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hh = lane >> 5;
+    const int nbh = p.Hq * p.B;
+    const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);  // heaviest (causal) first
+    const int bh = (int)(blockIdx.x % nbh);
+    const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.group;
+    const int q0 = qt * BM;
+    if (q0 >= p.L) return;
+    const int qrows = min(BM, p.L - q0);
+    const int kend = CAUSAL ? min(p.S, q0 + BM) : p.S;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    const uint16_t* sbase = p.ds + (((int64_t)b * p.Hq + h) * p.ds_lp + q0) * p.S;  // panel of q0
+    const int k_rs = (int)(p.k_sr * 2);
+    struct Tile {
+        uint4 k[KCH_T], s[SCH_T];
+    };
+    // block t into registers; a block past the last has empty ranges (its
+    // loads read nothing), so every step issues the same loads
+    auto load_tile = [&](int t, Tile& r) {
+        const int key0 = t < ntiles ? t * BN : 0;
+        const int rows = t < ntiles ? min(BN, p.S - key0) : 0;
+        const auto kr = make_rsrc(kbase + (int64_t)key0 * p.k_sr, rows > 0 ? (rows - 1) * k_rs + D * 2 : 0);
+        const auto sr = make_rsrc(sbase + (int64_t)key0 * BM, rows * BM * 2);
+#pragma unroll
+        for (int i = 0; i < KCH_T; ++i) {
+            const int c = tid + 256 * i, rr = c / (D / 8), col = (c % (D / 8)) * 8;
+            r.k[i] = buf_load16(kr, rr * k_rs + col * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < SCH_T; ++i) r.s[i] = buf_load16_nt(sr, (tid + 256 * i) * 16);
+    };
+    auto store_tile = [&](int stage, const Tile& r) {
+        uint16_t* Ks = smem + stage * STAGE;
+        uint16_t* Ds = Ks + KTILE;
+#pragma unroll
+        for (int i = 0; i < KCH_T; ++i) {
+            const int c = tid + 256 * i, rr = c / (D / 8), col = (c % (D / 8)) * 8;
+            *(uint4*)(Ks + bwd_pos(rr) * RS + col) = r.k[i];
+        }
+#pragma unroll
+        for (int i = 0; i < SCH_T; ++i) {
+            const int c = tid + 256 * i, rr = c / (BM / 8), col = (c % (BM / 8)) * 8;
+            *(uint4*)(Ds + bwd_pos(rr) * RQ + col) = r.s[i];
+        }
+    };
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+    // Transposed operand reads (as read_tr): lane (i = l & 15, g, hh) reads
+    // 4 rows from tile row rowpos(16c + 4hh + i / 4) (and two rows further),
+    // column col0 + 16g + 4(i & 3).  Per lane only a base address varies; the
+    // stage, chunk, column block and second read are immediate offsets.
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const int ri = lane & 15, rg = (lane >> 4) & 1;
+    const int rrow = 4 * (ri >> 2) + hh, rcol = 16 * rg + 4 * (ri & 3);
+    lds_char* const kb = (lds_char*)(uintptr_t)(uint32_t)(uintptr_t)(smem + rrow * RS + rcol);
+    lds_char* const sb = (lds_char*)(uintptr_t)(uint32_t)(uintptr_t)(smem + KTILE + rrow * RQ + wave * 32 + rcol);
+    auto tr_pair = [](lds_char* at, int rs_bytes) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)at);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + 2 * rs_bytes));
+        uint4 u;
+        u.x = __builtin_bit_cast(uint2, lo).x;
+        u.y = __builtin_bit_cast(uint2, lo).y;
+        u.z = __builtin_bit_cast(uint2, hi).x;
+        u.w = __builtin_bit_cast(uint2, hi).y;
+        return u;
+    };
+    // dQ^T (rows e, columns queries) += K^T dS^T over the block's 4 key chunks
+    auto products = [&](auto stage_c) {
+        constexpr int so = decltype(stage_c)::value * STAGE * 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint4 a[NDB];
+            const uint4 bop = tr_pair(sb + so + 16 * c * RQ * 2, RQ * 2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) a[db] = tr_pair(kb + so + (16 * c * RS + 32 * db) * 2, RS * 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma32(as_vec8<Tr>(a[db]), as_vec8<Tr>(bop), acc[db]);
+        }
+    };
+    // Block t sits in stage t & 1; registers ta hold even blocks, tb odd ones.
+    // Each step issues the loads of block t + 2 before its products and stores
+    // block t + 1 (loaded a step earlier) after them; a stage is rewritten only
+    // after the barrier that ends the step which read it.
+    Tile ta, tb;
+    load_tile(0, ta);
+    load_tile(1, tb);
+    store_tile(0, ta);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        load_tile(t + 2, ta);
+        products(std::integral_constant<int, 0>{});
+        store_tile(1, tb);
+        __syncthreads();
+        if (t + 1 >= ntiles) break;
+        load_tile(t + 3, tb);
+        products(std::integral_constant<int, 1>{});
+        store_tile(0, ta);
+        __syncthreads();
+    }
+
+    // dQ = scale * dQ^T, rounded to nearest-even; lane: query lrow, e = 32db + 8g + 4hh + 0..3
+    const int lrow = wave * 32 + lq;
+    const int dq_rs = (int)(p.dq_sr * 2);
+    const auto ors = make_rsrc((uint16_t*)p.dq + (int64_t)b * p.dq_sb + h * p.dq_sh + (int64_t)q0 * p.dq_sr,
+                               (qrows - 1) * dq_rs + D * 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + hh * 4;
+            uint2 st;
+            st.x = Tr::pack2(acc[db][4 * g + 0] * p.scale, acc[db][4 * g + 1] * p.scale);
+            st.y = Tr::pack2(acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+            buf_store8(st, ors, lrow * dq_rs + d * 2);
+        }
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 // x += sum over kk of A_kk B_kk, with A_kk the 16-byte LDS read at row + 16 kk
@@ -551,6 +764,17 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto active_at = [&](int qrow0) { return wave_has_keys && (!CAUSAL || qrow0 + BN - 1 >= wkey0); };
     // acc += X^T op over the two 16-query chunks of query half qb: X = dO (role
     // 0, op = P) or Q (role 1, op = dS), read transposed from the stage at Xs
+    // dS^T of this workgroup's keys, when the call keeps it (batched calls):
+    // lane (key lkey, queries qrow0 + 32qb + 16c + 8hh + 0..7) stores 16 bytes
+    // per chunk c into the 128-query panel of qrow0; keys past the last, and
+    // every store when keep is false, are dropped by the buffer range
+    auto store_ds = [&](bool keep, int h, int qrow0, int qb, const uint4* op) {
+        const auto r = make_rsrc(keep ? p.ds + (((int64_t)b * p.Hq + h) * p.ds_lp + (qrow0 & ~127)) * p.S + (int64_t)k0 * 128
+                                      : p.ds,
+                                 keep ? krows * 256 : 0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) buf_store16_nt(op[c], r, (lkey * 128 + (qrow0 & 127) + 32 * qb + 16 * c + 8 * hh) * 2);
+    };
     auto transposed_products = [&](const uint16_t* Xs, int qb, const uint4* op) {
         uint4 xa[2][NDB];   // all reads first: the products wait for the first only
 #pragma unroll
@@ -678,18 +902,25 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int it = 0; it <= nsteps; ++it) {
             if (it + 1 < nsteps) load_tile(it + 1);
             // phase A: dS and dK of step it - 1
-            if (it > 0) {
+            {
                 // dS = P (dP - D) of step it - 1 (its P in the exchange area since the
-                // previous iteration, its Q, D still in their stage), dK^T += Q^T dS
+                // previous iteration, its Q, D still in their stage), dK^T += Q^T dS.
+                // The dS^T stores are issued on every iteration (an empty range when
+                // nothing is kept, zeros for a slice with no kept key), so the number
+                // of memory operations after the next tile's loads is the same on
+                // every path and the wait for those loads leaves the stores in flight.
+                const int st = it > 0 ? it - 1 : 0;
                 int h, qrow0;
-                step_coords(it - 1, h, qrow0);
-                (void)h;
-                const uint16_t* Qs = smem + ((it - 1) & 1) * STAGE;
+                step_coords(st, h, qrow0);
+                const uint16_t* Qs = smem + (st & 1) * STAGE;
                 const float* Ls = (const float*)(Qs + 2 * TILE);
-                if (active_at(qrow0)) {
+                const bool act = it > 0 && active_at(qrow0);
+                const bool keep_ds = !VARLEN && it > 0 && p.ds != nullptr;
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        const float* pq = px_of((it - 1) & 1, qb);
+                for (int qb = 0; qb < 2; ++qb) {
+                    uint4 op[2] = {zero4(), zero4()};
+                    if (act) {
+                        const float* pq = px_of(st & 1, qb);
                         const int qbase = qb * 32 + 8 * hh;
                         float w[16];
 #pragma unroll
@@ -705,7 +936,6 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                             for (int j = 0; j < 8; ++j) w[8 * half + j] = w[8 * half + j] * (dp[qb][8 * half + j] - dv8[j]);
                         }
-                        uint4 op[2];
 #pragma unroll
                         for (int c = 0; c < 2; ++c) {
                             op[c].x = Tr::pack2(w[c * 8 + 0], w[c * 8 + 1]);
@@ -713,8 +943,9 @@ void bwd_dkdv_kernel(BwdParams p) {
                             op[c].z = Tr::pack2(w[c * 8 + 4], w[c * 8 + 5]);
                             op[c].w = Tr::pack2(w[c * 8 + 6], w[c * 8 + 7]);
                         }
-                        transposed_products(Qs, qb, op);
                     }
+                    if constexpr (!VARLEN) store_ds(keep_ds, h, qrow0, qb, op);
+                    if (act) transposed_products(Qs, qb, op);
                 }
             }
             __syncthreads();   // step it - 1's stage is no longer read
@@ -760,14 +991,22 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 template <typename Tr, int D, bool CAUSAL, int MASK, bool VARLEN>
 void launch_bwd_grads(const BwdParams& p, hipStream_t s) {
-    if ((int64_t)p.B * p.Hq * p.L > 0) {
-        const unsigned g = (unsigned)p.n_qtiles * p.Hq * p.B;
-        hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(g), dim3(256), 0, s, p);
+    const unsigned gq = (unsigned)p.n_qtiles * p.Hq * p.B;
+    const unsigned gk = (unsigned)p.n_ktiles * p.Hkv * p.B;
+    if (!VARLEN && p.ds) {
+        // D, then dK/dV (storing dS^T), then dQ from dS^T
+        if ((int64_t)p.B * p.Hq * p.L > 0)
+            hipLaunchKernelGGL((bwd_dsum_kernel<Tr, D>), dim3(gq), dim3(256), 0, s, p);
+        if ((int64_t)p.S * p.Hkv * p.B > 0)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(gk), dim3(512), 0, s, p);
+        if ((int64_t)p.B * p.Hq * p.L > 0)
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<Tr, D, CAUSAL>), dim3(gq), dim3(256), 0, s, p);
+        return;
     }
-    if ((int64_t)p.S * p.Hkv * p.B > 0) {
-        const unsigned g = (unsigned)p.n_ktiles * p.Hkv * p.B;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(g), dim3(512), 0, s, p);
-    }
+    if ((int64_t)p.B * p.Hq * p.L > 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(gq), dim3(256), 0, s, p);
+    if ((int64_t)p.S * p.Hkv * p.B > 0)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<Tr, D, CAUSAL, MASK, VARLEN>), dim3(gk), dim3(512), 0, s, p);
 }
 
 template <typename Tr, int D, int MASK, bool VARLEN = false>

@@ -147,5 +147,21 @@ __device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r, in
 __device__ __forceinline__ void buf_store4(float v, __amdgpu_buffer_rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
+// Streaming variants for data written once and read once much later (the
+// non-temporal cache policy, bit 1 of the policy operand): such lines are the
+// first the caches give up, so they do not push out data that is reused.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buf_store16_nt(uint4 v, __amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, kCachePolicyNT);
+}
 
 }  // namespace sdpa

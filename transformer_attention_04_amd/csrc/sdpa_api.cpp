@@ -208,6 +208,25 @@ hipError_t launch_single_pass(sdpa_dtype dtype, const sdpa::AttnParams& p, int D
 
 size_t bwd_workspace_bytes(const Shapes& s) { return (size_t)(s.B * s.Hq * s.L) * sizeof(float) + 256; }
 
+// The dS^T buffer of the backward schedule that stores dS (batched
+// matrix-core calls): 16-bit (b, h, key, query), rows padded to a multiple of
+// 128 queries.  0 when that schedule does not apply (vector-ALU calls, no
+// rows or keys, or more than kBwdDsMaxBytes).
+constexpr double kBwdDsMaxBytes = 2.0 * 1024 * 1024 * 1024;
+int64_t bwd_ds_row(const Shapes& s) { return (s.L + 127) / 128 * 128; }
+size_t bwd_ds_bytes(sdpa_dtype dtype, const Shapes& s) {
+    if (!matrix_core_backward(dtype, s.E, s.Ev)) return 0;
+    const double bytes = (double)s.B * (double)s.Hq * (double)s.S * (double)bwd_ds_row(s) * 2.0;
+    if (bytes <= 0 || bytes > kBwdDsMaxBytes) return 0;
+    return (size_t)bytes;
+}
+// D values (aligned to 256 bytes), then the dS^T buffer (256-byte aligned)
+size_t bwd_ds_offset(const Shapes& s) { return ((size_t)(s.B * s.Hq * s.L) * sizeof(float) + 255) / 256 * 256; }
+size_t bwd_full_workspace_bytes(sdpa_dtype dtype, const Shapes& s) {
+    const size_t ds = bwd_ds_bytes(dtype, s);
+    return ds ? 256 + bwd_ds_offset(s) + ds : bwd_workspace_bytes(s);
+}
+
 // Shapes and launch plan of a paged-cache call (host only).
 struct PagedPlan {
     int64_t B, Hq, Hkv, L, E, Ev, n_pages, page_size;
@@ -708,7 +727,7 @@ sdpa_status sdpa_bwd_workspace_size(sdpa_dtype dtype, const sdpa_tensor4* q, con
     Shapes s;
     sdpa_status st = check_shapes(dtype, q, k, v, nullptr, enable_gqa, &s);
     if (st != SDPA_OK) return st;
-    *bytes = bwd_workspace_bytes(s);
+    *bytes = bwd_full_workspace_bytes(dtype, s);
     return ok();
 }
 
@@ -768,6 +787,13 @@ sdpa_status sdpa_bwd(sdpa_dtype dtype, const sdpa_tensor4* q, const sdpa_tensor4
     p.q = q->data; p.k = k->data; p.v = v->data; p.o = out->data; p.dout = dout->data;
     p.lse = (const float*)lse->data;
     p.dsum = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    // a workspace of sdpa_bwd_workspace_size bytes also holds dS^T: the
+    // schedule with one matrix product for dQ; a smaller one: dQ recomputes
+    // S and dP
+    if (bwd_ds_bytes(dtype, s) > 0 && workspace_bytes >= bwd_full_workspace_bytes(dtype, s)) {
+        p.ds = (uint16_t*)((char*)p.dsum + bwd_ds_offset(s));
+        p.ds_lp = bwd_ds_row(s);
+    }
     p.dq = dq->data; p.dk = dk->data; p.dv = dv->data;
     p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sr = q->stride[2];
     p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sr = k->stride[2];

@@ -370,7 +370,7 @@ def sdpa_bwd_workspace_size(query, key, value, enable_gqa=False):
 
 
 def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False, scale=None,
-             enable_gqa=False, workspace=None, grads=None):
+             enable_gqa=False, workspace=None, grads=None, store_ds=True):
     """Gradients of exact attention on the GPU: returns (grad_query, grad_key, grad_value).
 
     ``out`` and ``lse`` are sdpa_fwd's results for the same arguments (the
@@ -378,7 +378,9 @@ def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False,
     with respect to ``out`` (exactref.ai "scaled_dot_product_attention.backward";
     the mask gets no gradient).  The outputs have the shapes and dtype of
     query, key and value; ``grads`` may pass them in as a tuple of contiguous
-    tensors (written in place).
+    tensors (written in place).  ``store_ds=False`` hands the library only the
+    workspace of the D values, so that dQ recomputes S and dP instead of reading
+    the stored dS^T (the same values either way).
     """
     lib = load_library()
     _require_gpu(query, key, value, out, lse, grad, attn_mask)
@@ -405,7 +407,7 @@ def sdpa_bwd(query, key, value, out, lse, grad, attn_mask=None, is_causal=False,
             if tuple(t.shape) != shp or t.dtype != query.dtype or not t.is_contiguous() or t.device != dev:
                 raise ValueError(f"grads must be contiguous {query.dtype} tensors of shapes {want}")
     with torch.cuda.device(dev):
-        nbytes = sdpa_bwd_workspace_size(q4, k4, v4, enable_gqa)
+        nbytes = sdpa_bwd_workspace_size(q4, k4, v4, enable_gqa) if store_ds else B * Hq * L * 4 + 256
         if workspace is None or workspace.numel() < nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _check(lib.sdpa_bwd(_DTYPE[query.dtype], _desc(q4), _desc(k4), _desc(v4),
