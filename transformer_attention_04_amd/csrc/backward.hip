@@ -9,29 +9,42 @@
 // definition's sum up to the rounding of O), as the blocked algorithm on the
 // khchao.com NN Lab page keeps only O(N) state per row.
 //
-// Two kernels:
-//   bwd_dq_kernel     one workgroup per 128 query rows (4 wavefronts x 32);
-//                     first D_i = dO_i . O_i in fp32 from the dO rows it holds
-//                     and the O rows in the same layout (written to the
-//                     workspace for the second kernel, which runs after it);
-//                     for each 64-key block, S^T = K Q^T and dP^T = V dO^T on
-//                     the matrix cores (the transposed score layout of the
-//                     forward kernels, one query per lane), P^T and dS^T in
-//                     registers, then dQ^T += K^T dS^T with dS^T as the B
-//                     operand straight from the score registers and K^T read
-//                     from LDS with the transposing ds_read_b64_tr_b16.
+// Two schedules, chosen by the workspace the caller hands in:
+//
+// Stored dS (batched calls given the full workspace), three kernels:
+//   bwd_dsum_kernel   D_i = dO_i . O_i in fp32 for every query row.
 //   bwd_dkdv_kernel   one workgroup per 128 keys, over the query heads of the
 //                     key/value head and their 64-row query blocks, with two
 //                     roles per 32-key slice, sharing a SIMD: one wavefront
 //                     computes S = Q K^T (one key per lane) and P, hands P to
 //                     the other through LDS and accumulates dV^T += dO^T P;
 //                     the other computes dP = dO V^T, then dS = P (dP - D) and
-//                     dK^T += Q^T dS.  P and dS are B operands from registers,
-//                     dO^T and Q^T are read transposed from LDS.
-// No atomics: each gradient element has one owner.  The price is that S and
-// dP are computed twice (once per kernel), 7 matrix products per kept (query,
-// key) pair and head dimension instead of the 5 of one shared pass; in
-// exchange every wavefront fits in 256 registers (two per SIMD).
+//                     dK^T += Q^T dS, and writes dS^T to the workspace in the
+//                     16-bit input format.  P and dS are B operands from
+//                     registers, dO^T and Q^T are read transposed from LDS.
+//   bwd_dq_ds_kernel  one workgroup per 128 query rows: dQ^T += K^T dS^T from
+//                     the stored dS^T, one matrix product per kept pair.
+//   Four products in the dK/dV kernel and one in the dQ kernel: the 5 of the
+//   definition (S, dP, dV, dK, dQ) per kept (query, key) pair and head
+//   dimension, at the price of writing and reading dS^T once.
+//
+// Recomputed dS (packed batches, or a workspace holding only D), two kernels:
+//   bwd_dq_kernel     one workgroup per 128 query rows (4 wavefronts x 32);
+//                     first D_i = dO_i . O_i from the dO rows it holds and the
+//                     O rows in the same layout (written to the workspace for
+//                     the second kernel, which runs after it); for each 64-key
+//                     block, S^T = K Q^T and dP^T = V dO^T on the matrix cores
+//                     (the transposed score layout of the forward kernels, one
+//                     query per lane), P^T and dS^T in registers, then
+//                     dQ^T += K^T dS^T with dS^T as the B operand straight from
+//                     the score registers and K^T read from LDS with the
+//                     transposing ds_read_b64_tr_b16.
+//   bwd_dkdv_kernel   as above, without the dS^T stores.
+//   S and dP are then computed twice (once per kernel), 7 products per kept
+//   pair and head dimension.
+// Both schedules compute D, P and dS with the same arithmetic, so they give
+// bit-identical gradients.  No atomics: each gradient element has one owner,
+// and every wavefront fits in 256 registers (two per SIMD).
 //
 // Optional masks, as in the forward: a float32 bias enters the logit as
 // scale * s + bias, a bool mask sets P = 0 on the keys it drops; the dQ kernel
