@@ -365,8 +365,12 @@ def main(argv=None):
         main_res = bench_prefill("bf16_causal_e128", a.steps, a.warmup)
         print(f"# bf16_causal_e128: {main_res['kernel_ms'] * 1e3:.1f} us/launch, "
               f"{main_res['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # Warm-up calls of each secondary line: enough for the clocks to settle
+    # after the host-side set-up between lines (a 1 GiB mask upload, say); with
+    # 5, the first timed calls of the ALiBi and backward lines ran 10-15% slow.
+    sw = max(5, min(a.warmup, 40))
     if run_all or "decode" in sel:
-        d = bench_decode(max(5, a.steps // 2), min(a.warmup, 5))
+        d = bench_decode(max(5, a.steps // 2), sw)
         secondary["bf16_gqa_decode"] = {"metric": "GB/s", "value": round(d["gbs"], 1),
                                         "frac_hbm_peak": round(d["frac_hbm"], 4),
                                         "kernel_us": round(d["kernel_ms"] * 1e3, 1),
@@ -375,7 +379,7 @@ def main(argv=None):
                                         "kernels": "decode_split_kernel + decode_merge_kernel"}
         print(f"# bf16_gqa_decode: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     if run_all or "paged" in sel:
-        d = bench_paged(max(5, a.steps // 2), min(a.warmup, 5))
+        d = bench_paged(max(5, a.steps // 2), sw)
         secondary["bf16_gqa_decode paged"] = {"metric": "GB/s", "value": round(d["gbs"], 1),
                                               "frac_hbm_peak": round(d["frac_hbm"], 4),
                                               "kernel_us": round(d["kernel_ms"] * 1e3, 1),
@@ -384,7 +388,7 @@ def main(argv=None):
         print(f"# bf16_gqa_decode paged: {d['kernel_ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s", file=sys.stderr,
               flush=True)
     if run_all or "chunked" in sel:
-        r = bench_chunked(max(5, a.steps // 4), min(a.warmup, 5))
+        r = bench_chunked(max(5, a.steps // 4), sw)
         secondary["bf16 chunked prefill paged"] = {
             "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
             "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -394,7 +398,7 @@ def main(argv=None):
         print(f"# chunked prefill paged: {r['kernel_ms'] * 1e3:.1f} us, {r['kernel_tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
     if run_all or "boolmask" in sel:
-        r = bench_boolmask(max(5, a.steps // 4), min(a.warmup, 5))
+        r = bench_boolmask(max(5, a.steps // 4), sw)
         secondary["bf16_causal_e128 + bool mask"] = {
             "metric": "TFLOP/s", "value": round(r["contiguous"]["kernel_tflops"], 1),
             "frac_mfma_peak": round(r["contiguous"]["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -409,32 +413,30 @@ def main(argv=None):
               file=sys.stderr, flush=True)
     if run_all or "neox" in sel:
         for tag, sc in (("1/sqrt96", None), ("1/96", 1 / 96), ("1.0", 1.0)):
-            r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), scale=sc)
+            r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), sw, scale=sc)
             secondary[f"bf16_neox_e96 scale={tag}"] = {
                 "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
                 "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                 "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
         bias = inputs.alibi_causal_bias(64, 2048, 2048)
-        r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), min(a.warmup, 5), mask=bias)
+        r = bench_prefill("bf16_neox_e96", max(5, a.steps // 2), sw, mask=bias)
         secondary["bf16_neox_e96 alibi+causal"] = {
             "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
             "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "gbs": round(r["gbs"], 1), "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
         del bias
     if run_all or "varlen" in sel:
-        r = bench_varlen(max(5, a.steps // 2), min(a.warmup, 5))
+        r = bench_varlen(max(5, a.steps // 2), sw)
         secondary["fp16_varlen_e64"] = {"metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
                                         "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                                         "kernel_us": round(r["kernel_ms"] * 1e3, 1)}
     if run_all or "fp32" in sel:
-        r = bench_prefill("fp32_single_head", max(5, a.steps // 2), min(a.warmup, 5))
+        r = bench_prefill("fp32_single_head", max(5, a.steps // 2), sw)
         secondary["fp32_single_head"] = {"metric": "us per call", "value": round(r["kernel_ms"] * 1e3, 2),
                                          "tflops": round(r["kernel_tflops"], 3)}
 
     if run_all or "bwd" in sel:
-        # warm-up long enough for the clocks to settle after the tiny fp32 calls
-        # (with 5 calls the first timed ones ran ~15% slow)
-        r = bench_backward(max(5, a.steps // 4), max(5, min(a.warmup, 40)))
+        r = bench_backward(max(5, a.steps // 4), sw)
         secondary["bf16_causal_e128 backward"] = {
             "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
             "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
