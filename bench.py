@@ -394,7 +394,7 @@ def main(argv=None):
             "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "kernel_us": round(r["kernel_ms"] * 1e3, 1), "flop_per_call": r["flops"],
             "shape": "B=8 Hq=32 Hkv=8 E=128, 512 new rows on 4096 cached keys, 64-key pages, causal",
-            "kernels": "prefill_mfma_kernel (paged)"}
+            "kernels": "prefill_pp_kernel (paged)"}
         print(f"# chunked prefill paged: {r['kernel_ms'] * 1e3:.1f} us, {r['kernel_tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
     if run_all or "boolmask" in sel:

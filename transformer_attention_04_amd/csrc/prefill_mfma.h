@@ -1,12 +1,14 @@
 // Single-pass attention forward for bf16 / fp16 inputs on gfx950 matrix cores:
 // the four-wave kernel, and the dispatch of all bf16 / fp16 forward calls.
-// Unmasked batched calls, float masks with aligned rows and bool masks whose
-// rows are whole 16-byte chunks go to the eight-wave kernel of prefill_pp.h;
-// this kernel takes the other masks, packed variable-length batches, value
-// rows of another width (Ev != E), head dims padded to a multiple of 32
-// (columns past E never read or written), and queries against a paged
-// key/value cache (chunked prefill: pages read through the block table in
-// 16-key groups, causal aligned bottom-right).
+// Unmasked batched calls, float masks with aligned rows, bool masks whose
+// rows are whole 16-byte chunks and queries against a paged cache with
+// contiguous rows go to the eight-wave kernel of prefill_pp.h; this kernel
+// takes the other masks, packed variable-length batches, value rows of
+// another width (Ev != E), head dims padded to a multiple of 32 (columns past
+// E never read or written), and the other queries against a paged key/value
+// cache (packed rows per sequence, padded pool rows, more than 256 pages per
+// sequence, a zero scale: pages read through the block table in 16-key
+// groups, causal aligned bottom-right).
 //
 // Method: the blocked form of exact attention described on the khchao.com NN
 // Lab page ("FlashAttention Tiling & Online Softmax Algorithm"): queries in
@@ -162,9 +164,15 @@ void prefill_mfma_kernel(AttnParams p) {
         h = (int)(blockIdx.x % p.Hq);
         if (!packed_tile(p, (int)(blockIdx.x / p.Hq), b, qt, listed_a, listed_rows)) return;
     } else {
+        // Query tiles heaviest first; within one tile index, workgroups are
+        // dealt to the 8 XCDs round-robin, so (when B * Hq is a multiple of 8)
+        // XCD x takes the contiguous heads x * nbh / 8 .. : the query heads of
+        // a key/value group share their keys in one L2, and each head stays
+        // on one XCD for all its tiles.
         const int nbh = p.Hq * p.B;
         qt = p.n_qtiles - 1 - (int)(blockIdx.x / nbh);
-        const int bh = (int)(blockIdx.x % nbh);
+        int bh = (int)(blockIdx.x % nbh);
+        if ((nbh & 7) == 0) bh = (bh & 7) * (nbh >> 3) + (bh >> 3);
         h = bh % p.Hq;
         b = bh / p.Hq;
     }
@@ -628,6 +636,12 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
         if (varlen)
             return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, true, true>(p, s)
                           : launch_prefill_one<Tr, D, D, false, MASK_NONE, true, true>(p, s);
+        // the eight-wave kernel when the pool's rows are contiguous (its rows
+        // of NaN for pages outside the pool have that stride), a sequence's
+        // table row fits in four registers (256 pages) and the scale is not 0
+        if (p.scale_log2 > 0.f && p.k_sr == D && p.v_sr == D && p.max_blocks <= 256)
+            return causal ? launch_prefill_pp<Tr, D, true, MASK_NONE, true>(p, s)
+                          : launch_prefill_pp<Tr, D, false, MASK_NONE, true>(p, s);
         return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, false, true>(p, s)
                       : launch_prefill_one<Tr, D, D, false, MASK_NONE, false, true>(p, s);
     }

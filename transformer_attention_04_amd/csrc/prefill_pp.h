@@ -76,6 +76,19 @@
 // come from the Q^T staging area: Q^T is loaded into registers at each tile
 // start instead.  Causal and edge masking are applied after the bias.
 //
+// Paged key/value cache (PAGED; chunked prefill: the L new rows of each
+// sequence are its last L positions, causal aligned bottom-right): the key
+// blocks of sequence b are read through its row of the block table.  The
+// direct-to-LDS loads of one wave and block cover exactly one 16-key group
+// (rows 16w .. 16w + 15 of wave w of either group), which lies inside one
+// page (pages hold a power of two >= 16 keys), so each wave looks up one page
+// per block: the table row of the cursor's sequence sits in the wave's lanes
+// (loaded when the cursor enters a new sequence) and the group's entry comes
+// out with readlane.  An entry outside the pool is never dereferenced: its K
+// rows come from a block of NaN rows and its V rows read as 0, so exactly the
+// rows that keep one of its keys come out NaN.  Pool rows must be contiguous
+// (row stride E) for that NaN block's layout to match.
+//
 // Bool mask (MASK_BOOL; rows in whole 16-byte chunks, positive scale): the
 // same cursor moves the wave's 32 rows x 64 keys of mask bytes (2 KB) in two
 // direct-to-LDS loads per block; each lane reads 8 bytes per 16-key chunk
@@ -212,20 +225,38 @@ struct PPWork {
 // and the B heads that share a head index h next to each other, so that all
 // tiles of a (b, h) run on one XCD at the same time (sharing its K/V in L2)
 // and so do the B batches of a head (sharing a mask broadcast over the batch).
+// XCD x takes the heads h = x mod 8, or with CONTIG (paged caches, where
+// grouped query heads are the rule) the contiguous heads x Hq / 8 ..
+// (x + 1) Hq / 8 - 1, so that the query heads of a key/value group read its
+// pages through one L2.
+template <bool CONTIG = false>
 __device__ __forceinline__ void pp_pair(const PPWork& w, int B, int Hq, int P, int& bh, int& pp) {
     if (w.xcd) {
         const int x = P & 7, t = P >> 3;
         const int u = t >> w.npp_log2;
         pp = t & ((1 << w.npp_log2) - 1);
         const int b = u & ((1 << w.b_log2) - 1), m = u >> w.b_log2;
-        bh = b * Hq + m * 8 + x;
+        bh = CONTIG ? b * Hq + x * (Hq >> 3) + m : b * Hq + m * 8 + x;
     } else {
         bh = P % w.nbh;
         pp = P / w.nbh;
     }
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
+// 16 key rows of all-ones 16-bit words (NaN in bf16 and fp16) at the widest
+// head dim: the K rows a paged call reads for a block-table entry outside the
+// page pool, so that exactly the rows that keep one of its keys come out NaN.
+struct PPNanRows {
+    uint32_t w[16 * 128 / 2];
+};
+constexpr PPNanRows pp_make_nan_rows() {
+    PPNanRows x{};
+    for (int i = 0; i < 16 * 128 / 2; ++i) x.w[i] = 0xffffffffu;
+    return x;
+}
+static __device__ const PPNanRows kPPNanRows = pp_make_nan_rows();
+
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr bool FMASK = MASK == MASK_FLOAT;
@@ -249,6 +280,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr int NBDMA = BMASK ? 2 : 8;   // direct-to-LDS loads per wave per mask block
     constexpr int NBRD = BMASK ? 4 : 8;    // mask reads per lane per block
     static_assert(D == 64 || D == 96 || D == 128, "head dim must be 64, 96 or 128");
+    static_assert(!(PAGED && MASK != MASK_NONE), "no mask on a paged cache");
     static_assert(2 * NKK == 4 * NDB, "one K operand read per P.V product");
     static_assert((NSTAGE * STAGE + QAREA + BAREA) * 2 <= 160 * 1024, "LDS budget");
 
@@ -268,12 +300,12 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     // key blocks.  A pair whose two tiles coincide (odd nq) has one item.
     auto pair_qt = [&](int P, int s) {
         int bh, pp;
-        pp_pair(w, p.B, p.Hq, P, bh, pp);
+        pp_pair<PAGED>(w, p.B, p.Hq, P, bh, pp);
         return s == 0 ? w.nq - 1 - pp : pp;
     };
     auto next_item = [&](int& P, int& s) {
         int bh, pp;
-        pp_pair(w, p.B, p.Hq, P, bh, pp);
+        pp_pair<PAGED>(w, p.B, p.Hq, P, bh, pp);
         if (s == 0 && w.nq - 1 - pp != pp) {
             s = 1;
         } else {
@@ -283,11 +315,25 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     };
     // Key blocks of tile qt (at least one, so that every item takes one step
     // of the ring; an empty causal range gives a block of zeros and no work).
-    auto kend_of = [&](int qt) { return CAUSAL ? min(p.S, min(qt * BM + BM, p.L)) : p.S; };
-    auto steps_of = [&](int qt) { return max(1, (kend_of(qt) + BN - 1) / BN); };
+    // sk: the keys of the item's sequence (p.S, or on a paged cache the
+    // sequence's own count, its L query rows being its last L positions:
+    // causal aligns bottom-right).
+    auto seq_keys = [&](int b) {
+        if constexpr (PAGED)
+            return min(max(p.seq_lens[b], 0), min(p.S, p.max_blocks << p.page_shift));
+        else
+            return p.S;
+    };
+    auto kend_of = [&](int qt, int sk) {
+        if constexpr (PAGED)
+            return CAUSAL ? max(0, min(sk, min(qt * BM + BM, p.L) + sk - p.L)) : sk;
+        else
+            return CAUSAL ? min(sk, min(qt * BM + BM, p.L)) : sk;
+    };
+    auto steps_of = [&](int qt, int sk) { return max(1, (kend_of(qt, sk) + BN - 1) / BN); };
     auto head_of = [&](int P, int& b, int& h, int& kvh) {
         int bh, pp;
-        pp_pair(w, p.B, p.Hq, P, bh, pp);
+        pp_pair<PAGED>(w, p.B, p.Hq, P, bh, pp);
         h = bh % p.Hq;
         b = bh / p.Hq;
         kvh = h / p.group;
@@ -305,10 +351,10 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         if (grp == 0) {
             const int r = (P / (16 * NC)) * 16 + P % 16, c = (P % (16 * NC)) / 16;
             const int row = (r & ~31) | swap_bits23(r & 31);
-            g_off[i] = row * k_rs + c * 16;
+            g_off[i] = (row - (PAGED ? 16 * wg : 0)) * k_rs + c * 16;
         } else {
             const int k = (P / (4 * NC)) * 4 + P % 4, c = (P % (4 * NC)) / 4;
-            g_off[i] = k * v_rs + c * 16;
+            g_off[i] = (k - (PAGED ? 16 * wg : 0)) * v_rs + c * 16;
         }
     }
     const int g_rs = grp == 0 ? k_rs : v_rs;
@@ -323,26 +369,62 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     // load was issued.
     // Per-item quantities (head pointer, block count) are set when the cursor
     // enters an item; a block costs a few scalar instructions.
+    // Paged cache: each wave's part of a block is one 16-key group (rows 16wg
+    // .. 16wg + 15), which lies inside one page; the cursor keeps the block
+    // table row of its sequence in the wave's lanes (entry 64j + lane in
+    // ltab[j], at most 256 pages) and takes the group's page with readlane.
     int lP = (int)blockIdx.x, ls = 0, lt = 0, lsteps = 0, lstage = 0;
-    const uint16_t* lptr = g_ptr;  // K or V of the cursor's head, at block lt
+    const uint16_t* lptr = g_ptr;  // K or V of the cursor's head, at block lt (paged: the pool's head)
+    int lS = p.S, lb = -1;         // paged: keys and index of the cursor's sequence
+    int ltab[PAGED ? 4 : 1];
     auto load_enter = [&] {
         if (lP < w.n_pairs) {
             int b, h, kvh;
             head_of(lP, b, h, kvh);
-            lptr = g_ptr + (int64_t)b * g_sb + (int64_t)kvh * g_sh;
-            lsteps = steps_of(pair_qt(lP, ls));
+            if constexpr (PAGED) {
+                lptr = g_ptr + (int64_t)kvh * g_sh;
+                if (b != lb) {
+                    lb = b;
+                    lS = seq_keys(b);
+                    const auto tr = make_rsrc(p.block_table + (int64_t)b * p.bt_stride, p.max_blocks * 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ltab[j] = (int)buf_load4(tr, (j * 64 + lane) * 4);
+                }
+            } else {
+                lptr = g_ptr + (int64_t)b * g_sb + (int64_t)kvh * g_sh;
+            }
+            lsteps = steps_of(pair_qt(lP, ls), lS);
         }
     };
     load_enter();
     auto load_next = [&] {
         if (lP >= w.n_pairs) return false;
-        const int rows = min(BN, p.S - lt * BN);
-        const u32x4_t rs = pp_rsrc(lptr, (rows - 1) * g_rs + D * 2);
+        u32x4_t rs;
+        if constexpr (PAGED) {
+            const int k16 = lt * BN + 16 * wg;
+            const int nv = min(16, lS - k16);
+            int pg = -1;
+            if (nv > 0) {
+                const int ix = k16 >> p.page_shift, j = ix >> 6, ln = ix & 63;
+                pg = j == 0 ? __builtin_amdgcn_readlane(ltab[0], ln)
+                   : j == 1 ? __builtin_amdgcn_readlane(ltab[1], ln)
+                   : j == 2 ? __builtin_amdgcn_readlane(ltab[2], ln)
+                            : __builtin_amdgcn_readlane(ltab[3], ln);
+            }
+            const bool ok = nv > 0 && (unsigned)pg < (unsigned)p.n_pages;
+            // a kept key on a page outside the pool: K rows of NaN, V rows of 0
+            const uint16_t* src = ok ? lptr + (int64_t)pg * g_sb + (int64_t)(k16 & ((1 << p.page_shift) - 1)) * g_sr
+                                     : (const uint16_t*)kPPNanRows.w;
+            rs = pp_rsrc(src, (ok || (nv > 0 && grp == 0)) ? (nv - 1) * g_rs + D * 2 : 0);
+        } else {
+            const int rows = min(BN, p.S - lt * BN);
+            rs = pp_rsrc(lptr, (rows - 1) * g_rs + D * 2);
+        }
         const uint32_t dst = smem_addr + (uint32_t)((lstage * STAGE + grp * KTILE) * 2 + wg * NDMA * 1024);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) pp_dma16(rs, g_off[i], dst + i * 1024);
         lstage = lstage == NSTAGE - 1 ? 0 : lstage + 1;
-        lptr += (int64_t)BN * g_sr;
+        if constexpr (!PAGED) lptr += (int64_t)BN * g_sr;
         if (++lt == lsteps) {
             next_item(lP, ls);
             lt = 0;
@@ -407,7 +489,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             head_of(bP, b, h, kvh);
             const int qt = pair_qt(bP, bs);
             const int qrows = min(BM, p.L - qt * BM);
-            const int ntl = (kend_of(qt) + BN - 1) / BN;
+            const int ntl = (kend_of(qt, p.S) + BN - 1) / BN;
             blast = wave * 32 >= qrows ? -1
                     : CAUSAL ? min(ntl - 1, (qt * BM + wave * 32 + 31) / BN)
                              : ntl - 1;
@@ -508,6 +590,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     f32x16_t sA[2], sB[2];   // scores of block t and t + 1, roles swapping each iteration
     // current item
     int Sb = p.S, q0 = 0, wrow0 = wave * 32, my_row = 0;
+    int coff = 0;   // paged: keys before the first query row (causal aligns bottom-right)
 
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
@@ -559,7 +642,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         const int key0 = t * BN;
         // s_cur[kb][8c + j] is the score of key key0 + 32kb + 16c + 8hh + j for query my_row.
         int lim = Sb - (key0 + hh * 8);
-        if (CAUSAL) lim = min(lim, my_row + 1 - (key0 + hh * 8));
+        if (CAUSAL) lim = min(lim, my_row + 1 + coff - (key0 + hh * 8));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -748,13 +831,17 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         head_of(P, b, h, kvh);
         q0 = pair_qt(P, s) * BM;
         my_row = q0 + wrow0 + lq;
-        const int ntiles = (kend_of(q0 / BM) + BN - 1) / BN;  // 0 when no key is kept
+        if constexpr (PAGED) {
+            Sb = seq_keys(b);
+            coff = Sb - p.L;
+        }
+        const int ntiles = (kend_of(q0 / BM, Sb) + BN - 1) / BN;  // 0 when no key is kept
         const int nsteps = max(1, ntiles);
         const int qrows = min(BM, p.L - q0);
         const bool wave_has_rows = wrow0 < qrows;
         // last key block this wave takes part in (causal: its last row's block)
         const int last_tile = !wave_has_rows ? -1
-                              : CAUSAL ? min(ntiles - 1, (q0 + wrow0 + 31) / BN)
+                              : CAUSAL ? min(ntiles - 1, (q0 + wrow0 + 31 + coff) / BN)
                                        : ntiles - 1;
         int nP = P, ns = s;
         next_item(nP, ns);
@@ -854,7 +941,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         // last block the next scores are computed from whatever the next stage
         // holds and unused).
         auto step = [&](int t, f32x16_t* sc, f32x16_t* sn) {
-            const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0);
+            const bool edge = (t * BN + BN > Sb) || (CAUSAL && t * BN + BN - 1 > q0 + wrow0 + coff);
             if (edge) mask_scores(t, sc);
             iteration(cur, advance(cur), sc, sn);
             step_end(t, t + 1 <= last_tile);
@@ -912,7 +999,7 @@ inline int pp_device_cus() {
     return cache[dev];
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false>
 hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     PPWork w;
     w.nbh = p.Hq * p.B;
@@ -929,7 +1016,7 @@ hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     w.xcd = (MASK == MASK_NONE && p.Hq % 8 == 0 && grid % 8 == 0 && pow2(npp) && pow2(p.B)) ? 1 : 0;
     w.npp_log2 = log2i(npp);
     w.b_log2 = log2i(p.B);
-    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, MASK>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
+    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, MASK, PAGED>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
     return hipGetLastError();
 }
 
