@@ -147,6 +147,30 @@ def test_paged_chunked_prefill_bad_table_entry():
           "rows before the bad block")
 
 
+@pytest.mark.parametrize("case", ["padded_rows", "257_pages", "256_pages", "zero_scale"])
+def test_paged_chunked_prefill_kernel_choice(case):
+    """Chunked prefill takes the eight-wave kernel when pool rows are
+    contiguous, a sequence spans at most 256 pages and the scale is not 0, and
+    the four-wave kernel otherwise: both sides of each condition against the
+    oracle (a pool whose rows are padded to E + 8, 257 and 256 pages of 16 keys
+    in one sequence, a zero scale)."""
+    E, ps = 64, 16
+    lens = {"257_pages": [4100, 900], "256_pages": [4096, 900]}.get(case, [700, 333])
+    q, kc, vc, bt, ln = make_cache(len(lens), 4, 2, 40, E, ps, lens, "bf16", seed=len(case) + 3)
+    kw = dict(is_causal=True, enable_gqa=True)
+    if case == "zero_scale":
+        kw["scale"] = 0.0
+    kd, vd = kc, vc
+    if case == "padded_rows":
+        kd = torch.zeros(kc.shape[:3] + (E + 8,), dtype=kc.dtype)
+        vd = torch.zeros(vc.shape[:3] + (E + 8,), dtype=vc.dtype)
+        kd[..., :E], vd[..., :E] = kc, vc
+        kd, vd = kd.to(DEV)[..., :E], vd.to(DEV)[..., :E]
+        assert kd.stride(2) == E + 8
+    ref = O.sdpa_paged(q, kc, vc, bt, ln, **kw)
+    check(run(q, kd, vd, bt, ln, "bf16", **kw), ref, "bf16", case)
+
+
 def test_paged_chunked_prefill_full_shape_sampled():
     """B=8 sequences of 4096 cached keys whose last 512 are the new chunk,
     Hq=32, Hkv=8, E=128, 64-key pages in a shuffled pool, causal; query heads
