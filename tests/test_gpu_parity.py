@@ -178,6 +178,28 @@ def test_varlen_small(dtype, causal):
     assert_parity(out[0], lse[0].T, ro, rl.T, dtype, f"varlen causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale(dtype, causal):
+    """scale = 0: every kept key gets the same weight (the output is the mean of
+    the kept values, lse the log of their count) and masked keys stay out,
+    also in the causal edge blocks, where a masked score is -inf and
+    -inf * 0 would be NaN.  Batched with ragged tiles and GQA, with a bool
+    mask, and packed segments."""
+    q, k, v = inputs.randn_qkv((2, 4, 150, 64), (2, 2, 170, 64), (2, 2, 170, 64), dtype, seed=41)
+    r = run_both(q, k, v, dtype, is_causal=causal, scale=0.0, enable_gqa=True)
+    assert_parity(*r, dtype, f"zero scale causal={causal}")
+    m = torch.rand((1, 1, 150, 170), generator=torch.Generator().manual_seed(42)) < 0.7
+    r = run_both(q, k, v, dtype, is_causal=causal, scale=0.0, enable_gqa=True, attn_mask=m)
+    assert_parity(*r, dtype, f"zero scale, bool mask, causal={causal}")
+    lengths = [37, 120, 8, 200]
+    q, k, v, cu = inputs.varlen_inputs(lengths, 4, 4, 64, dtype, seed=43)
+    out, lse = S.sdpa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), is_causal=causal, scale=0.0)
+    torch.cuda.synchronize()
+    ro, rl = O.sdpa_varlen(q[0], k[0], v[0], cu.numpy(), is_causal=causal, scale=0.0)
+    assert_parity(out[0], lse[0].T, ro, rl.T, dtype, f"zero scale, packed, causal={causal}")
+
+
 def test_varlen_edge_segments_and_gqa():
     lengths = [0, 1, 129, 0, 64, 300]
     q, _, _, cu = inputs.varlen_inputs(lengths, 8, 8, 128, "bf16", seed=5)
