@@ -131,20 +131,26 @@ def test_paged_chunked_prefill_no_gqa_and_scale():
         check(run(q, kc, vc, bt, ln, "bf16", is_causal=True, scale=scale), ref, "bf16", f"scale={scale}")
 
 
-def test_paged_chunked_prefill_bad_table_entry():
-    """A page outside the pool at keys 240..255 of sequence 1: causal rows that
-    keep those keys are NaN, earlier rows and sequence 0 are unaffected."""
+@pytest.mark.parametrize("E,ps,dtype", [(64, 16, "fp16"), (128, 16, "bf16"), (96, 64, "fp16"), (128, 32, "bf16")])
+def test_paged_chunked_prefill_bad_table_entry(E, ps, dtype):
+    """A page outside the pool holding keys 240.. of sequence 1 (the page of
+    key 240): causal rows that keep one of its keys are NaN, earlier rows and
+    sequence 0 are unaffected (eight-wave kernel: the K rows of such a page come
+    from its block of NaN rows, the whole block at E = 128)."""
     lens = [300, 300]
-    q, kc, vc, bt, ln = make_cache(2, 4, 2, 100, 64, 16, lens, "fp16", seed=91)
+    q, kc, vc, bt, ln = make_cache(2, 4, 2, 100, E, ps, lens, dtype, seed=91 + E + ps)
     bad = bt.clone()
-    bad[1, 15] = kc.shape[0] + 3
-    out, lse = run(q, kc, vc, bad, ln, "fp16", is_causal=True, enable_gqa=True)
-    # row i keeps keys <= 200 + i: rows 40.. keep the bad block
-    assert np.isnan(out[1, :, 40:]).all() and np.isnan(lse[1, :, 40:]).all()
+    blk = 240 // ps
+    bad[1, blk] = kc.shape[0] + 3
+    # row i keeps keys <= 200 + i: rows from the page's first key - 200 on keep it
+    r0 = max(0, blk * ps - 200)
+    out, lse = run(q, kc, vc, bad, ln, dtype, is_causal=True, enable_gqa=True)
+    assert np.isnan(out[1, :, r0:]).all() and np.isnan(lse[1, :, r0:]).all()
     ref = O.sdpa_paged(q, kc, vc, bt, ln, is_causal=True, enable_gqa=True)
-    check((out[:1], lse[:1]), (ref[0][:1], ref[1][:1]), "fp16", "good sequence")
-    check((out[1:, :, :40], lse[1:, :, :40]), (ref[0][1:, :, :40], ref[1][1:, :, :40]), "fp16",
-          "rows before the bad block")
+    check((out[:1], lse[:1]), (ref[0][:1], ref[1][:1]), dtype, "good sequence")
+    if r0 > 0:
+        check((out[1:, :, :r0], lse[1:, :, :r0]), (ref[0][1:, :, :r0], ref[1][1:, :, :r0]), dtype,
+              "rows before the bad page")
 
 
 @pytest.mark.parametrize("case", ["padded_rows", "257_pages", "256_pages", "zero_scale"])
