@@ -212,3 +212,38 @@ def test_paged_packed_rows(dtype, E, ps):
         # lse (Hq, total) -> (total, Hq), the leading dims of out
         check((out.cpu().double().numpy(), lse.cpu().double().numpy().T), (ro, rl.T), dtype,
               f"E={E} ps={ps} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype,E,ps", [("bf16", 64, 16), ("fp16", 96, 64), ("bf16", 128, 32), ("fp16", 128, 256)])
+def test_paged_packed_rows_even_counts(dtype, E, ps):
+    """Packed new rows of about equal counts per sequence (at least 3/4 of
+    n_seqs x the largest count: the eight-wave kernel): counts 300, 280, 290,
+    240, 300 (the second 256-row tile of the 240-row sequence is empty) against
+    cached lengths 1000, 250 (fewer keys than new rows), 700, 2000, 300,
+    grouped heads, causal and not; then a page outside the pool in sequence 3."""
+    lens = [1000, 250, 700, 2000, 300]
+    counts = [300, 280, 290, 240, 300]
+    q4, kc, vc, bt, ln = make_cache(len(lens), 8, 2, 1, E, ps, lens, dtype, seed=E + ps + 13)
+    cu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int32)
+    q = inputs.randn_qkv((int(cu[-1]), 8, E), (1, 1, E), (1, 1, E), dtype, seed=E + ps + 14)[0]
+    assert 4 * sum(counts) >= 3 * len(counts) * max(counts)
+
+    def run_packed(table, causal):
+        out, lse = S.sdpa_fwd_paged_varlen(q.to(DEV), cu.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV),
+                                           ln.to(DEV), is_causal=causal, enable_gqa=True)
+        torch.cuda.synchronize()
+        return out.cpu().double().numpy(), lse.cpu().double().numpy().T
+
+    for causal in (False, True):
+        ro, rl = O.sdpa_paged_varlen(q, cu, kc, vc, bt, ln, is_causal=causal, enable_gqa=True)
+        check(run_packed(bt, causal), (ro, rl.T), dtype, f"E={E} ps={ps} causal={causal}")
+    # a page outside the pool at key 1200 of sequence 3 (2000 keys, 240 new rows at
+    # positions 1760..): every causal row of that sequence keeps it, the others do not read it
+    bad = bt.clone()
+    bad[3, 1200 // ps] = kc.shape[0] + 5
+    out, lse = run_packed(bad, True)
+    a, e = int(cu[3]), int(cu[4])
+    assert np.isnan(out[a:e]).all() and np.isnan(lse[a:e]).all()
+    ro, rl = O.sdpa_paged_varlen(q, cu, kc, vc, bt, ln, is_causal=True, enable_gqa=True)
+    keep = np.r_[0:a, e:int(cu[-1])]
+    check((out[keep], lse[keep]), (ro[keep], rl.T[keep]), dtype, "sequences without the bad page")

@@ -2,13 +2,14 @@
 // the four-wave kernel, and the dispatch of all bf16 / fp16 forward calls.
 // Unmasked batched calls, float masks with aligned rows, bool masks whose
 // rows are whole 16-byte chunks and queries against a paged cache with
-// contiguous rows go to the eight-wave kernel of prefill_pp.h; this kernel
-// takes the other masks, packed variable-length batches, value rows of
-// another width (Ev != E), head dims padded to a multiple of 32 (columns past
-// E never read or written), and the other queries against a paged key/value
-// cache (packed rows per sequence, padded pool rows, more than 256 pages per
-// sequence, a zero scale: pages read through the block table in 16-key
-// groups, causal aligned bottom-right).
+// contiguous rows (packed rows too when the sequences bring about equal
+// counts) go to the eight-wave kernel of prefill_pp.h; this kernel takes the
+// other masks, packed variable-length batches, value rows of another width
+// (Ev != E), head dims padded to a multiple of 32 (columns past E never read
+// or written), and the other queries against a paged key/value cache
+// (uneven packed rows, padded pool rows, more than 256 pages per sequence, a
+// zero scale: pages read through the block table in 16-key groups, causal
+// aligned bottom-right).
 //
 // Method: the blocked form of exact attention described on the khchao.com NN
 // Lab page ("FlashAttention Tiling & Online Softmax Algorithm"): queries in
@@ -633,13 +634,22 @@ hipError_t launch_prefill_d(const AttnParams& p, bool causal, int mask, bool var
         // queries against a paged cache (more new rows than the split-KV decode
         // takes, or packed rows of several sequences)
         if (mask != MASK_NONE) return hipErrorInvalidValue;
-        if (varlen)
-            return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, true, true>(p, s)
-                          : launch_prefill_one<Tr, D, D, false, MASK_NONE, true, true>(p, s);
         // the eight-wave kernel when the pool's rows are contiguous (its rows
         // of NaN for pages outside the pool have that stride), a sequence's
-        // table row fits in four registers (256 pages) and the scale is not 0
-        if (p.scale_log2 > 0.f && p.k_sr == D && p.v_sr == D && p.max_blocks <= 256)
+        // table row fits in four registers (256 pages) and the scale is not 0;
+        // packed rows only when the sequences bring about equal counts (at
+        // least 3/4 of n_seqs x max_seqlen_q rows): its workgroups take fixed
+        // shares of the tiles, where the four-wave kernel's are handed out as
+        // compute units free up
+        const bool eight = p.scale_log2 > 0.f && p.k_sr == D && p.v_sr == D && p.max_blocks <= 256;
+        if (varlen) {
+            if (eight && 4 * p.total_q >= 3 * (int64_t)p.B * p.L)
+                return causal ? launch_prefill_pp<Tr, D, true, MASK_NONE, true, true>(p, s)
+                              : launch_prefill_pp<Tr, D, false, MASK_NONE, true, true>(p, s);
+            return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, true, true>(p, s)
+                          : launch_prefill_one<Tr, D, D, false, MASK_NONE, true, true>(p, s);
+        }
+        if (eight)
             return causal ? launch_prefill_pp<Tr, D, true, MASK_NONE, true>(p, s)
                           : launch_prefill_pp<Tr, D, false, MASK_NONE, true>(p, s);
         return causal ? launch_prefill_one<Tr, D, D, true, MASK_NONE, false, true>(p, s)

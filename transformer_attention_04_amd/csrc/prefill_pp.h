@@ -87,7 +87,10 @@
 // out with readlane.  An entry outside the pool is never dereferenced: its K
 // rows come from a block of NaN rows and its V rows read as 0, so exactly the
 // rows that keep one of its keys come out NaN.  Pool rows must be contiguous
-// (row stride E) for that NaN block's layout to match.
+// (row stride E) for that NaN block's layout to match.  With VARQ the new
+// rows of sequence b are packed at tokens cu_q[b] .. (their own count, at
+// most L); tiles past a sequence's rows are items with no rows, which take
+// one step of the ring and compute nothing.
 //
 // Bool mask (MASK_BOOL; rows in whole 16-byte chunks, positive scale): the
 // same cursor moves the wave's 32 rows x 64 keys of mask bytes (2 KB) in two
@@ -256,7 +259,7 @@ constexpr PPNanRows pp_make_nan_rows() {
 }
 static __device__ const PPNanRows kPPNanRows = pp_make_nan_rows();
 
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false, bool VARQ = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr bool FMASK = MASK == MASK_FLOAT;
@@ -281,6 +284,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     constexpr int NBRD = BMASK ? 4 : 8;    // mask reads per lane per block
     static_assert(D == 64 || D == 96 || D == 128, "head dim must be 64, 96 or 128");
     static_assert(!(PAGED && MASK != MASK_NONE), "no mask on a paged cache");
+    static_assert(!VARQ || PAGED, "packed query rows only against a paged cache");
     static_assert(2 * NKK == 4 * NDB, "one K operand read per P.V product");
     static_assert((NSTAGE * STAGE + QAREA + BAREA) * 2 <= 160 * 1024, "LDS budget");
 
@@ -324,13 +328,31 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         else
             return p.S;
     };
-    auto kend_of = [&](int qt, int sk) {
-        if constexpr (PAGED)
-            return CAUSAL ? max(0, min(sk, min(qt * BM + BM, p.L) + sk - p.L)) : sk;
+    // VARQ (packed new rows of each sequence, tokens cu_q[b] ..): the rows of
+    // sequence b and its first token; tiles past its rows are empty items
+    auto seq_tok0 = [&](int b) -> int64_t {
+        if constexpr (VARQ)
+            return min(max((int64_t)p.cu_q[b], (int64_t)0), p.total_q);
         else
-            return CAUSAL ? min(sk, min(qt * BM + BM, p.L)) : sk;
+            return 0;
     };
-    auto steps_of = [&](int qt, int sk) { return max(1, (kend_of(qt, sk) + BN - 1) / BN); };
+    auto seq_rows = [&](int b) {
+        if constexpr (VARQ) {
+            const int64_t a = seq_tok0(b);
+            return (int)min(min(max((int64_t)p.cu_q[b + 1], a), p.total_q) - a, (int64_t)p.L);
+        } else {
+            return p.L;
+        }
+    };
+    auto kend_of = [&](int qt, int sk, int lq) {
+        if constexpr (PAGED) {
+            if (VARQ && qt * BM >= lq) return 0;
+            return CAUSAL ? max(0, min(sk, min(qt * BM + BM, lq) + sk - lq)) : sk;
+        } else {
+            return CAUSAL ? min(sk, min(qt * BM + BM, lq)) : sk;
+        }
+    };
+    auto steps_of = [&](int qt, int sk, int lq) { return max(1, (kend_of(qt, sk, lq) + BN - 1) / BN); };
     auto head_of = [&](int P, int& b, int& h, int& kvh) {
         int bh, pp;
         pp_pair<PAGED>(w, p.B, p.Hq, P, bh, pp);
@@ -376,6 +398,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
     int lP = (int)blockIdx.x, ls = 0, lt = 0, lsteps = 0, lstage = 0;
     const uint16_t* lptr = g_ptr;  // K or V of the cursor's head, at block lt (paged: the pool's head)
     int lS = p.S, lb = -1;         // paged: keys and index of the cursor's sequence
+    int lL = p.L;                  // its query rows
     int ltab[PAGED ? 4 : 1];
     auto load_enter = [&] {
         if (lP < w.n_pairs) {
@@ -386,6 +409,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
                 if (b != lb) {
                     lb = b;
                     lS = seq_keys(b);
+                    lL = seq_rows(b);
                     const auto tr = make_rsrc(p.block_table + (int64_t)b * p.bt_stride, p.max_blocks * 4);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) ltab[j] = (int)buf_load4(tr, (j * 64 + lane) * 4);
@@ -393,7 +417,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             } else {
                 lptr = g_ptr + (int64_t)b * g_sb + (int64_t)kvh * g_sh;
             }
-            lsteps = steps_of(pair_qt(lP, ls), lS);
+            lsteps = steps_of(pair_qt(lP, ls), lS, lL);
         }
     };
     load_enter();
@@ -442,10 +466,10 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         int b, h, kvh;
         head_of(P, b, h, kvh);
         const int q0 = pair_qt(P, s) * BM;
-        const int rows = min(32, p.L - q0 - wave * 32);
-        const u32x4_t rs = pp_rsrc((const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh +
-                                       (int64_t)(q0 + wave * 32) * p.q_sr,
-                                   (rows - 1) * q_rs + D * 2);
+        const int rows = min(32, seq_rows(b) - q0 - wave * 32);
+        const int64_t qoff = VARQ ? (int64_t)h * p.q_sh + (seq_tok0(b) + q0 + wave * 32) * p.q_sr
+                                  : (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)(q0 + wave * 32) * p.q_sr;
+        const u32x4_t rs = pp_rsrc((const uint16_t*)p.q + qoff, (rows - 1) * q_rs + D * 2);
         // lane index made opaque here, so that the per-lane offsets below are
         // computed per tile and not kept in registers across the whole loop
         int ln = lane;
@@ -489,7 +513,7 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             head_of(bP, b, h, kvh);
             const int qt = pair_qt(bP, bs);
             const int qrows = min(BM, p.L - qt * BM);
-            const int ntl = (kend_of(qt, p.S) + BN - 1) / BN;
+            const int ntl = (kend_of(qt, p.S, p.L) + BN - 1) / BN;
             blast = wave * 32 >= qrows ? -1
                     : CAUSAL ? min(ntl - 1, (qt * BM + wave * 32 + 31) / BN)
                              : ntl - 1;
@@ -831,13 +855,15 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         head_of(P, b, h, kvh);
         q0 = pair_qt(P, s) * BM;
         my_row = q0 + wrow0 + lq;
+        const int Lb = seq_rows(b);
+        const int64_t tok0 = seq_tok0(b);
         if constexpr (PAGED) {
             Sb = seq_keys(b);
-            coff = Sb - p.L;
+            coff = Sb - Lb;
         }
-        const int ntiles = (kend_of(q0 / BM, Sb) + BN - 1) / BN;  // 0 when no key is kept
+        const int ntiles = (kend_of(q0 / BM, Sb, Lb) + BN - 1) / BN;  // 0 when no key is kept
         const int nsteps = max(1, ntiles);
-        const int qrows = min(BM, p.L - q0);
+        const int qrows = min(BM, Lb - q0);
         const bool wave_has_rows = wrow0 < qrows;
         // last key block this wave takes part in (causal: its last row's block)
         const int last_tile = !wave_has_rows ? -1
@@ -964,7 +990,8 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
         const int o_rs = (int)(p.o_sr * 2);
         int lrow = wrow0 + lq;
         asm volatile("" : "+v"(lrow));  // per-lane store offsets computed here, not kept across the loop
-        const auto ors = make_rsrc((uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)q0 * p.o_sr,
+        const auto ors = make_rsrc((uint16_t*)p.o + (VARQ ? 0 : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh +
+                                       (tok0 + q0) * p.o_sr,
                                    (qrows - 1) * o_rs + D * 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -978,7 +1005,8 @@ void prefill_pp_kernel(AttnParams p, PPWork w) {
             }
         if (hh == 0) {
             const float lse = (l_tot == 0.f) ? kNegInf : (sh_run + fast_log2(l_tot)) * kLn2;
-            const auto lrs = make_rsrc(p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + q0, qrows * 4);
+            const auto lrs = make_rsrc(p.lse + (VARQ ? 0 : (int64_t)b * p.lse_sb) + (int64_t)h * p.lse_sh + tok0 + q0,
+                                       qrows * 4);
             buf_store4(lse, lrs, lrow * 4);
         }
         P = nP;
@@ -999,7 +1027,7 @@ inline int pp_device_cus() {
     return cache[dev];
 }
 
-template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false>
+template <typename Tr, int D, bool CAUSAL, int MASK = MASK_NONE, bool PAGED = false, bool VARQ = false>
 hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     PPWork w;
     w.nbh = p.Hq * p.B;
@@ -1016,7 +1044,7 @@ hipError_t launch_prefill_pp(const AttnParams& p, hipStream_t stream) {
     w.xcd = (MASK == MASK_NONE && p.Hq % 8 == 0 && grid % 8 == 0 && pow2(npp) && pow2(p.B)) ? 1 : 0;
     w.npp_log2 = log2i(npp);
     w.b_log2 = log2i(p.B);
-    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, MASK, PAGED>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
+    hipLaunchKernelGGL((prefill_pp_kernel<Tr, D, CAUSAL, MASK, PAGED, VARQ>), dim3((unsigned)grid), dim3(512), 0, stream, p, w);
     return hipGetLastError();
 }
 
