@@ -270,10 +270,12 @@ def bench_paged(steps, warmup, device="cuda", page=64):
 CHUNKED = dict(B=8, Hq=32, Hkv=8, E=128, L=512, S=4096, page=64, seed=11)
 
 
-def bench_chunked(steps, warmup, device="cuda"):
+def bench_chunked(steps, warmup, device="cuda", packed=False):
     """Chunked prefill against a paged cache: 8 sequences of 4096 cached keys
     (bf16, 64-key pages in a shuffled pool) whose last 512 positions are the new
-    rows, Hq=32 over Hkv=8, E=128, causal aligned bottom-right."""
+    rows, Hq=32 over Hkv=8, E=128, causal aligned bottom-right.  packed: the
+    same rows packed token-major and passed with cu_seqlens_q
+    (sdpa_fwd_paged_varlen, the serving-batch form)."""
     import torch
     from transformer_attention_04_amd import inputs
     from transformer_attention_04_amd import sdpa as S
@@ -286,7 +288,13 @@ def bench_chunked(steps, warmup, device="cuda"):
     g = torch.Generator().manual_seed(c["seed"] + 1)
     bt = torch.randperm(n_pages, generator=g).reshape(c["B"], nb).to(torch.int32).to(device)
     lens = torch.full((c["B"],), c["S"], dtype=torch.int32, device=device)
-    fn = lambda: S.sdpa_fwd_paged(q, kc, vc, bt, lens, max_seq_len=c["S"], is_causal=True, enable_gqa=True)
+    if packed:
+        qp = q.permute(0, 2, 1, 3).reshape(c["B"] * c["L"], c["Hq"], c["E"]).contiguous()
+        cu = torch.arange(0, c["B"] + 1, dtype=torch.int32, device=device) * c["L"]
+        fn = lambda: S.sdpa_fwd_paged_varlen(qp, cu, kc, vc, bt, lens, max_seqlen_q=c["L"], max_seq_len=c["S"],
+                                             is_causal=True, enable_gqa=True)
+    else:
+        fn = lambda: S.sdpa_fwd_paged(q, kc, vc, bt, lens, max_seq_len=c["S"], is_causal=True, enable_gqa=True)
     wall, per = time_launches(fn, steps, warmup)
     L, Sk = c["L"], c["S"]
     pairs = L * (Sk - L) + L * (L + 1) // 2
@@ -397,6 +405,15 @@ def main(argv=None):
             "kernels": "prefill_pp_kernel (paged)"}
         print(f"# chunked prefill paged: {r['kernel_ms'] * 1e3:.1f} us, {r['kernel_tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+        r = bench_chunked(max(5, a.steps // 4), sw, packed=True)
+        secondary["bf16 chunked prefill paged, packed rows"] = {
+            "metric": "TFLOP/s", "value": round(r["kernel_tflops"], 1),
+            "frac_mfma_peak": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "kernel_us": round(r["kernel_ms"] * 1e3, 1), "flop_per_call": r["flops"],
+            "shape": "the same rows packed token-major with cu_seqlens_q (sdpa_fwd_paged_varlen)",
+            "kernels": "prefill_pp_kernel (paged, packed rows)"}
+        print(f"# chunked prefill paged, packed rows: {r['kernel_ms'] * 1e3:.1f} us, "
+              f"{r['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if run_all or "boolmask" in sel:
         r = bench_boolmask(max(5, a.steps // 4), sw)
         secondary["bf16_causal_e128 + bool mask"] = {
