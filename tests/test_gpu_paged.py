@@ -247,3 +247,27 @@ def test_paged_packed_rows_even_counts(dtype, E, ps):
     ro, rl = O.sdpa_paged_varlen(q, cu, kc, vc, bt, ln, is_causal=True, enable_gqa=True)
     keep = np.r_[0:a, e:int(cu[-1])]
     check((out[keep], lse[keep]), (ro[keep], rl.T[keep]), dtype, "sequences without the bad page")
+
+
+def test_paged_packed_rows_full_shape_sampled():
+    """The chunked-prefill shape as packed rows (sdpa_fwd_paged_varlen, the
+    eight-wave kernel with its pairs numbered by XCD): 8 sequences of 512 new
+    rows on 4096 cached keys, Hq=32, Hkv=8, E=128, 64-key pages, causal; the
+    query heads of the first and last cache head of three sequences checked."""
+    B, Hq, Hkv, E, ps, Sk, L = 8, 32, 8, 128, 64, 4096, 512
+    q, kc, vc, bt, ln = make_cache(B, Hq, Hkv, L, E, ps, [Sk] * B, "bf16", seed=6, extra_pages=0)
+    qp = q.permute(0, 2, 1, 3).reshape(B * L, Hq, E).contiguous()
+    cu = torch.arange(0, B + 1, dtype=torch.int32) * L
+    out, lse = S.sdpa_fwd_paged_varlen(qp.to(DEV), cu.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), ln.to(DEV),
+                                       is_causal=True, enable_gqa=True)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()           # (B * L, Hq, E)
+    lse = lse.cpu().double().numpy()           # (Hq, B * L)
+    for b in (0, 4, 7):
+        for g in (0, Hkv - 1):
+            hs = slice(4 * g, 4 * g + 4)
+            ro, rl = O.sdpa_paged(q[b:b + 1, hs], kc[:, g:g + 1], vc[:, g:g + 1], bt[b:b + 1], ln[b:b + 1],
+                                  is_causal=True, enable_gqa=True)
+            go = out[b * L:(b + 1) * L, hs].transpose(1, 0, 2)[None]
+            gl = lse[hs, b * L:(b + 1) * L][None]
+            check((go, gl), (ro, rl), "bf16", f"packed sequence {b} cache head {g}")
