@@ -218,11 +218,12 @@ def test_paged_packed_rows(dtype, E, ps):
 def test_paged_packed_rows_even_counts(dtype, E, ps):
     """Packed new rows of about equal counts per sequence (at least 3/4 of
     n_seqs x the largest count: the eight-wave kernel): counts 300, 280, 290,
-    240, 300 (the second 256-row tile of the 240-row sequence is empty) against
-    cached lengths 1000, 250 (fewer keys than new rows), 700, 2000, 300,
-    grouped heads, causal and not; then a page outside the pool in sequence 3."""
-    lens = [1000, 250, 700, 2000, 300]
-    counts = [300, 280, 290, 240, 300]
+    240, 300, 0 (the second 256-row tile of the 240-row sequence is empty, and
+    both tiles of the last one) against cached lengths 1000, 250 (fewer keys
+    than new rows), 700, 2000, 300, 64, grouped heads, causal and not; then a
+    page outside the pool in sequence 3."""
+    lens = [1000, 250, 700, 2000, 300, 64]
+    counts = [300, 280, 290, 240, 300, 0]
     q4, kc, vc, bt, ln = make_cache(len(lens), 8, 2, 1, E, ps, lens, dtype, seed=E + ps + 13)
     cu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int32)
     q = inputs.randn_qkv((int(cu[-1]), 8, E), (1, 1, E), (1, 1, E), dtype, seed=E + ps + 14)[0]
